@@ -1,0 +1,202 @@
+"""Python binding of libsk_repack.so: the skinny W4A8 / W6A8 linear for MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/sk_repack.h; PyTorch is used for
+device memory and streams.  If the shared library is missing the import of
+this module fails: there is no CPU path.
+
+Function names follow the C ABI: ``sk_repack_w4a8``, ``sk_unrepack_w4a8``,
+``sk_gemm_w4a8``, ``sk_gemm_w6a8``, ``sk_gemm_fused_rmsnorm``,
+``sk_gemm_fused_swiglu``, ``sk_debug_gemm``.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsk_repack.so")
+
+SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ALIGN, SK_ERR_FORMAT, SK_ERR_LAYOUT, SK_ERR_HIP, \
+    SK_ERR_UNSUPPORTED = range(8)
+SK_F32, SK_BF16 = 0, 1
+SK_W4_SYM, SK_W4_CODEBOOK, SK_W6_SYM = 0, 1, 2
+SK_LAYOUT_CANONICAL, SK_LAYOUT_STREAM = 0, 1
+PRO_NONE, PRO_RMSNORM, PRO_SWIGLU = 0, 1, 2
+BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
+
+# Every symbol include/sk_repack.h and include/sk_repack_test.h declare.
+EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4a8",
+           "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu", "sk_debug_gemm",
+           "sk_test_repack_on_host"]
+
+
+class SkWeightStruct(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("k", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("format", ctypes.c_int32), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("bytes", ctypes.c_size_t), ("codebook", ctypes.c_void_p)]
+
+
+class SkError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with gemm_sk_repack_amd/build.py "
+                          "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    W = ctypes.POINTER(SkWeightStruct)
+    sig = {
+        "sk_status_string": ([I], ctypes.c_char_p),
+        "sk_repack_w4a8": ([W, P], I),
+        "sk_unrepack_w4a8": ([W, P], I),
+        "sk_gemm_w4a8": ([W, P, I, I, P, P], I),
+        "sk_gemm_w6a8": ([W, P, I, I, P, P], I),
+        "sk_gemm_fused_rmsnorm": ([W, P, I, P, F, I, P, P], I),
+        "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P], I),
+        "sk_debug_gemm": ([W, I, P, P, I64, I, P, F, I, P, P, P, P, P], I),
+        "sk_test_repack_on_host": ([W, P, I], I),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.sk_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != SK_OK:
+        raise SkError(status, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensors only: the library has no CPU path")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _xt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SK_F32
+    if t.dtype == torch.bfloat16:
+        return SK_BF16
+    raise ValueError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+class QuantWeight:
+    """A quantised weight in device memory plus its C descriptor.
+
+    ``data`` is a uint8 CUDA tensor of ``weight_bytes(fmt, n, k, g)`` bytes in
+    the canonical layout (packed codes then FP32 scales); after
+    ``sk_repack_w4a8`` the same tensor holds the stream layout.
+    """
+
+    def __init__(self, data: torch.Tensor, n: int, k: int, group: int, fmt: int,
+                 codebook: torch.Tensor | None = None):
+        self.data = data
+        self.codebook = codebook
+        self.desc = SkWeightStruct(n, k, group, fmt, SK_LAYOUT_CANONICAL, 0,
+                                   data.data_ptr(), data.numel(),
+                                   codebook.data_ptr() if codebook is not None else None)
+
+    n = property(lambda self: self.desc.n)
+    k = property(lambda self: self.desc.k)
+    group = property(lambda self: self.desc.group)
+    fmt = property(lambda self: self.desc.format)
+    layout = property(lambda self: self.desc.layout)
+
+
+def weight_bytes(fmt: int, n: int, k: int, g: int) -> int:
+    return n * k * BITS[fmt] // 8 + n * (k // g) * 4
+
+
+def sk_repack_w4a8(w: QuantWeight, stream=None) -> None:
+    _check(LIB.sk_repack_w4a8(ctypes.byref(w.desc), _stream(stream)), "sk_repack_w4a8")
+
+
+def sk_unrepack_w4a8(w: QuantWeight, stream=None) -> None:
+    _check(LIB.sk_unrepack_w4a8(ctypes.byref(w.desc), _stream(stream)), "sk_unrepack_w4a8")
+
+
+def _out(w: QuantWeight, m: int, y):
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device="cuda")
+    return y
+
+
+def sk_gemm_w4a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+    m = x.shape[0]
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_w4a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
+           "sk_gemm_w4a8")
+    return y
+
+
+def sk_gemm_w6a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+    m = x.shape[0]
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_w6a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
+           "sk_gemm_w6a8")
+    return y
+
+
+def sk_gemm_fused_rmsnorm(w: QuantWeight, x: torch.Tensor, gamma: torch.Tensor, eps: float,
+                          y=None, stream=None) -> torch.Tensor:
+    m = x.shape[0]
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_fused_rmsnorm(ctypes.byref(w.desc), _ptr(x), _xt(x), _ptr(gamma),
+                                     ctypes.c_float(eps), m, _ptr(y), _stream(stream)),
+           "sk_gemm_fused_rmsnorm")
+    return y
+
+
+def sk_gemm_fused_swiglu(w: QuantWeight, gate: torch.Tensor, up: torch.Tensor, y=None,
+                         stream=None) -> torch.Tensor:
+    """gate and up are [M, K] views sharing one row stride (e.g. halves of [M, 2K])."""
+    m = gate.shape[0]
+    if gate.stride() != up.stride() or gate.stride(1) != 1:
+        raise ValueError("gate and up must be row-major with the same row stride")
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_fused_swiglu(ctypes.byref(w.desc), _ptr(gate), _ptr(up), gate.stride(0),
+                                    _xt(gate), m, _ptr(y), _stream(stream)),
+           "sk_gemm_fused_swiglu")
+    return y
+
+
+def sk_debug_gemm(w: QuantWeight, prologue: int, x: torch.Tensor, x2=None, gamma=None,
+                  eps: float = 0.0, want_partials: bool = True, stream=None):
+    """Runs the GEMM with the export flag; returns (y, q, sx, P or None)."""
+    m, k = x.shape[0], w.k
+    ld = x.stride(0) if prologue == PRO_SWIGLU else k
+    y = torch.empty((m, w.n), dtype=torch.float32, device="cuda")
+    q = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    sx = torch.empty((m,), dtype=torch.float32, device="cuda")
+    p = (torch.empty((m, w.n, k // w.group), dtype=torch.int32, device="cuda")
+         if want_partials else None)
+    _check(LIB.sk_debug_gemm(ctypes.byref(w.desc), prologue, _ptr(x), _ptr(x2), ld, _xt(x),
+                             _ptr(gamma), ctypes.c_float(eps), m, _ptr(y), _ptr(q), _ptr(sx),
+                             _ptr(p), _stream(stream)), "sk_debug_gemm")
+    return y, q, sx, p

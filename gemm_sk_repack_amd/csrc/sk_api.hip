@@ -1,0 +1,193 @@
+// sk_api.hip -- the C ABI: host-side validation, then dispatch to the kernels.
+//
+// Every check runs on the host before any HIP call, so a rejected call has
+// touched neither the device nor the caller's memory.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "../../include/sk_repack.h"
+#include "../../include/sk_repack_test.h"
+#include "sk_internal.h"
+
+#define SK_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using sk::Geom;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int format_bits(int fmt) { return fmt == SK_W6_SYM ? 6 : 4; }
+
+// The page's shape rules for the format ("Comfy quantization formats", format options).
+bool page_shape_ok(int fmt, int64_t k, int64_t g) {
+    if (g <= 0 || k <= 0 || k % g != 0) return false;
+    if (fmt == SK_W6_SYM) return k % 32 == 0 && g % 16 == 0;
+    return k % 16 == 0 && g >= 4 && (16 % g == 0 || g % 16 == 0);
+}
+
+bool backend_group_ok(int fmt, int64_t g) {
+    if (fmt == SK_W4_CODEBOOK) return g == 16 || g == 32 || g == 64 || g == 128;
+    return g == 32 || g == 64 || g == 128;
+}
+
+// Checks shared by every entry point that takes a weight.
+sk_status check_weight(const sk_weight* w) {
+    if (!w || !w->data) return SK_ERR_NULL;
+    if (w->format != SK_W4_SYM && w->format != SK_W4_CODEBOOK && w->format != SK_W6_SYM)
+        return SK_ERR_FORMAT;
+    if (w->reserved != 0) return SK_ERR_FORMAT;
+    if ((w->format == SK_W4_CODEBOOK) != (w->codebook != nullptr)) return SK_ERR_FORMAT;
+    if (w->n < 1 || w->k < 1) return SK_ERR_SHAPE;
+    if (!page_shape_ok(w->format, w->k, w->group)) return SK_ERR_SHAPE;
+    const int64_t n = w->n, k = w->k, g = w->group;
+    const size_t want = (size_t)(n * k * format_bits(w->format) / 8 + n * (k / g) * 4);
+    if (w->bytes != want) return SK_ERR_SHAPE;
+    if (!aligned16(w->data) || (w->codebook && !aligned16(w->codebook))) return SK_ERR_ALIGN;
+    if (w->layout != SK_LAYOUT_CANONICAL && w->layout != SK_LAYOUT_STREAM) return SK_ERR_LAYOUT;
+    if (k % sk::SB_K != 0 || k > sk::kMaxGemmK || !backend_group_ok(w->format, g) ||
+        n > (1 << 24))
+        return SK_ERR_UNSUPPORTED;
+    if (!sk::reorder_fits(sk::make_geom(n, k, g, w->format))) return SK_ERR_UNSUPPORTED;
+    return SK_OK;
+}
+
+sk_status from_hip(hipError_t e) { return e == hipSuccess ? SK_OK : SK_ERR_HIP; }
+
+// Checks for the GEMM entry points, then the launch.
+sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* x, const void* x2,
+                   int64_t ld, int xt, const float* gamma, float eps, int m, float* y,
+                   int8_t* q_out, float* sx_out, int32_t* p_out, void* stream, bool any_format) {
+    sk_status s = check_weight(w);
+    if (s != SK_OK) return s;
+    if (!x || !y || (prologue == sk::PRO_SWIGLU && !x2) || (prologue == sk::PRO_RMSNORM && !gamma))
+        return SK_ERR_NULL;
+    if (xt != SK_F32 && xt != SK_BF16) return SK_ERR_FORMAT;
+    if (!any_format) {
+        if (w6_entry && w->format != SK_W6_SYM) return SK_ERR_FORMAT;
+        if (!w6_entry && w->format == SK_W6_SYM) return SK_ERR_FORMAT;
+    }
+    if (p_out && w->format == SK_W4_CODEBOOK) return SK_ERR_FORMAT;
+    if (m < 1 || m > 8) return SK_ERR_SHAPE;
+    const int esize = (xt == SK_BF16) ? 2 : 4;
+    if (prologue == sk::PRO_SWIGLU) {
+        if (ld < w->k) return SK_ERR_SHAPE;
+        if ((ld * esize) % 16 != 0) return SK_ERR_ALIGN;
+    } else {
+        ld = w->k;
+    }
+    if (!aligned16(x) || !aligned16(y) || (x2 && !aligned16(x2)) || (gamma && !aligned16(gamma)) ||
+        (q_out && !aligned16(q_out)) || (p_out && !aligned16(p_out)))
+        return SK_ERR_ALIGN;
+    if (w->layout != SK_LAYOUT_STREAM) return SK_ERR_LAYOUT;
+    const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
+    if (w->format == SK_W4_CODEBOOK) return SK_ERR_UNSUPPORTED;
+    if (sk::gemm_lds_bytes(G, m) > 160 * 1024) return SK_ERR_UNSUPPORTED;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p_out) {
+        hipError_t e = hipMemsetAsync(p_out, 0, (size_t)m * w->n * (w->k / w->group) * 4, st);
+        if (e != hipSuccess) return SK_ERR_HIP;
+    }
+    sk::GemmCall c;
+    c.data = static_cast<const uint8_t*>(w->data);
+    c.codebook = w->codebook;
+    c.x = x;
+    c.x2 = x2;
+    c.ld = ld;
+    c.xt = xt;
+    c.gamma = gamma;
+    c.eps = eps;
+    c.prologue = prologue;
+    c.m = m;
+    c.y = y;
+    c.q_out = q_out;
+    c.sx_out = sx_out;
+    c.p_out = p_out;
+    return from_hip(sk::launch_gemm(G, c, st));
+}
+
+}  // namespace
+
+SK_EXPORT const char* sk_status_string(sk_status s) {
+    switch (s) {
+        case SK_OK: return "ok";
+        case SK_ERR_NULL: return "a required pointer is NULL";
+        case SK_ERR_SHAPE: return "shape rule violated (format rules, M range, bytes or ld)";
+        case SK_ERR_ALIGN: return "pointer or row stride not 16-byte aligned";
+        case SK_ERR_FORMAT: return "wrong format, dtype or codebook for this entry point";
+        case SK_ERR_LAYOUT: return "weight is in the wrong layout for this call";
+        case SK_ERR_HIP: return "HIP runtime error";
+        case SK_ERR_UNSUPPORTED: return "shape not supported by this backend";
+    }
+    return "unknown status";
+}
+
+SK_EXPORT sk_status sk_repack_w4a8(sk_weight* w, void* stream) {
+    sk_status s = check_weight(w);
+    if (s != SK_OK) return s;
+    if (w->layout != SK_LAYOUT_CANONICAL) return SK_ERR_LAYOUT;
+    const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
+    s = from_hip(sk::repack_device(static_cast<uint8_t*>(w->data), G, false,
+                                   static_cast<hipStream_t>(stream)));
+    if (s == SK_OK) w->layout = SK_LAYOUT_STREAM;
+    return s;
+}
+
+SK_EXPORT sk_status sk_unrepack_w4a8(sk_weight* w, void* stream) {
+    sk_status s = check_weight(w);
+    if (s != SK_OK) return s;
+    if (w->layout != SK_LAYOUT_STREAM) return SK_ERR_LAYOUT;
+    const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
+    s = from_hip(sk::repack_device(static_cast<uint8_t*>(w->data), G, true,
+                                   static_cast<hipStream_t>(stream)));
+    if (s == SK_OK) w->layout = SK_LAYOUT_CANONICAL;
+    return s;
+}
+
+SK_EXPORT sk_status sk_gemm_w4a8(const sk_weight* w, const void* x, int xt, int m, float* y,
+                                 void* stream) {
+    return run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
+                    nullptr, nullptr, stream, false);
+}
+
+SK_EXPORT sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m, float* y,
+                                 void* stream) {
+    return run_gemm(w, true, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
+                    nullptr, nullptr, stream, false);
+}
+
+SK_EXPORT sk_status sk_gemm_fused_rmsnorm(const sk_weight* w, const void* x, int xt,
+                                          const float* gamma, float eps, int m, float* y,
+                                          void* stream) {
+    return run_gemm(w, false, sk::PRO_RMSNORM, x, nullptr, 0, xt, gamma, eps, m, y, nullptr,
+                    nullptr, nullptr, stream, true);
+}
+
+SK_EXPORT sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void* up,
+                                         int64_t ld, int xt, int m, float* y, void* stream) {
+    return run_gemm(w, false, sk::PRO_SWIGLU, gate, up, ld, xt, nullptr, 0.0f, m, y, nullptr,
+                    nullptr, nullptr, stream, true);
+}
+
+SK_EXPORT sk_status sk_debug_gemm(const sk_weight* w, int prologue, const void* x, const void* x2,
+                                  int64_t ld, int xt, const float* gamma, float eps, int m,
+                                  float* y, int8_t* q_out, float* sx_out, int32_t* p_out,
+                                  void* stream) {
+    if (prologue < sk::PRO_NONE || prologue > sk::PRO_SWIGLU) return SK_ERR_FORMAT;
+    return run_gemm(w, false, prologue, x, x2, ld, xt, gamma, eps, m, y, q_out, sx_out, p_out,
+                    stream, true);
+}
+
+SK_EXPORT sk_status sk_test_repack_on_host(const sk_weight* w, void* host_bytes, int inverse) {
+    if (!w || !host_bytes) return SK_ERR_NULL;
+    sk_weight tmp = *w;
+    tmp.data = host_bytes;
+    tmp.layout = SK_LAYOUT_CANONICAL;
+    sk_status s = check_weight(&tmp);
+    if (s != SK_OK) return s;
+    const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
+    return sk::repack_host(static_cast<uint8_t*>(host_bytes), G, inverse != 0) ? SK_OK
+                                                                               : SK_ERR_SHAPE;
+}

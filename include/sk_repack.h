@@ -1,0 +1,200 @@
+/*
+ * sk_repack.h -- C ABI of the MI355X (gfx950) skinny quantized linear library.
+ *
+ *   Y[M,N] = dequant(W)[N,K] . int8(h)[M,K]^T ,   M = 1..8,
+ *
+ * where W is a 4-bit or 6-bit weight with FP32 per-group scales, h is the
+ * activation (optionally produced by an RMSNorm or SwiGLU prologue) and int8()
+ * is per-row symmetric quantisation done inside the GEMM launch.
+ *
+ * Sources, cited by page title and section:
+ *  [LIN]  "在 ComfyUI 中将 LLM token 速率翻倍" (Doubling the LLM token rate in
+ *         ComfyUI), section "优化线性 Kernel" (optimizing linear kernels):
+ *         W4A8/W6A8 skinny GEMV/GEMM; weights and their per-group scales
+ *         interleaved in the order the kernel consumes them, so each workgroup
+ *         streams contiguous memory; the re-layout is done once per model load,
+ *         in place, with no extra memory; M up to 8 rows; RMSNorm/SwiGLU folded
+ *         into the activation quantisation.
+ *  [FMT]  "Comfy 量化格式" (Comfy quantization formats), sections "权重格式"
+ *         (weight formats: N, K, G, FP32 scales), "格式选项" (format options:
+ *         W4 codebook, W6, symmetric export, shape rules) and "激活与平滑"
+ *         (activations: integer formats quantise float input in the kernel).
+ *
+ * Conventions for every entry point
+ *  - All pointers except `sk_weight*` itself are DEVICE pointers to memory the
+ *    caller owns.  The library allocates and frees no device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Calls only enqueue work and return; nothing synchronises the host.
+ *  - Validation is synchronous and happens before any GPU work: on any status
+ *    other than SK_OK nothing was launched and no memory was touched.
+ *    A device fault inside a launched kernel shows up at the caller's next
+ *    synchronisation, not in the return value.
+ *  - There is no silent fallback: a shape this backend does not handle
+ *    returns SK_ERR_UNSUPPORTED rather than running a slower path.
+ *  - NaN/Inf inputs are outside the contract.
+ */
+#ifndef SK_REPACK_H
+#define SK_REPACK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SK_OK = 0,
+    SK_ERR_NULL = 1,        /* a required pointer is NULL                                   */
+    SK_ERR_SHAPE = 2,       /* the format's shape rules [FMT] fail, or M not in 1..8, N < 1,
+                               ld < K, or `bytes` does not match N, K, G                    */
+    SK_ERR_ALIGN = 3,       /* a pointer (or a row stride in bytes) is not 16-byte aligned  */
+    SK_ERR_FORMAT = 4,      /* wrong entry point for the weight's format, unknown format or
+                               dtype, or the codebook is missing / given when not allowed    */
+    SK_ERR_LAYOUT = 5,      /* GEMM on a canonical (not repacked) weight, repack of an
+                               already repacked weight, or unrepack of a canonical one      */
+    SK_ERR_HIP = 6,         /* a HIP runtime call failed (launch error, no device, ...)    */
+    SK_ERR_UNSUPPORTED = 7  /* allowed by [FMT] but not by this backend (see below)         */
+} sk_status;
+
+typedef enum { SK_F32 = 0, SK_BF16 = 1 } sk_dtype;
+
+typedef enum {
+    SK_W4_SYM = 0,          /* 4-bit two's-complement weights, FP32 group scales [FMT]     */
+    SK_W4_CODEBOOK = 1,     /* 4-bit unsigned index into a float[16] table [FMT]           */
+    SK_W6_SYM = 2           /* 6-bit two's-complement weights, FP32 group scales [FMT]     */
+} sk_format;
+
+typedef enum {
+    SK_LAYOUT_CANONICAL = 0,  /* the storage layout below                                  */
+    SK_LAYOUT_STREAM = 1      /* the library's interleaved stream layout (opaque)           */
+} sk_layout;
+
+/*
+ * Weight descriptor.  The struct lives in host memory and is owned by the
+ * caller; `data` and `codebook` are device pointers, also caller-owned.
+ *
+ * Canonical layout of `data` (SK_LAYOUT_CANONICAL), one allocation of
+ * `bytes` = N*K*bits/8 + N*(K/G)*4 bytes:
+ *   packed weights, [N][K*bits/8] uint8, row-major:
+ *     W4 / codebook: byte j of a row holds element 2j in the low nibble and
+ *       2j+1 in the high nibble (W4: two's complement in [-8,7]; codebook:
+ *       unsigned index in [0,15]);
+ *     W6: every 3 bytes are a little-endian 24-bit word with 4 consecutive
+ *       elements, element r at bits 6r..6r+5, two's complement in [-32,31];
+ *   followed directly by the scales, [N][K/G] float32, row-major; group j of
+ *   row n covers k = j*G .. j*G+G-1 (no zero point: weights are symmetric).
+ * After sk_repack_w4a8 the same bytes hold the stream layout; only this
+ * library reads it.  `bytes` never changes.
+ */
+typedef struct {
+    int32_t n;                /* N: output features                                        */
+    int32_t k;                /* K: input features                                         */
+    int32_t group;            /* G: group size along K                                     */
+    int32_t format;           /* sk_format                                                 */
+    int32_t layout;           /* sk_layout; set by sk_repack_w4a8 / sk_unrepack_w4a8       */
+    int32_t reserved;         /* must be 0                                                 */
+    void*   data;             /* device, 16-byte aligned                                   */
+    size_t  bytes;            /* N*K*bits/8 + N*(K/G)*4                                    */
+    const float* codebook;    /* device float[16] for SK_W4_CODEBOOK, else NULL            */
+} sk_weight;
+
+/*
+ * Backend restrictions (returned as SK_ERR_UNSUPPORTED; [FMT] allows
+ * accelerated backends to add shape limits):
+ *   K % 128 == 0; G in {32, 64, 128} for SK_W4_SYM and SK_W6_SYM and
+ *   G in {16, 32, 64, 128} for SK_W4_CODEBOOK; N <= 2^24;
+ *   16 rows of one weight (16*K*bits/8 + 16*(K/G)*4 bytes) <= 256 KiB;
+ *   K <= 17408 for the GEMM entry points.
+ */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* sk_status_string(sk_status s);
+
+/*
+ * One-time, in-place repack [LIN]: rewrites `w->data` from the canonical
+ * layout into the stream layout, in which every 16-row tile's weights and
+ * their group scales sit together in the order the GEMM workgroups consume
+ * them.  Every format is accepted (the name follows the W4A8 case).
+ * No device memory is allocated: the permutation is done with in-place
+ * rotations and an in-register per-tile reorder.  Weight codes are re-encoded
+ * to offset binary (w + 8, w + 32) so the kernels unpack them with masks.
+ * On success sets w->layout = SK_LAYOUT_STREAM (the host struct is updated at
+ * enqueue time; the bytes are ready when the stream reaches this point).
+ * Errors: NULL, SHAPE, ALIGN, FORMAT, LAYOUT (already repacked), UNSUPPORTED, HIP.
+ */
+sk_status sk_repack_w4a8(sk_weight* w, void* stream);
+
+/*
+ * Inverse of sk_repack_w4a8, in place: restores the canonical bytes exactly
+ * and sets w->layout = SK_LAYOUT_CANONICAL.  For saving a loaded model and for
+ * tests.  Errors as sk_repack_w4a8 (LAYOUT if the weight is canonical).
+ */
+sk_status sk_unrepack_w4a8(sk_weight* w, void* stream);
+
+/*
+ * Skinny W4A8 linear [LIN]: y[M][N] = sx[m] * sum_j s[n][j] * P[m][n][j],
+ * P = per-group integer dot product of the weights (or, for the codebook,
+ * the float levels) with q, where (q, sx) = per-row int8 quantisation of x
+ * (sx = absmax/127, q = round-half-even(x/sx) clamped to +-127, all-zero row
+ * -> sx = 0), done inside the launch [FMT activations].
+ *   w  : repacked SK_W4_SYM or SK_W4_CODEBOOK weight
+ *   x  : device [M][K], row-major, dtype xt (SK_F32 or SK_BF16), 16-byte aligned
+ *   m  : 1..8
+ *   y  : device [M][N] float32, row-major, 16-byte aligned (fully overwritten)
+ * Errors: NULL, SHAPE, ALIGN, FORMAT (not a W4 format), LAYOUT, UNSUPPORTED, HIP.
+ */
+sk_status sk_gemm_w4a8(const sk_weight* w, const void* x, int xt, int m,
+                       float* y, void* stream);
+
+/* Same for a repacked SK_W6_SYM weight [LIN] [FMT]. */
+sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m,
+                       float* y, void* stream);
+
+/*
+ * RMSNorm prologue fused into the quantisation [LIN]:
+ *   h[m][k] = fp32(fp32(x[m][k] * r[m]) * gamma[k]),
+ *   r[m] = fp32(1 / fp32(sqrt(fp32(fp32(ss[m]/K) + eps)))),
+ *   ss[m] = sum_k x[m][k]^2 in float64,
+ * then y = linear(w, h) exactly as sk_gemm_w4a8 / sk_gemm_w6a8 would with x = h.
+ * h never leaves registers/LDS.  Any weight format.
+ *   gamma: device [K] float32, 16-byte aligned.  eps: added in fp32.
+ */
+sk_status sk_gemm_fused_rmsnorm(const sk_weight* w, const void* x, int xt,
+                                const float* gamma, float eps, int m,
+                                float* y, void* stream);
+
+/*
+ * SwiGLU prologue fused into the quantisation [LIN]:
+ *   h[m][k] = fp32(fp32(g / fp32(1 + E(-g))) * u),  g = gate[m][k], u = up[m][k],
+ * where E is a fixed float32 exp (Cody-Waite reduction by ln 2 in two parts,
+ * degree-7 Taylor polynomial in Horner form, scaling by 2^n in two exact
+ * steps; arguments >= 89 give +inf, <= -104 give 0), then y = linear(w, h).
+ *   gate, up: device, rows of K elements with row stride `ld` elements
+ *             (ld >= K; ld * element size a multiple of 16 bytes), dtype xt.
+ * Any weight format.
+ */
+sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void* up,
+                               int64_t ld, int xt, int m, float* y, void* stream);
+
+/*
+ * Test hook: the GEMM kernels instantiated with an export flag.  Runs the same
+ * computation as the entry point selected by `prologue` (0 = none,
+ * 1 = RMSNorm, 2 = SwiGLU; `x2`, `ld`, `gamma`, `eps` as there; for prologue 0
+ * and 1 `ld` is ignored and rows are K apart) and additionally writes
+ *   q_out  [M][K]     int8    : the quantised activations the kernel used,
+ *   sx_out [M]        float32 : their scales,
+ *   p_out  [M][N][K/G] int32  : the per-group integer partials (integer
+ *                               formats; must be NULL for the codebook).
+ * Any of q_out / sx_out / p_out may be NULL.  p_out is zeroed by the call.
+ */
+sk_status sk_debug_gemm(const sk_weight* w, int prologue, const void* x, const void* x2,
+                        int64_t ld, int xt, const float* gamma, float eps, int m,
+                        float* y, int8_t* q_out, float* sx_out, int32_t* p_out,
+                        void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SK_REPACK_H */

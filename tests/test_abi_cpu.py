@@ -1,0 +1,120 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+declared symbol, and rejects bad calls on the host with the documented codes
+(validation runs before any HIP call, so these never touch a device)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gemm_sk_repack_amd as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
+
+
+def declared_symbols():
+    names = []
+    for h in ("sk_repack.h", "sk_repack_test.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        names += re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(sk_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_every_declared_symbol_is_exported():
+    decl = declared_symbols()
+    assert set(decl) == set(sk.EXPORTS), decl
+    for name in decl:
+        assert hasattr(sk.LIB, name), name
+
+
+def test_status_strings():
+    for s in range(8):
+        assert sk.status_string(s)
+    assert sk.status_string(99) == "unknown status"
+
+
+def W(n=64, k=256, g=32, fmt=0, layout=0, data=FAKE, nbytes=None, cb=None, reserved=0):
+    if nbytes is None:
+        nbytes = sk.weight_bytes(fmt, n, k, g)
+    return sk.SkWeightStruct(n, k, g, fmt, layout, reserved, data, nbytes, cb)
+
+
+def gemm(w, x=FAKE, xt=0, m=1, y=FAKE):
+    return sk.LIB.sk_gemm_w4a8(ctypes.byref(w), x, xt, m, y, None)
+
+
+def test_null_pointers():
+    assert sk.LIB.sk_repack_w4a8(None, None) == sk.SK_ERR_NULL
+    assert sk.LIB.sk_repack_w4a8(ctypes.byref(W(data=None)), None) == sk.SK_ERR_NULL
+    assert gemm(W(layout=1), x=None) == sk.SK_ERR_NULL
+    assert gemm(W(layout=1), y=None) == sk.SK_ERR_NULL
+    w = W(layout=1)
+    assert sk.LIB.sk_gemm_fused_rmsnorm(ctypes.byref(w), FAKE, 0, None, 1e-6, 1, FAKE, None) \
+        == sk.SK_ERR_NULL
+    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, None, 256, 0, 1, FAKE, None) \
+        == sk.SK_ERR_NULL
+
+
+def test_format_errors():
+    assert gemm(W(fmt=7, nbytes=1)) == sk.SK_ERR_FORMAT
+    assert gemm(W(layout=1), xt=5) == sk.SK_ERR_FORMAT
+    # codebook format needs a codebook; other formats must not have one
+    assert gemm(W(fmt=1, layout=1)) == sk.SK_ERR_FORMAT
+    assert gemm(W(fmt=0, layout=1, cb=FAKE)) == sk.SK_ERR_FORMAT
+    # entry point / format mismatch
+    w6 = W(fmt=2, g=64, layout=1)
+    assert gemm(w6) == sk.SK_ERR_FORMAT
+    w4 = W(layout=1)
+    assert sk.LIB.sk_gemm_w6a8(ctypes.byref(w4), FAKE, 0, 1, FAKE, None) == sk.SK_ERR_FORMAT
+    assert gemm(W(reserved=1, layout=1)) == sk.SK_ERR_FORMAT
+
+
+@pytest.mark.parametrize("k,g,fmt", [(48, 12, 0), (40, 8, 0), (48, 16, 2), (64, 8, 2), (64, 2, 0)])
+def test_page_shape_rules_rejected(k, g, fmt):
+    assert gemm(W(k=k, g=g, fmt=fmt, layout=1)) == sk.SK_ERR_SHAPE
+
+
+def test_shape_errors():
+    assert gemm(W(layout=1), m=0) == sk.SK_ERR_SHAPE
+    assert gemm(W(layout=1), m=9) == sk.SK_ERR_SHAPE
+    assert gemm(W(n=0, layout=1)) == sk.SK_ERR_SHAPE
+    assert gemm(W(layout=1, nbytes=12345)) == sk.SK_ERR_SHAPE
+    w = W(layout=1)
+    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, FAKE, 255, 0, 1, FAKE, None) \
+        == sk.SK_ERR_SHAPE
+
+
+def test_align_errors():
+    assert gemm(W(layout=1, data=FAKE + 8)) == sk.SK_ERR_ALIGN
+    assert gemm(W(layout=1), x=FAKE + 4) == sk.SK_ERR_ALIGN
+    assert gemm(W(layout=1), y=FAKE + 4) == sk.SK_ERR_ALIGN
+    w = W(layout=1)
+    # ld * 4 bytes must be a multiple of 16
+    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, FAKE, 258, 0, 1, FAKE, None) \
+        == sk.SK_ERR_ALIGN
+
+
+def test_layout_errors():
+    assert gemm(W(layout=0)) == sk.SK_ERR_LAYOUT                     # not repacked
+    assert sk.LIB.sk_repack_w4a8(ctypes.byref(W(layout=1)), None) == sk.SK_ERR_LAYOUT
+    assert sk.LIB.sk_unrepack_w4a8(ctypes.byref(W(layout=0)), None) == sk.SK_ERR_LAYOUT
+    assert gemm(W(layout=5)) == sk.SK_ERR_LAYOUT
+
+
+def test_backend_restrictions():
+    # allowed by the page's rules, not by this backend
+    assert gemm(W(k=48, g=16, layout=1)) == sk.SK_ERR_UNSUPPORTED        # K % 128
+    assert gemm(W(k=256, g=16, layout=1)) == sk.SK_ERR_UNSUPPORTED       # W4 sym G=16
+    assert gemm(W(k=256, g=8, layout=1)) == sk.SK_ERR_UNSUPPORTED        # G < 16
+    assert gemm(W(k=20480, g=32, layout=1)) == sk.SK_ERR_UNSUPPORTED     # K too large
+    # the codebook GEMM is not built yet
+    assert gemm(W(fmt=1, g=16, layout=1, cb=FAKE)) == sk.SK_ERR_UNSUPPORTED
+
+
+def test_failed_call_leaves_descriptor_unchanged():
+    w = W(layout=0, data=FAKE + 8)
+    assert sk.LIB.sk_repack_w4a8(ctypes.byref(w), None) == sk.SK_ERR_ALIGN
+    assert w.layout == 0

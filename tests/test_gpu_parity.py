@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: quantised activations q and scales sx bit-exact, per-group int32
+partials P bit-exact, and Y within 1e-4 of the oracle relative to the
+magnitude sx * sum_j |s * P| (the natural scale of fp32 accumulation error;
+an elementwise relative error is ill-posed where Y sits near 0).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth as S
+from layout_spec import stream_layout
+
+pytestmark = pytest.mark.gpu
+
+import gemm_sk_repack_amd as sk  # noqa: E402
+
+TOL = 1e-4
+F32 = np.float32
+
+
+def gpu_weight(fmt, n, k, g, seed):
+    vals, s, buf = S.make_weight(fmt, n, k, g, seed, seed + 1)
+    cb = torch.from_numpy(S.codebook(seed + 6)).cuda() if fmt == 1 else None
+    t = torch.from_numpy(buf.copy()).cuda()
+    return sk.QuantWeight(t, n, k, g, fmt, cb), buf
+
+
+def to_dev(h, xt):
+    """Activations as the device sees them, and the fp32 values the oracle must use."""
+    if xt == "bf16":
+        bits = S.to_bf16_bits(h)
+        dev = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        return dev, O.bf16_to_f32(bits)
+    return torch.from_numpy(h).cuda(), h
+
+
+def assert_y_close(y, ref, tol=TOL):
+    y = y.astype(np.float64)
+    err = np.abs(y - ref["Y"])
+    mag = ref["mag"]
+    zero = mag == 0
+    assert np.all(err[zero] == 0)
+    rel = err[~zero] / mag[~zero]
+    assert rel.size == 0 or rel.max() <= tol, f"max normalised error {rel.max():.3e}"
+
+
+def check_call(w, buf, fmt, n, k, g, h_dev, h_ref, m):
+    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_NONE, h_dev, want_partials=(fmt != 1))
+    torch.cuda.synchronize()
+    ref = O.reference(fmt, buf, n, k, g, h_ref, None)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    if p is not None:
+        assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"])
+    assert_y_close(y.cpu().numpy(), ref)
+    return y, ref
+
+
+# ----------------------------------------------------------------------------
+# repack
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,n,k,g", [
+    (0, 1024, 1024, 32), (0, 1000, 512, 32), (0, 17, 256, 64), (0, 5, 128, 128),
+    (0, 6144, 4096, 32), (2, 300, 1024, 64), (2, 33, 256, 32), (1, 48, 256, 16),
+])
+def test_repack_bytes_match_spec_and_invert(fmt, n, k, g):
+    w, buf = gpu_weight(fmt, n, k, g, 7 + n)
+    sk.sk_repack_w4a8(w)
+    assert w.layout == sk.SK_LAYOUT_STREAM
+    torch.cuda.synchronize()
+    got = w.data.cpu().numpy()
+    assert np.array_equal(got, stream_layout(fmt, buf, n, k, g))
+    sk.sk_unrepack_w4a8(w)
+    torch.cuda.synchronize()
+    assert w.layout == sk.SK_LAYOUT_CANONICAL
+    assert np.array_equal(w.data.cpu().numpy(), buf)
+
+
+def test_repack_allocates_nothing():
+    w, _ = gpu_weight(0, 4096, 4096, 32, 3)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    sk.sk_repack_w4a8(w)
+    torch.cuda.synchronize()
+    free1, _ = torch.cuda.mem_get_info()
+    assert free1 == free0
+
+
+# ----------------------------------------------------------------------------
+# GEMM parity
+# ----------------------------------------------------------------------------
+
+GEMM_CASES = [
+    # fmt, n, k, g, ms
+    (0, 1024, 1024, 32, (1, 2, 3, 4, 5, 6, 7, 8)),
+    (0, 1000, 512, 32, (1, 3, 8)),
+    (0, 17, 256, 64, (1, 5)),
+    (0, 5, 128, 128, (1, 2)),
+    (0, 2048, 4096, 32, (1, 8)),
+    (2, 300, 1024, 64, (1, 4, 8)),
+    (2, 33, 256, 32, (1, 8)),
+    (2, 64, 512, 128, (1, 8)),
+]
+
+
+@pytest.mark.parametrize("fmt,n,k,g,ms", GEMM_CASES)
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_gemm_matches_oracle(fmt, n, k, g, ms, xt):
+    w, buf = gpu_weight(fmt, n, k, g, 100 + n + k)
+    sk.sk_repack_w4a8(w)
+    for m in ms:
+        h = S.activations(300 + m, m, k)
+        h_dev, h_ref = to_dev(h, xt)
+        check_call(w, buf, fmt, n, k, g, h_dev, h_ref, m)
+
+
+def test_public_entry_points_equal_debug_run():
+    for fmt, g in ((0, 32), (2, 64)):
+        n, k = 640, 2048
+        w, buf = gpu_weight(fmt, n, k, g, 11)
+        sk.sk_repack_w4a8(w)
+        for m in (1, 8):
+            x = torch.from_numpy(S.activations(12, m, k)).cuda()
+            y_dbg = sk.sk_debug_gemm(w, sk.PRO_NONE, x, want_partials=False)[0]
+            y = (sk.sk_gemm_w4a8 if fmt == 0 else sk.sk_gemm_w6a8)(w, x)
+            torch.cuda.synchronize()
+            assert torch.equal(y, y_dbg)
+
+
+def test_zero_and_constant_rows():
+    n, k, g = 256, 1024, 32
+    w, buf = gpu_weight(0, n, k, g, 21)
+    sk.sk_repack_w4a8(w)
+    h = S.activations(22, 4, k)
+    h[1] = 0.0
+    h[2] = -3.25
+    h[3, :] = 0.0
+    h[3, 17] = 1e-30
+    y, ref = check_call(w, buf, 0, n, k, g, torch.from_numpy(h).cuda(), h, 4)
+    assert np.all(y.cpu().numpy()[1] == 0)
+
+
+def test_rows_do_not_interact_and_runs_repeat():
+    n, k, g = 512, 2048, 32
+    w, buf = gpu_weight(0, n, k, g, 31)
+    sk.sk_repack_w4a8(w)
+    x = torch.from_numpy(S.activations(32, 8, k)).cuda()
+    y8 = sk.sk_gemm_w4a8(w, x)
+    y8b = sk.sk_gemm_w4a8(w, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y8, y8b)                        # deterministic
+    for m in range(2, 8):                              # same MFMA path: bit-identical rows
+        ym = sk.sk_gemm_w4a8(w, x[:m].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(ym, y8[:m])
+    ref = O.reference(0, buf, n, k, g, x.cpu().numpy())
+    for mi in range(8):                                # M = 1 (dot4 path): within tolerance
+        y1 = sk.sk_gemm_w4a8(w, x[mi:mi + 1].contiguous())
+        torch.cuda.synchronize()
+        assert_y_close(y1.cpu().numpy(), {"Y": ref["Y"][mi:mi + 1], "mag": ref["mag"][mi:mi + 1]})
+
+
+# ----------------------------------------------------------------------------
+# fused prologues
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("fmt,g", [(0, 32), (2, 64)])
+def test_fused_rmsnorm(m, fmt, g):
+    n, k = 384, 4096
+    w, buf = gpu_weight(fmt, n, k, g, 41)
+    sk.sk_repack_w4a8(w)
+    x = S.activations(42 + m, m, k) * F32(2.5)
+    gam = S.gamma(43, k)
+    eps = 1e-6
+    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_RMSNORM, torch.from_numpy(x).cuda(),
+                                   gamma=torch.from_numpy(gam).cuda(), eps=eps)
+    y_pub = sk.sk_gemm_fused_rmsnorm(w, torch.from_numpy(x).cuda(), torch.from_numpy(gam).cuda(), eps)
+    torch.cuda.synchronize()
+    h = O.prologue_rmsnorm(x, gam, eps)
+    ref = O.reference(fmt, buf, n, k, g, h)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"])
+    assert_y_close(y.cpu().numpy(), ref)
+    assert torch.equal(y, y_pub)
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_fused_swiglu(m, xt):
+    n, k, g = 256, 12288, 32
+    w, buf = gpu_weight(0, n, k, g, 51)
+    sk.sk_repack_w4a8(w)
+    gu = np.concatenate([S.activations(52 + m, m, k), S.activations(62 + m, m, k)], axis=1)
+    gu[:, :64] *= 30.0                                     # reach the exp overflow branch
+    dev, ref_vals = to_dev(np.ascontiguousarray(gu), xt)
+    gate, up = dev[:, :k], dev[:, k:]
+    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_SWIGLU, gate, x2=up)
+    y_pub = sk.sk_gemm_fused_swiglu(w, gate, up)
+    torch.cuda.synchronize()
+    h = O.prologue_swiglu(ref_vals[:, :k], ref_vals[:, k:])
+    ref = O.reference(0, buf, n, k, g, h)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"])
+    assert_y_close(y.cpu().numpy(), ref)
+    assert torch.equal(y, y_pub)
+
+
+# ----------------------------------------------------------------------------
+# full decoder shapes, sampled rows
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,n,k", [("qkv", 6144, 4096), ("o", 4096, 4096),
+                                      ("gate_up", 24576, 4096), ("down", 4096, 12288)])
+def test_decoder_shapes_sampled(name, n, k):
+    g = 32
+    w, buf = gpu_weight(0, n, k, g, 1000 + n // 16)
+    sk.sk_repack_w4a8(w)
+    rows = np.sort(np.random.default_rng(n).choice(n, size=96, replace=False))
+    vals, s = O.split_canonical(buf, 0, n, k, g)
+    for m in (1, 8):
+        x = S.activations(1002 + m, m, k)
+        y = sk.sk_gemm_w4a8(w, torch.from_numpy(x).cuda()).cpu().numpy()
+        q, sx = O.quantize_rows(x)
+        p = O.group_partials(vals[rows], q, g)
+        ref = {"Y": O.output(p, s[rows], sx), "mag": O.output_magnitude(p, s[rows], sx)}
+        assert_y_close(y[:, rows], ref)
