@@ -31,7 +31,8 @@ BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
 # Every symbol include/sk_repack.h and include/sk_repack_test.h declare.
 EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4a8",
            "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu", "sk_debug_gemm",
-           "sk_test_repack_on_host"]
+           "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
+           "sk_test_set_spin_limit"]
 
 
 class SkWeightStruct(ctypes.Structure):
@@ -64,6 +65,9 @@ def _load() -> ctypes.CDLL:
         "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P], I),
         "sk_debug_gemm": ([W, I, P, P, I64, I, P, F, I, P, P, P, P, P], I),
         "sk_test_repack_on_host": ([W, P, I], I),
+        "sk_test_gemm_plan": ([I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_int64)], I),
+        "sk_test_set_split": ([I], I),
+        "sk_test_set_spin_limit": ([I], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -200,3 +204,26 @@ def sk_debug_gemm(w: QuantWeight, prologue: int, x: torch.Tensor, x2=None, gamma
                              _ptr(gamma), ctypes.c_float(eps), m, _ptr(y), _ptr(q), _ptr(sx),
                              _ptr(p), _stream(stream)), "sk_debug_gemm")
     return y, q, sx, p
+
+
+PLAN_FIELDS = ["S", "R", "P", "TW", "KW", "spw", "KBs", "KS", "WPR", "lds", "part_floats"]
+
+
+def gemm_plan(n: int, k: int, group: int, fmt: int, m: int, cus: int = 256,
+              prologue: int = PRO_NONE) -> dict:
+    """The launch plan of a GEMM call (test hook; host arithmetic only)."""
+    f = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    st = LIB.sk_test_gemm_plan(n, k, group, fmt, m, prologue, cus, f)
+    out = dict(zip(PLAN_FIELDS, list(f)))
+    out["status"] = st
+    return out
+
+
+def set_split(s: int) -> None:
+    """Test hook: force the number of K-slices (0 = automatic)."""
+    _check(LIB.sk_test_set_split(s), "sk_test_set_split")
+
+
+def set_spin_limit(polls: int) -> None:
+    """Test hook: exchange polls before the local fallback (0 = default)."""
+    _check(LIB.sk_test_set_spin_limit(polls), "sk_test_set_spin_limit")

@@ -55,6 +55,8 @@ sk_status check_weight(const sk_weight* w) {
 
 sk_status from_hip(hipError_t e) { return e == hipSuccess ? SK_OK : SK_ERR_HIP; }
 
+int g_spin_limit = 0;   // test hook: exchange polls before the local fallback (0 = default)
+
 // Checks for the GEMM entry points, then the launch.
 sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* x, const void* x2,
                    int64_t ld, int xt, const float* gamma, float eps, int m, float* y,
@@ -83,7 +85,7 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     if (w->layout != SK_LAYOUT_STREAM) return SK_ERR_LAYOUT;
     const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
     if (w->format == SK_W4_CODEBOOK) return SK_ERR_UNSUPPORTED;
-    if (sk::gemm_lds_bytes(G, m) > 160 * 1024) return SK_ERR_UNSUPPORTED;
+    if (!sk::gemm_plan_ok(G, m, prologue)) return SK_ERR_UNSUPPORTED;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p_out) {
@@ -105,6 +107,7 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     c.q_out = q_out;
     c.sx_out = sx_out;
     c.p_out = p_out;
+    c.spin_limit = g_spin_limit;
     return from_hip(sk::launch_gemm(G, c, st));
 }
 
@@ -190,4 +193,30 @@ SK_EXPORT sk_status sk_test_repack_on_host(const sk_weight* w, void* host_bytes,
     const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
     return sk::repack_host(static_cast<uint8_t*>(host_bytes), G, inverse != 0) ? SK_OK
                                                                                : SK_ERR_SHAPE;
+}
+
+SK_EXPORT sk_status sk_test_gemm_plan(int n, int k, int group, int format, int m, int prologue,
+                                      int cus, int64_t* fields) {
+    if (!fields) return SK_ERR_NULL;
+    if (n < 1 || k < 128 || k % 128 != 0 || group < 16 || 128 % group != 0 || m < 1 || m > 8 ||
+        cus < 1 || prologue < 0 || prologue > 2)
+        return SK_ERR_SHAPE;
+    const Geom G = sk::make_geom(n, k, group, format);
+    const sk::Plan p = sk::make_plan(G, m, prologue, cus, 0);
+    const int64_t v[11] = {p.S, p.R, p.P, p.TW, p.KW, p.spw, p.KBs, p.KS, p.WPR, (int64_t)p.lds,
+                           (int64_t)p.part_floats};
+    for (int i = 0; i < 11; ++i) fields[i] = v[i];
+    return p.ok ? SK_OK : SK_ERR_UNSUPPORTED;
+}
+
+SK_EXPORT sk_status sk_test_set_split(int s) {
+    if (s < 0 || s > 32) return SK_ERR_SHAPE;
+    sk::set_split_override(s);
+    return SK_OK;
+}
+
+SK_EXPORT sk_status sk_test_set_spin_limit(int polls) {
+    if (polls < 0) return SK_ERR_SHAPE;
+    g_spin_limit = polls;
+    return SK_OK;
 }

@@ -32,12 +32,42 @@ struct GemmCall {
     int8_t* q_out;         // debug exports (may be null)
     float* sx_out;
     int32_t* p_out;
+    int spin_limit;        // polls of an exchange slot before computing it locally (0 = default)
 };
 
-// Largest K a GEMM call accepts (the int8 activations of all M rows live in LDS).
+// Largest K a GEMM call accepts.
 constexpr int64_t kMaxGemmK = 17408;
 
-size_t gemm_lds_bytes(const Geom& G, int m);
+// Device workspace header (zeroed once when allocated).  `gen` counts launches
+// that used the cross-slice exchange; slots carry gen + 1 as their tag.
+struct WsHeader {
+    uint32_t gen;
+    uint32_t done;
+    uint32_t pad[30];
+    unsigned long long amax[32 * 8];   // (tag << 32) | float bits, [slice][row]
+    unsigned long long ssh[32 * 8];    // (tag << 32) | high half of the double sum of squares
+    unsigned long long ssl[32 * 8];    // (tag << 32) | low half
+};
+
+// How one GEMM call is laid out on the GPU (pure host arithmetic).
+struct Plan {
+    int S;        // K-slices (a divisor of K/128, at most 32)
+    int R;        // workgroups per slice
+    int P;        // workgroups = S * R
+    int TW, KW;   // waves = TW tile groups x KW waves along k
+    int spw;      // super-blocks per wave per tile
+    int KBs;      // super-blocks per slice
+    int KS;       // K per slice
+    int WPR;      // waves per activation row in the prologue
+    int ks;       // LDS row stride of q
+    size_t lds;   // dynamic LDS bytes
+    size_t part_floats;  // workspace floats for slice partials
+    bool ok;
+};
+
+Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override);
+bool gemm_plan_ok(const Geom& G, int m, int pro);
+void set_split_override(int s);
 hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st);
 
 }  // namespace sk

@@ -22,7 +22,18 @@
  *
  * Conventions for every entry point
  *  - All pointers except `sk_weight*` itself are DEVICE pointers to memory the
- *    caller owns.  The library allocates and frees no device memory.
+ *    caller owns.  The repack entry points allocate no device memory.  The
+ *    GEMM entry points share one per-device workspace: a header of about 6 KiB (a
+ *    generation counter and the activation-statistics exchange), a 4-byte
+ *    arrival counter per 16-row tile and, for launches that split K into S
+ *    slices, 8 bytes per (slice, output element).  It is allocated and zeroed
+ *    by the first GEMM call on the device and grown (with a device
+ *    synchronisation) by the first call that needs more, so such a call must
+ *    not be inside a stream capture; it is kept until the process ends.  A
+ *    call that fits the current workspace allocates nothing (graph capture of
+ *    such calls works).  GEMM calls on one device must not overlap in time:
+ *    issue them on one stream, or order them with events.  Every launch
+ *    leaves the workspace in the state the next launch expects.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls only enqueue work and return; nothing synchronises the host.
  *  - Validation is synchronous and happens before any GPU work: on any status

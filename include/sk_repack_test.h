@@ -26,6 +26,29 @@ extern "C" {
  */
 sk_status sk_test_repack_on_host(const sk_weight* w, void* host_bytes, int inverse);
 
+/*
+ * The launch plan the library would use for a GEMM call with this shape, M,
+ * prologue (0 none, 1 RMSNorm, 2 SwiGLU) and compute-unit count (host
+ * arithmetic only).  fields[0..10] receive
+ * S (K-slices), R (workgroups per slice), P (workgroups), TW (tile groups per
+ * workgroup), KW (waves along k), super-blocks per wave per tile,
+ * super-blocks per slice, K per slice, waves per activation row, dynamic LDS
+ * bytes and workspace floats for slice partials.  SK_ERR_UNSUPPORTED if no
+ * plan exists; SK_ERR_SHAPE for shapes outside the backend's range.
+ */
+sk_status sk_test_gemm_plan(int n, int k, int group, int format, int m, int prologue, int cus,
+                            int64_t* fields);
+
+/* Forces the number of K-slices of later GEMM calls (1..32; 0 restores the
+ * automatic choice).  Calls whose K/128 the forced value does not divide, or
+ * whose slice does not fit the kernel's layout, return SK_ERR_UNSUPPORTED. */
+sk_status sk_test_set_split(int s);
+
+/* Number of polls of a cross-slice exchange slot before a workgroup computes
+ * that slice's statistics itself (0 restores the default).  A small value
+ * forces the local path, which must give identical results. */
+sk_status sk_test_set_spin_limit(int polls);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ Sources (web pages; cited by title and section):
   shape rules.  Section "激活与平滑" (activations and smoothing): integer
   formats take float activations and quantise them in the kernel.
 
-Readings where the pages are silent (each one is listed in the design doc):
+Readings where the pages are silent:
 
 * Canonical bit encodings (the format table is missing from the page): see
   ``decode_w4``, ``decode_w6``, ``decode_u4``.

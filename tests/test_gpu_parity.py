@@ -154,15 +154,15 @@ def test_rows_do_not_interact_and_runs_repeat():
     y8b = sk.sk_gemm_w4a8(w, x)
     torch.cuda.synchronize()
     assert torch.equal(y8, y8b)                        # deterministic
-    for m in range(2, 8):                              # same MFMA path: bit-identical rows
-        ym = sk.sk_gemm_w4a8(w, x[:m].contiguous())
-        torch.cuda.synchronize()
-        assert torch.equal(ym, y8[:m])
     ref = O.reference(0, buf, n, k, g, x.cpu().numpy())
-    for mi in range(8):                                # M = 1 (dot4 path): within tolerance
-        y1 = sk.sk_gemm_w4a8(w, x[mi:mi + 1].contiguous())
+    for m in range(1, 8):
+        # q and the integer partials of a row never depend on M; y may differ in the
+        # last bits because M selects the K-split (fp32 summation order)
+        ym, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_NONE, x[:m].contiguous())
         torch.cuda.synchronize()
-        assert_y_close(y1.cpu().numpy(), {"Y": ref["Y"][mi:mi + 1], "mag": ref["mag"][mi:mi + 1]})
+        assert np.array_equal(q.cpu().numpy(), ref["q"][:m])
+        assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"][:m])
+        assert_y_close(ym.cpu().numpy(), {"Y": ref["Y"][:m], "mag": ref["mag"][:m]})
 
 
 # ----------------------------------------------------------------------------
@@ -232,3 +232,107 @@ def test_decoder_shapes_sampled(name, n, k):
         p = O.group_partials(vals[rows], q, g)
         ref = {"Y": O.output(p, s[rows], sx), "mag": O.output_magnitude(p, s[rows], sx)}
         assert_y_close(y[:, rows], ref)
+
+
+# ----------------------------------------------------------------------------
+# K-split variants: cross-slice exchange and last-arriver merge
+# ----------------------------------------------------------------------------
+
+@pytest.fixture
+def reset_hooks():
+    yield
+    sk.set_split(0)
+    sk.set_spin_limit(0)
+
+
+def run_prologue(w, pro, k, m, seed):
+    """Returns (debug outputs, oracle reference) for one prologue kind."""
+    if pro == sk.PRO_SWIGLU:
+        gu = np.concatenate([S.activations(seed, m, k), S.activations(seed + 1, m, k)], axis=1)
+        dev = torch.from_numpy(np.ascontiguousarray(gu)).cuda()
+        out = sk.sk_debug_gemm(w, pro, dev[:, :k], x2=dev[:, k:])
+        h = O.prologue_swiglu(gu[:, :k], gu[:, k:])
+    elif pro == sk.PRO_RMSNORM:
+        x = S.activations(seed, m, k)
+        gam = S.gamma(seed + 2, k)
+        out = sk.sk_debug_gemm(w, pro, torch.from_numpy(x).cuda(),
+                               gamma=torch.from_numpy(gam).cuda(), eps=1e-6)
+        h = O.prologue_rmsnorm(x, gam, 1e-6)
+    else:
+        x = S.activations(seed, m, k)
+        out = sk.sk_debug_gemm(w, pro, torch.from_numpy(x).cuda())
+        h = x
+    torch.cuda.synchronize()
+    return out, h
+
+
+def assert_bit_exact(out, ref):
+    y, q, sx, p = out
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"])
+    assert_y_close(y.cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("split", [1, 2, 4, 8, 16])
+@pytest.mark.parametrize("pro", [sk.PRO_NONE, sk.PRO_RMSNORM, sk.PRO_SWIGLU])
+def test_forced_split_matches_oracle(split, pro, reset_hooks):
+    n, k, g = 520, 4096, 32
+    w, buf = gpu_weight(0, n, k, g, 71)
+    sk.sk_repack_w4a8(w)
+    sk.set_split(split)
+    ran = 0
+    for m in (1, 3, 8):
+        # a forced split must still fit the kernel's register layout
+        sk.set_split(0)
+        p = sk.gemm_plan(n, k, g, 0, m, prologue=pro)
+        sk.set_split(split)
+        tpr = (16 // m) * 64
+        if (k // split) // 8 > tpr * 2:
+            with pytest.raises(sk.SkError):
+                run_prologue(w, pro, k, m, 72 + m)
+            continue
+        ran += 1
+        out, h = run_prologue(w, pro, k, m, 72 + m)
+        assert_bit_exact(out, O.reference(0, buf, n, k, g, h))
+    assert ran >= 1
+
+
+@pytest.mark.parametrize("pro", [sk.PRO_NONE, sk.PRO_RMSNORM, sk.PRO_SWIGLU])
+def test_exchange_local_fallback_is_identical(pro, reset_hooks):
+    n, k, g = 1040, 4096, 32
+    w, buf = gpu_weight(0, n, k, g, 81)
+    sk.sk_repack_w4a8(w)
+    sk.set_split(8)
+    fast, h = run_prologue(w, pro, k, 8, 82)
+    sk.set_spin_limit(1)                      # almost every slot times out -> computed locally
+    slow, _ = run_prologue(w, pro, k, 8, 82)
+    for a, b in zip(fast, slow):
+        assert torch.equal(a, b)
+    assert_bit_exact(slow, O.reference(0, buf, n, k, g, h))
+
+
+def test_back_to_back_calls_in_one_graph(reset_hooks):
+    """Repeated launches reuse the exchange slots and merge counters; replaying
+    a captured graph with new activations must still match the oracle."""
+    n, k, g = 2048, 4096, 32
+    w, buf = gpu_weight(0, n, k, g, 91)
+    sk.sk_repack_w4a8(w)
+    x = torch.zeros((8, k), dtype=torch.float32, device="cuda")
+    ys = [torch.empty((8, n), dtype=torch.float32, device="cuda") for _ in range(3)]
+    x.copy_(torch.from_numpy(S.activations(92, 8, k)))
+    sk.sk_gemm_w4a8(w, x, y=ys[0])            # warm: workspace allocated outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for y in ys:
+            sk.sk_gemm_w4a8(w, x, y=y)
+    for rep in range(4):
+        xh = S.activations(93 + rep, 8, k)
+        x.copy_(torch.from_numpy(xh))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = O.reference(0, buf, n, k, g, xh)
+        for y in ys:
+            assert_y_close(y.cpu().numpy(), ref)
+        assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])

@@ -1,0 +1,86 @@
+"""The GEMM launch planner on the host: every plan the library would launch is
+inside the kernel's assumptions, and the work it assigns covers every
+(tile, super-block) of the weight exactly once."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import gemm_sk_repack_amd as sk
+
+NW, MO = 16, 2
+
+SHAPES = [
+    # n, k, g, fmt
+    (1024, 1024, 32, 0), (6144, 4096, 32, 0), (4096, 4096, 32, 0), (24576, 4096, 32, 0),
+    (4096, 12288, 32, 0), (12288, 4096, 64, 2), (151936, 4096, 32, 0), (7168, 5120, 32, 0),
+    (5120, 5120, 32, 0), (34816, 5120, 32, 0), (5120, 17408, 32, 0), (17, 256, 64, 0),
+    (5, 128, 128, 0), (1000, 512, 32, 0), (300, 1024, 64, 2),
+]
+
+
+@pytest.mark.parametrize("n,k,g,fmt", SHAPES)
+@pytest.mark.parametrize("m", range(1, 9))
+@pytest.mark.parametrize("pro", [sk.PRO_NONE, sk.PRO_RMSNORM, sk.PRO_SWIGLU])
+def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
+    p = sk.gemm_plan(n, k, g, fmt, m, prologue=pro)
+    assert p["status"] == sk.SK_OK, p
+    T, KB = (n + 15) // 16, k // 128
+    S = p["S"]
+    assert 1 <= S <= 32 and KB % S == 0
+    assert p["KBs"] == KB // S and p["KS"] == k // S
+    assert p["P"] == S * p["R"] and p["P"] <= 256 and 1 <= p["R"] <= T
+    assert p["WPR"] == NW // m
+    assert p["KS"] // 8 <= p["WPR"] * 64 * MO              # the slice fits the registers
+    assert p["TW"] * p["KW"] <= NW and p["TW"] * m * 16 <= NW * 64
+    assert p["spw"] * p["KW"] == p["KBs"]
+    assert p["lds"] <= 150 * 1024
+    if m == 1 and k <= 16384:
+        assert S == 1                                        # no cross-slice merge at M = 1
+    assert p["part_floats"] == (T * S * m * 16 if S > 1 else 0)
+
+
+def covered(n, k, m, p):
+    """Simulate the kernel's work assignment; count visits per (tile, super-block)."""
+    T, KB = (n + 15) // 16, k // 128
+    seen = np.zeros((T, KB), dtype=np.int64)
+    for blk in range(p["P"]):
+        s, r = blk // p["R"], blk % p["R"]
+        t0, t1 = r * T // p["R"], (r + 1) * T // p["R"]
+        ntile = t1 - t0
+        jn = (ntile + p["TW"] - 1) // p["TW"]
+        for wv in range(NW):
+            tg, kw = wv // p["KW"], wv % p["KW"]
+            if tg >= p["TW"]:
+                continue
+            for i in range(jn * p["spw"]):
+                t = t0 + tg + (i // p["spw"]) * p["TW"]
+                if t >= t1:
+                    continue
+                kb = s * p["KBs"] + kw * p["spw"] + i % p["spw"]
+                seen[t, kb] += 1
+    return seen
+
+
+@pytest.mark.parametrize("n,k,g,fmt", [s for s in SHAPES if s[0] <= 34816])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_work_covers_every_superblock_once(n, k, g, fmt, m):
+    p = sk.gemm_plan(n, k, g, fmt, m)
+    assert np.all(covered(n, k, m, p) == 1)
+
+
+@pytest.mark.parametrize("cus", [1, 7, 64, 80, 256, 304])
+def test_plans_for_other_cu_counts(cus):
+    for (n, k, g, fmt), m in itertools.product(SHAPES[:6], (1, 8)):
+        p = sk.gemm_plan(n, k, g, fmt, m, cus)
+        assert p["status"] == sk.SK_OK
+        assert p["P"] <= max(cus, p["S"]) and np.all(covered(n, k, m, p) == 1)
+
+
+def test_forced_split_hook_validates():
+    with pytest.raises(sk.SkError):
+        sk.set_split(33)
+    with pytest.raises(sk.SkError):
+        sk.set_split(-1)
+    sk.set_split(0)
