@@ -46,7 +46,6 @@ constexpr int NW = 16;         // waves per workgroup
 constexpr int NT = NW * 64;    // threads per workgroup
 constexpr int PIPE = 4;        // super-blocks in flight per wave
 constexpr int PRIME = 2;       // of which issued before the activation prologue
-constexpr int MO = 2;          // activation octets per thread
 constexpr int SMAX = 32;       // largest number of K-slices
 constexpr int kMaxTilesPerGroup = 64;
 
@@ -68,17 +67,30 @@ struct KArgs {
     u64* part;
     int n, k, m;
     int T, KB, kg;
-    int sb_row, wsb_row;
-    int64_t tile_full;
     int S, R, P, TW, KW, spw, KBs, KS, WPR, ks;
     int spin_limit;
+    // tiles of block r: [r * tq + min(r, trem), ... + tq + (r < trem)); jn1 / jn0
+    // = tiles per tile group, rounded up, for the two block sizes
+    int tq, trem, jn0, jn1;
+    // stream-layout addressing: full tiles (16 rows) and the ragged last tile
+    int64_t tile_full;      // bytes per full tile
+    int64_t tstep;          // TW * tile_full - spw * sbf: from a tile's last slot to the next tile
+    int sbf, swo;           // bytes per super-block of a full tile; offset of its scales
+    int cpr, tpr;           // activation chunks per row of the slice; threads per row
+    int t_rag;              // index of the ragged tile, -1 if N % 16 == 0
+    int nr_last;            // rows of the ragged tile (16 if none)
+    int64_t rag_w, rag_s;   // byte offsets of the ragged tile's weights and scales
+    int rag_sbw, rag_sbs;   // their bytes per super-block
+    // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
+    // wave index within the row (14-18) and activation chunk steps (19-21)
+    uint32_t wtab[NW];
 };
 
 struct Smem {
-    double wd[NW];
-    float wf[NW];
-    double exd[SMAX * 8];
-    float exf[SMAX * 8];
+    alignas(16) double wd[NW];          // per-wave values
+    alignas(16) float wf[NW];
+    alignas(16) double exd[8 * SMAX];   // [row][slice] statistics of the slices
+    alignas(16) float exf[8 * SMAX];
     float sx[8];
     float inv[8];
     float rr[8];
@@ -148,100 +160,227 @@ __device__ inline float rms_apply(float x, float r, float g) {
     return t * g;
 }
 
-// q = clamp(rint(fp32(h / sx)), -127, 127), bit-exactly, for sx > 0.
-// t = h * inv with inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here)
-// of h/sx, and fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t)
-// equals rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only
-// then (or for a tiny sx) is the quotient formed by IEEE division.
-__device__ inline int quant1(float h, float sx, float inv, bool exact_row) {
-    float t = h * inv;
-    float r = __builtin_rintf(t);
-    if (exact_row || fabsf(t - r) > 0.49998f) {
-        t = h / sx;
-        r = __builtin_rintf(t);
-    }
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (int)r;
-}
-
 #pragma clang fp contract(on)
 
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+// ---- cross-lane reductions (DPP within 16-lane rows, then the four rows) ----
+template <int CTRL>
+__device__ inline int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
 }
-__device__ inline double wave_sum(double v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within 8 lanes
+constexpr int DPP_MIRROR = 0x140;   // lane i <-> 15 - i within 16 lanes
+
+// Sum over aligned groups of L lanes (L = 1, 2, 4, 8, 16, 32); every lane of a
+// group gets the group's sum.  Integer adds, so the order does not matter.
+template <int L>
+__device__ inline int lane_group_sum(int v) {
+    if (L >= 2) v += dpp<DPP_XOR1>(v);
+    if (L >= 4) v += dpp<DPP_XOR2>(v);
+    if (L >= 8) v += dpp<DPP_HMIRROR>(v);
+    if (L >= 16) v += dpp<DPP_MIRROR>(v);
+    if (L >= 32) v += __builtin_amdgcn_ds_swizzle(v, 0x401F);   // lane ^ 16 within 32
     return v;
 }
 
-// Thread -> activation mapping: row m = wave / WPR (WPR waves per row); the
-// thread's octets of the slice are it and it + TPR (it = index in the row).
-struct ActMap {
-    int m;       // row, or >= M if the thread holds no activations
-    int it;      // index within the row's threads
-    int tpr;     // threads per row
+// Max over the wave (wave-uniform result).
+__device__ inline float wave_max(float v) {
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_HMIRROR>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_MIRROR>(__float_as_int(v))));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+template <int CTRL>
+__device__ inline double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp<CTRL>((int)(b & 0xFFFFFFFFll));
+    const int hi = dpp<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ inline double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// Sum over the wave in one fixed tree order (wave-uniform result).
+__device__ inline double wave_sum(double v) {
+    v += dpp_d<DPP_XOR1>(v);
+    v += dpp_d<DPP_XOR2>(v);
+    v += dpp_d<DPP_HMIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
+// Thread -> activation mapping.  Each thread holds up to NCH 16-byte chunks of
+// its row's slice (a chunk is 4 fp32 or 8 bf16 elements): WPR waves per row,
+// row m = wave / WPR, chunk c = it + i * TPR for i < NCH.  `nw` counts the
+// iterations i in which the wave has at least one chunk, so a wave skips the
+// rest with a uniform branch.
+template <int XT>
+struct Act {
+    static constexpr int E = XT == 0 ? 4 : 8;      // elements per chunk
+    static constexpr int NCH = XT == 0 ? 4 : 2;    // chunks per thread (16 elements)
+    static constexpr int ES = XT == 0 ? 4 : 2;     // bytes per element
+    int m;      // row of this wave; >= M: the wave holds no activations
+    int it;     // thread index within the row
+    int tpr;    // threads per row
+    int cpr;    // chunks per row of the slice
+    int nw;     // wave-uniform
 };
 
-__device__ inline ActMap act_map(const KArgs& a, int wv, int lane) {
-    ActMap am;
-    am.m = wv / a.WPR;
-    am.it = (wv % a.WPR) * 64 + lane;
-    am.tpr = a.WPR * 64;
+template <int XT>
+__device__ inline Act<XT> act_map(const KArgs& a, uint32_t wt, int lane) {
+    Act<XT> am;
+    am.m = (wt >> 10) & 15;
+    am.it = ((wt >> 14) & 31) * 64 + lane;
+    am.tpr = a.tpr;
+    am.cpr = a.cpr;
+    am.nw = (wt >> 19) & 7;
     return am;
 }
 
-__device__ inline bool oct_valid(const KArgs& a, const ActMap& am, int i) {
-    return am.m < a.m && am.it + i * am.tpr < (a.KS >> 3);
-}
-
-// Raw activations of slice [k_lo, k_lo + KS) (SwiGLU: gate in xv, up in uv).
-// Unconditional loads: an invalid octet reads element 0 and is zeroed later.
+// Raw 16-byte chunks of slice [k_lo, k_lo + KS) (SwiGLU: gate in xr, up in ur).
 template <int PRO, int XT>
-__device__ inline void load_act(const KArgs& a, const ActMap& am, int k_lo, float xv[MO][8],
-                                float uv[MO][8]) {
+__device__ inline void load_act(const KArgs& a, const Act<XT>& am, int k_lo,
+                                uint4 xr[Act<XT>::NCH], uint4 ur[Act<XT>::NCH]) {
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x);
+    const uint8_t* ub = static_cast<const uint8_t*>(a.x2);
 #pragma unroll
-    for (int i = 0; i < MO; ++i) {
-        const bool ok = oct_valid(a, am, i);
-        const int64_t off = ok ? (int64_t)am.m * a.ld + k_lo + 8 * (am.it + i * am.tpr) : 0;
-        load8<XT>(a.x, off, xv[i]);
-        if (PRO == PRO_SWIGLU) load8<XT>(a.x2, off, uv[i]);
-    }
-}
-
-// Turn loaded raw values into h (SwiGLU) and zero invalid octets.
-template <int PRO>
-__device__ inline void finish_act(const KArgs& a, const ActMap& am, float xv[MO][8], float uv[MO][8]) {
-#pragma unroll
-    for (int i = 0; i < MO; ++i) {
-        const bool ok = oct_valid(a, am, i);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float h = xv[i][e];
-            if (PRO == PRO_SWIGLU) h = silu_mul(xv[i][e], uv[i][e]);
-            xv[i][e] = ok ? h : 0.0f;
+    for (int i = 0; i < Act<XT>::NCH; ++i) {
+        xr[i] = make_uint4(0u, 0u, 0u, 0u);
+        ur[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (i < am.nw) {
+            const int c = am.it + i * am.tpr;
+            const int cc = c < am.cpr ? c : 0;
+            const int64_t off = ((int64_t)am.m * a.ld + k_lo + (int64_t)cc * Act<XT>::E) * Act<XT>::ES;
+            xr[i] = *reinterpret_cast<const uint4*>(xb + off);
+            if (PRO == PRO_SWIGLU) ur[i] = *reinterpret_cast<const uint4*>(ub + off);
         }
     }
 }
 
-__device__ inline void row_sum_d(Smem& sm, int wv, int lane, double v) {
-    v = wave_sum(v);
-    if (lane == 0) sm.wd[wv] = v;
+template <int XT>
+__device__ inline void load_gamma(const KArgs& a, const Act<XT>& am, int k_lo,
+                                  float g[Act<XT>::NCH * Act<XT>::E]) {
+    constexpr int E = Act<XT>::E;
+#pragma unroll
+    for (int i = 0; i < Act<XT>::NCH; ++i) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) g[i * E + e] = 0.0f;
+        if (i < am.nw) {
+            const int c = am.it + i * am.tpr;
+            const int cc = c < am.cpr ? c : 0;
+            const float4* gp = reinterpret_cast<const float4*>(a.gamma + k_lo + (int64_t)cc * E);
+#pragma unroll
+            for (int v = 0; v < E / 4; ++v) {
+                const float4 t = gp[v];
+                g[i * E + 4 * v] = t.x; g[i * E + 4 * v + 1] = t.y;
+                g[i * E + 4 * v + 2] = t.z; g[i * E + 4 * v + 3] = t.w;
+            }
+        }
+    }
 }
-__device__ inline void row_max_f(Smem& sm, int wv, int lane, float v) {
-    v = wave_max(v);
-    if (lane == 0) sm.wf[wv] = v;
+
+// h values of the thread's chunks (SwiGLU applied); invalid elements are 0.
+template <int PRO, int XT>
+__device__ inline void finish_act(const Act<XT>& am, const uint4 xr[Act<XT>::NCH],
+                                  const uint4 ur[Act<XT>::NCH], float h[Act<XT>::NCH * Act<XT>::E]) {
+    constexpr int E = Act<XT>::E;
+#pragma unroll
+    for (int i = 0; i < Act<XT>::NCH; ++i) {
+        const bool ok = i < am.nw && am.it + i * am.tpr < am.cpr;
+        const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        const uint32_t uw[4] = {ur[i].x, ur[i].y, ur[i].z, ur[i].w};
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float xv, uv;
+            if (XT == 0) {
+                xv = __uint_as_float(xw[e]);
+                uv = __uint_as_float(uw[e]);
+            } else {
+                xv = __uint_as_float((e & 1) ? (xw[e >> 1] & 0xFFFF0000u) : (xw[e >> 1] << 16));
+                uv = __uint_as_float((e & 1) ? (uw[e >> 1] & 0xFFFF0000u) : (uw[e >> 1] << 16));
+            }
+            const float v = (PRO == PRO_SWIGLU) ? silu_mul(xv, uv) : xv;
+            h[i * E + e] = ok ? v : 0.0f;
+        }
+    }
 }
+
+template <int XT>
+__device__ inline double sum_sq(const float h[Act<XT>::NCH * Act<XT>::E]) {
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < Act<XT>::NCH * Act<XT>::E; ++j) ss += (double)h[j] * (double)h[j];
+    return ss;
+}
+template <int XT>
+__device__ inline float abs_max(const float h[Act<XT>::NCH * Act<XT>::E]) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Act<XT>::NCH * Act<XT>::E; ++j) mx = fmaxf(mx, fabsf(h[j]));
+    return mx;
+}
+
+// A row's slice statistic from its waves' values, in wave order.
 __device__ inline double combine_d(const KArgs& a, const Smem& sm, int m) {
+    const int lo = m * a.WPR, hi = lo + a.WPR;
+    const double2* p = reinterpret_cast<const double2*>(sm.wd);
+    double v[NW];
+#pragma unroll
+    for (int q = 0; q < NW / 2; ++q) {
+        const double2 t = p[q];
+        v[2 * q] = t.x;
+        v[2 * q + 1] = t.y;
+    }
     double s = 0.0;
-    for (int w = m * a.WPR; w < (m + 1) * a.WPR; ++w) s += sm.wd[w];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s = (w >= lo && w < hi) ? s + v[w] : s;
     return s;
 }
 __device__ inline float combine_f(const KArgs& a, const Smem& sm, int m) {
+    const int lo = m * a.WPR, hi = lo + a.WPR;
+    const float4* p = reinterpret_cast<const float4*>(sm.wf);
     float s = 0.0f;
-    for (int w = m * a.WPR; w < (m + 1) * a.WPR; ++w) s = fmaxf(s, sm.wf[w]);
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+        const float4 t = p[q];
+        const float e[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (4 * q + k >= lo && 4 * q + k < hi) s = fmaxf(s, e[k]);
+    }
+    return s;
+}
+// Row m's statistic over all slices (S > 1), slices in ascending order.
+__device__ inline double slices_sum(const KArgs& a, const Smem& sm, int m) {
+    const double2* p = reinterpret_cast<const double2*>(sm.exd + m * SMAX);
+    double s = 0.0;
+    for (int q = 0; q < a.S; q += 2) {
+        const double2 t = p[q >> 1];
+        s += t.x;
+        if (q + 1 < a.S) s += t.y;
+    }
+    return s;
+}
+__device__ inline float slices_max(const KArgs& a, const Smem& sm, int m) {
+    const float4* p = reinterpret_cast<const float4*>(sm.exf + m * SMAX);
+    float s = 0.0f;
+    for (int q = 0; q < a.S; q += 4) {
+        const float4 t = p[q >> 2];
+        s = fmaxf(s, t.x);
+        if (q + 1 < a.S) s = fmaxf(s, t.y);
+        if (q + 2 < a.S) s = fmaxf(s, t.z);
+        if (q + 3 < a.S) s = fmaxf(s, t.w);
+    }
     return s;
 }
 
@@ -249,59 +388,58 @@ __device__ inline float combine_f(const KArgs& a, const Smem& sm, int m) {
 // arrive in time.  Same thread mapping and summation order as the workgroups
 // that own that slice, so the result is bit-identical.  All threads call it.
 template <int PRO, int XT>
-__device__ inline void slice_stat(const KArgs& a, Smem& sm, int wv, int lane, int sl, bool want_ss) {
-    const ActMap am = act_map(a, wv, lane);
-    float xv[MO][8], uv[MO][8];
-    load_act<PRO, XT>(a, am, sl * a.KS, xv, uv);
-    finish_act<PRO>(a, am, xv, uv);
+__device__ inline void slice_stat(const KArgs& a, Smem& sm, uint32_t wt, int lane, int wv, int sl,
+                                  bool want_ss) {
+    constexpr int E = Act<XT>::E;
+    const Act<XT> am = act_map<XT>(a, wt, lane);
+    uint4 xr[Act<XT>::NCH], ur[Act<XT>::NCH];
+    float h[Act<XT>::NCH * E];
+    load_act<PRO, XT>(a, am, sl * a.KS, xr, ur);
+    finish_act<PRO, XT>(am, xr, ur, h);
     if (want_ss) {
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < MO; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss += (double)xv[i][e] * (double)xv[i][e];
-        row_sum_d(sm, wv, lane, ss);
+        const double ss = wave_sum(sum_sq<XT>(h));
+        if (lane == 0) sm.wd[wv] = ss;
     } else {
-        float mx = 0.0f;
-        const float r = (am.m < a.m) ? sm.rr[am.m] : 1.0f;
+        if (PRO == PRO_RMSNORM) {
+            float g[Act<XT>::NCH * E];
+            load_gamma<XT>(a, am, sl * a.KS, g);
+            const float r = (am.m < a.m) ? sm.rr[am.m] : 1.0f;
 #pragma unroll
-        for (int i = 0; i < MO; ++i) {
-            const int k0 = sl * a.KS + 8 * (am.it + i * am.tpr);
-            const bool ok = oct_valid(a, am, i);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float h = xv[i][e];
-                if (PRO == PRO_RMSNORM && ok) h = rms_apply(h, r, a.gamma[k0 + e]);
-                mx = fmaxf(mx, fabsf(h));
-            }
+            for (int j = 0; j < Act<XT>::NCH * E; ++j) h[j] = rms_apply(h[j], r, g[j]);
         }
-        row_max_f(sm, wv, lane, mx);
+        const float mx = wave_max(abs_max<XT>(h));
+        if (lane == 0) sm.wf[wv] = mx;
     }
     __syncthreads();
     if (threadIdx.x < a.m) {
-        if (want_ss) sm.exd[sl * 8 + threadIdx.x] = combine_d(a, sm, threadIdx.x);
-        else sm.exf[sl * 8 + threadIdx.x] = combine_f(a, sm, threadIdx.x);
+        if (want_ss) sm.exd[threadIdx.x * SMAX + sl] = combine_d(a, sm, threadIdx.x);
+        else sm.exf[threadIdx.x * SMAX + sl] = combine_f(a, sm, threadIdx.x);
     }
     __syncthreads();
 }
 
 // Exchange this slice's per-row value with the other slices (S > 1), run by
-// the poller wave only.  Every word carries the call's tag in its high half,
-// so no fence is needed: a reader simply waits until all words show the tag.
-// absmax: one word (tag | float bits).  Sum of squares (double): two words
-// (tag | high half), (tag | low half).
+// the poller wave only, after the waves' values are in sm.wd / sm.wf.  Every
+// word carries the call's tag in its high half, so no fence is needed: a
+// reader simply waits until all words show the tag.  absmax: one word
+// (tag | float bits).  Sum of squares (double): two words (tag | high half),
+// (tag | low half).
 __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, bool is_ss) {
     const uint32_t tag = sm.tag;
     if (lane < a.m) {
         const int slot = s * 8 + lane;
         if (is_ss) {
-            const u64 bits = (u64)__double_as_longlong(sm.exd[slot]);
+            const double v = combine_d(a, sm, lane);
+            sm.exd[lane * SMAX + s] = v;
+            const u64 bits = (u64)__double_as_longlong(v);
             __hip_atomic_store(&a.ws->ssh[slot], ((u64)tag << 32) | (bits >> 32), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(&a.ws->ssl[slot], ((u64)tag << 32) | (bits & 0xFFFFFFFFull),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
-            __hip_atomic_store(&a.ws->amax[slot], ((u64)tag << 32) | __float_as_uint(sm.exf[slot]),
+            const float v = combine_f(a, sm, lane);
+            sm.exf[lane * SMAX + s] = v;
+            __hip_atomic_store(&a.ws->amax[slot], ((u64)tag << 32) | __float_as_uint(v),
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
@@ -316,7 +454,7 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
                 const u64 hi = __hip_atomic_load(&a.ws->ssh[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const u64 lo = __hip_atomic_load(&a.ws->ssl[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if ((uint32_t)(hi >> 32) == tag && (uint32_t)(lo >> 32) == tag) {
-                    sm.exd[slot] = __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) |
+                    sm.exd[mm * SMAX + sl] = __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) |
                                                                     (lo & 0xFFFFFFFFull)));
                     ok = true;
                     break;
@@ -324,7 +462,7 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
             } else {
                 const u64 v = __hip_atomic_load(&a.ws->amax[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if ((uint32_t)(v >> 32) == tag) {
-                    sm.exf[slot] = __uint_as_float((uint32_t)v);
+                    sm.exf[mm * SMAX + sl] = __uint_as_float((uint32_t)v);
                     ok = true;
                     break;
                 }
@@ -345,64 +483,85 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __shared__ Smem sm;
     constexpr int NG = 4 / GS;                  // groups per super-block
     constexpr int OFF = (FMT == FMT_W6) ? 32 : 8;
+    constexpr int E = Act<XT>::E;
+    constexpr int NCH = Act<XT>::NCH;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int nl = lane & 15;
     const int hl = lane >> 4;
     const int M = a.m;
 
-    // work assignment
-    const int s = blockIdx.x / a.R;
-    const int r = blockIdx.x % a.R;
+    // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
+    // wave wv works on tile group tg (every TW-th tile) and super-blocks
+    // [kw * spw, (kw + 1) * spw) of the slice
+    const int r = blockIdx.x;
+    const int s = blockIdx.y;
     const int k_lo = s * a.KS;
     const int kb_lo = s * a.KBs;
-    const int64_t t_begin = (int64_t)r * a.T / a.R;
-    const int64_t t_end = (int64_t)(r + 1) * a.T / a.R;
-    const int ntile = (int)(t_end - t_begin);
-    const int tg = wv / a.KW;                   // tile group of this wave (idle if >= TW)
-    const int kw = wv % a.KW;
-    const int jn = (ntile + a.TW - 1) / a.TW;   // tiles per group (padded)
-    const int jall = jn * a.spw;                // iterations every wave runs
+    const bool big = r < a.trem;
+    const int t_begin = r * a.tq + (big ? r : a.trem);
+    const int t_end = t_begin + a.tq + (big ? 1 : 0);
+    const int jn = big ? a.jn1 : a.jn0;         // tiles per group, padded
+    const uint32_t wt = a.wtab[wv];
+    const int tg = wt & 31;
+    const int kw = (wt >> 5) & 31;
+    const int kbw = kb_lo + kw * a.spw;
     // With S > 1 the last wave only runs the cross-slice exchange: it never has
     // weight loads in flight, so its polls are not queued behind them.
     const bool poller = (a.S > 1) && (wv == NW - 1);
     const bool active = tg < a.TW && !poller;
 
-    // LDS: [q: M x ks int8][sums of q][wave partials]
-    const int KS8 = a.KS >> 3;
+    // LDS: [q: M x ks int8][sums of q][wave partials, two halves]
     int8_t* q_l = reinterpret_cast<int8_t*>(lds);
     int32_t* qs_l = reinterpret_cast<int32_t*>(lds + (size_t)M * a.ks);
-    const int qs_n = DOT4 ? KS8 : (a.KS / (32 * GS)) * 8;
-    float* red_l = reinterpret_cast<float*>(qs_l + qs_n);                        // 2 x [NW][8][16]
+    const int qs_n = DOT4 ? (a.KS >> 3) : (a.KS / (32 * GS)) * 8;
+    float* red_l = reinterpret_cast<float*>(qs_l + qs_n);
 
-    auto tile_of = [&](int i) -> int64_t { return t_begin + tg + (int64_t)(i / a.spw) * a.TW; };
+    // Per-lane byte offsets inside a super-block: a full tile (16 rows) and the
+    // weight's ragged last tile (nr_last rows; its lanes nl >= nr_last idle).
+    const int nr_rag = a.nr_last;
+    const bool lane_rag_ok = nl < nr_rag;
+    const int lw_full = lane * 16, lw_rag = (hl * nr_rag + nl) * 16;
+    const int lh_full = 16 * 64 + lane * 8, lh_rag = nr_rag * 64 + (hl * nr_rag + nl) * 8;
+    const int ls = nl * NG * 4;
 
-    // One super-block's loads into registers.  Always exactly the same load
-    // instructions; slots outside the work read the weight's first bytes.
-    // Branch-free address arithmetic of super-block slot i (selects only, so the
-    // loads issue back to back); an invalid slot reads the weight's first bytes.
-    auto addr = [&](int i, bool real, int64_t& wp, int64_t& sp, int& nr) -> bool {
-        const int64_t t = tile_of(i);
-        const bool valid = real && active && i < jall && t < t_end;
-        const int kb = kb_lo + kw * a.spw + i % a.spw;
-        const int64_t rem = (int64_t)a.n - t * TILE_ROWS;
-        nr = rem < TILE_ROWS ? (int)rem : TILE_ROWS;
-        const bool full = nr == TILE_ROWS;
-        const int64_t tb = t * a.tile_full;
-        wp = tb + (int64_t)kb * nr * (full ? a.sb_row : a.wsb_row);
-        sp = full ? wp + nr * a.wsb_row
-                  : tb + (int64_t)a.KB * nr * a.wsb_row + (int64_t)kb * nr * NG * 4;
-        return valid;
+    // A position in the wave's slot sequence: tile-group step j, super-block u
+    // of the wave's k-part, tile t and the full-tile byte offset of the slot.
+    struct Cur {
+        int j, u, t;
+        int64_t off;
     };
-    // slot i into registers (the steady-state pipeline)
-    auto load = [&](int i, uint4& w4, uint2& h2, float4& sv) {
-        int64_t wp, sp;
-        int nr;
-        const bool ok = addr(i, true, wp, sp, nr) && nl < nr;
-        const int64_t woff = ok ? wp + (hl * nr + nl) * 16 : 0;
-        const int64_t hoff = ok ? wp + nr * 64 + (hl * nr + nl) * 8 : 0;
-        const int64_t soff = ok ? sp + nl * NG * 4 : 0;
+    auto start = [&]() {
+        Cur c;
+        c.j = 0;
+        c.u = 0;
+        c.t = t_begin + tg;
+        c.off = (int64_t)c.t * a.tile_full + (int64_t)kbw * a.sbf;
+        return c;
+    };
+    auto advance = [&](Cur& c) {
+        c.off += a.sbf;
+        if (++c.u == a.spw) {
+            c.u = 0;
+            ++c.j;
+            c.t += a.TW;
+            c.off += a.tstep;
+        }
+    };
+    // The slot at c into registers.  Every wave issues the same load
+    // instructions; a slot outside the work reads the weight's first bytes, so
+    // the compiler's wait counts are exact.
+    auto load = [&](const Cur& c, uint4& w4, uint2& h2, float4& sv) {
+        const bool valid = active && c.j < jn && c.t < t_end;
+        const int kb = kbw + c.u;
+        const bool rag = c.t == a.t_rag;
+        const int64_t wp = rag ? a.rag_w + (int64_t)kb * a.rag_sbw : c.off;
+        const int64_t sp = rag ? a.rag_s + (int64_t)kb * a.rag_sbs : c.off + a.swo;
+        const bool ok = valid && (!rag || lane_rag_ok);
+        const int64_t woff = ok ? wp + (rag ? lw_rag : lw_full) : 0;
+        const int64_t hoff = ok ? wp + (rag ? lh_rag : lh_full) : 0;
+        const int64_t soff = ok ? sp + ls : 0;
         w4 = *reinterpret_cast<const uint4*>(a.data + woff);
         if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(a.data + hoff);
         if (NG == 4) {
@@ -414,144 +573,156 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             sv = make_float4(*reinterpret_cast<const float*>(a.data + soff), 0.0f, 0.0f, 0.0f);
         }
     };
-    // 1. the call's tag, the activations, then the weight stream (in this order:
-    //    a wave's loads complete in issue order, so anything waited on before the
-    //    weights arrive must be issued before them)
+
+    // 1. the call's tag, the activations, then the weight stream (in this
+    //    order: a wave's loads complete in issue order, so anything waited on
+    //    before the weights arrive must be issued before them)
     const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const ActMap am = act_map(a, wv, lane);
-    float xv[MO][8], uv[MO][8], gv[MO][8];
-    load_act<PRO, XT>(a, am, k_lo, xv, uv);
-    if (PRO == PRO_RMSNORM) {
-#pragma unroll
-        for (int i = 0; i < MO; ++i) {
-            const int64_t off = oct_valid(a, am, i) ? k_lo + 8 * (am.it + i * am.tpr) : 0;
-            const float4* gp = reinterpret_cast<const float4*>(a.gamma + off);
-            const float4 g0 = gp[0], g1 = gp[1];
-            gv[i][0] = g0.x; gv[i][1] = g0.y; gv[i][2] = g0.z; gv[i][3] = g0.w;
-            gv[i][4] = g1.x; gv[i][5] = g1.y; gv[i][6] = g1.z; gv[i][7] = g1.w;
-        }
-    }
-    // The first PRIME slots.  Every wave issues the same load instructions (the
-    // poller and idle waves read dummies), so the compiler's wait counts are exact.
+    const Act<XT> am = act_map<XT>(a, wt, lane);
+    uint4 xr[NCH], ur[NCH];
+    float gv[NCH * E];
+    load_act<PRO, XT>(a, am, k_lo, xr, ur);
+    if (PRO == PRO_RMSNORM) load_gamma<XT>(a, am, k_lo, gv);
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
     float4 sbuf[PIPE];
+    Cur cl = start();                           // next slot to load
 #pragma unroll
-    for (int d = 0; d < PRIME; ++d) load(d, wbuf[d], hbuf[d], sbuf[d]);
+    for (int d = 0; d < PRIME; ++d) {
+        load(cl, wbuf[d], hbuf[d], sbuf[d]);
+        advance(cl);
+    }
 
-    // 2. activation prologue
-    if (tid == 0) sm.tag = gen + 1u;
-    for (int i = tid; i < qs_n; i += NT) qs_l[i] = 0;
-    finish_act<PRO>(a, am, xv, uv);
+    // 2. activation prologue: per-row statistics of h, then q into LDS
+    if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
+    float h[NCH * E];
+    finish_act<PRO, XT>(am, xr, ur, h);
+    const int mrow = am.m < M ? am.m : 0;
+    const bool row_lead = lane == 0 && am.m < M && am.it == 0;   // one thread per row
 
     if (PRO == PRO_RMSNORM) {
-        double ss = 0.0;
-#pragma unroll
-        for (int i = 0; i < MO; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss += (double)xv[i][e] * (double)xv[i][e];
-        row_sum_d(sm, wv, lane, ss);
+        const double ss = wave_sum(sum_sq<XT>(h));
+        if (lane == 0) sm.wd[wv] = ss;
         __syncthreads();
-        if (tid < M) sm.exd[s * 8 + tid] = combine_d(a, sm, tid);
-        __syncthreads();
-        if (a.S > 1) {
+        double tot;
+        if (a.S == 1) {
+            tot = combine_d(a, sm, mrow);
+        } else {
             if (poller) exchange_poll(a, sm, lane, s, true);
             __syncthreads();
             for (int sl = 0; sl < a.S; ++sl)
-                if (sm.miss[sl]) slice_stat<PRO, XT>(a, sm, wv, lane, sl, true);
+                if (sm.miss[sl]) slice_stat<PRO, XT>(a, sm, wt, lane, wv, sl, true);
+            tot = slices_sum(a, sm, mrow);
         }
-        if (tid < M) {
-            double tot = 0.0;
-            for (int sl = 0; sl < a.S; ++sl) tot += sm.exd[sl * 8 + tid];
-            const float ms = (float)(tot / (double)a.k);
-            const float d = ms + a.eps;
-            const float sd = (float)__builtin_sqrt((double)d);   // correctly rounded fp32 sqrt
-            sm.rr[tid] = (float)(1.0 / (double)sd);               // correctly rounded fp32 1/x
-        }
-        __syncthreads();
-        if (am.m < M) {
-            const float rm = sm.rr[am.m];
+        const float ms = (float)(tot / (double)a.k);
+        const float d = ms + a.eps;
+        const float sd = (float)__builtin_sqrt((double)d);   // correctly rounded fp32 sqrt
+        const float rr = (float)(1.0 / (double)sd);          // correctly rounded fp32 1/x
+        if (row_lead) sm.rr[am.m] = rr;
 #pragma unroll
-            for (int i = 0; i < MO; ++i)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xv[i][e] = rms_apply(xv[i][e], rm, gv[i][e]);
-        }
+        for (int j = 0; j < NCH * E; ++j) h[j] = rms_apply(h[j], rr, gv[j]);
     }
+    float amx;
     {
-        float mx = 0.0f;
-#pragma unroll
-        for (int i = 0; i < MO; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(xv[i][e]));
-        row_max_f(sm, wv, lane, mx);
+        const float mx = wave_max(abs_max<XT>(h));
+        if (lane == 0) sm.wf[wv] = mx;
         __syncthreads();
-        if (tid < M) sm.exf[s * 8 + tid] = combine_f(a, sm, tid);
-        __syncthreads();
-        if (a.S > 1) {
+        if (a.S == 1) {
+            amx = combine_f(a, sm, mrow);
+        } else {
             if (poller) exchange_poll(a, sm, lane, s, false);
             __syncthreads();
             for (int sl = 0; sl < a.S; ++sl)
-                if (sm.miss[sl]) slice_stat<PRO, XT>(a, sm, wv, lane, sl, false);
+                if (sm.miss[sl]) slice_stat<PRO, XT>(a, sm, wt, lane, wv, sl, false);
+            amx = slices_max(a, sm, mrow);
         }
-        if (tid < 8) {
-            float amx = 0.0f;
-            if (tid < M)
-                for (int sl = 0; sl < a.S; ++sl) amx = fmaxf(amx, sm.exf[sl * 8 + tid]);
-            const float sx = amx / 127.0f;
-            sm.sx[tid] = (amx > 0.0f) ? sx : 0.0f;
-            sm.inv[tid] = (amx > 0.0f) ? 1.0f / sx : 0.0f;
-            if (a.sx_out && blockIdx.x == 0 && tid < M) a.sx_out[tid] = sm.sx[tid];
-        }
-        __syncthreads();
+    }
+    const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
+    const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+    if (row_lead) {
+        sm.sx[am.m] = sx;
+        if (a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
     }
 
-    // quantise this slice into LDS
-    if (am.m < M) {
-        const float sx = sm.sx[am.m];
-        const float inv = sm.inv[am.m];
-        const bool exact_row = sx < 2.3509887e-38f;       // 2^-125: 1/sx may not be normal
+    // quantise this slice into LDS, with the sums of q that undo the weights'
+    // offset: per octet (M = 1) or per weight group and row (M >= 2).
+    // q = clamp(rint(fp32(h / sx)), -127, 127) bit-exactly: t = h * inv with
+    // inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here) of h/sx, and
+    // fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t) equals
+    // rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then
+    // (or for a tiny sx) is the quotient formed by IEEE division.
+    {
+        constexpr int L = DOT4 ? 8 / E : (32 * GS) / E;      // chunks per summed run
+        const bool exact_row = sx < 2.3509887e-38f;           // 2^-125: 1/sx may not be normal
 #pragma unroll
-        for (int i = 0; i < MO; ++i) {
-            const int o = am.it + i * am.tpr;
-            if (o < KS8) {
-                uint32_t lo = 0, hi = 0;
+        for (int i = 0; i < NCH; ++i) {
+            if (i < am.nw) {
+                const int c = am.it + i * am.tpr;
+                const bool ok = c < am.cpr;
+                float rq[E];
+                bool redo = exact_row;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float t = h[i * E + e] * inv;
+                    rq[e] = __builtin_rintf(t);
+                    redo = redo || fabsf(t - rq[e]) > 0.49998f;
+                }
+                if (redo && sx > 0.0f) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) rq[e] = __builtin_rintf(h[i * E + e] / sx);
+                }
+                uint32_t pk[E / 4];
                 int sum = 0;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int qi = (sx > 0.0f) ? quant1(xv[i][e], sx, inv, exact_row) : 0;
+                for (int e = 0; e < E; ++e) {
+                    const int qi = (int)fminf(fmaxf(rq[e], -127.0f), 127.0f);
                     sum += qi;
-                    const uint32_t b = (uint32_t)(qi & 0xFF);
-                    if (e < 4) lo |= b << (8 * e); else hi |= b << (8 * (e - 4));
+                    if (e % 4 == 0) pk[e / 4] = 0u;
+                    pk[e / 4] |= (uint32_t)(qi & 0xFF) << (8 * (e % 4));
                 }
-                *reinterpret_cast<uint2*>(q_l + am.m * a.ks + 8 * o) = make_uint2(lo, hi);
-                if (a.q_out && r == 0)
-                    *reinterpret_cast<uint2*>(a.q_out + (int64_t)am.m * a.k + k_lo + 8 * o) =
-                        make_uint2(lo, hi);
-                if (DOT4) qs_l[o] = sum;
-                else atomicAdd(&qs_l[(8 * o / (32 * GS)) * 8 + am.m], sum);
+                const int gsum = lane_group_sum<L>(sum);
+                if (ok) {
+                    int8_t* dst = q_l + am.m * a.ks + c * E;
+                    if (E == 4) {
+                        *reinterpret_cast<uint32_t*>(dst) = pk[0];
+                    } else {
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[E / 4 - 1]);
+                    }
+                    if (a.q_out && r == 0) {
+                        int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
+                        if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[0];
+                        else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[0], pk[E / 4 - 1]);
+                    }
+                    if (c % L == 0) {
+                        if (DOT4) qs_l[c / L] = gsum;
+                        else qs_l[(c / L) * 8 + am.m] = gsum;
+                    }
+                }
             }
         }
     }
     __syncthreads();
 
 #pragma unroll
-    for (int d = PRIME; d < PIPE; ++d) load(d, wbuf[d], hbuf[d], sbuf[d]);
+    for (int d = PRIME; d < PIPE; ++d) {
+        load(cl, wbuf[d], hbuf[d], sbuf[d]);
+        advance(cl);
+    }
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int ml = nl;   // A-operand row (activation row m) of this lane
+    const int jall = jn * a.spw;
     const int iters = (jall + PIPE - 1) / PIPE * PIPE;
-    // consume super-block slot i (weights w_in/h_in, scales s_in), then the tile
-    // epilogue when slot i is the last one of its tile
-    auto process = [&](int i, const uint4 w_in, const uint2 h_in, const float4 s_in) {
-        const int64_t t = tile_of(i);
-        const int slot_i = i % a.spw;
-        if (active && i < jall && t < t_end) {
-            const int kbr = kw * a.spw + slot_i;          // super-block within the slice
+    Cur cp = start();                           // next slot to consume
+    // consume the slot at cp (weights w_in/h_in, scales s_in), then the tile
+    // epilogue when it is the last super-block of its tile
+    auto process = [&](const uint4 w_in, const uint2 h_in, const float4 s_in) {
+        const int t = cp.t;
+        if (active && cp.j < jn && t < t_end) {
+            const int kbr = kw * a.spw + cp.u;           // super-block within the slice
             const int kb = kb_lo + kbr;
-            const int64_t rem = (int64_t)a.n - t * TILE_ROWS;
-            const int nr = rem < TILE_ROWS ? (int)rem : TILE_ROWS;
-            const bool row_ok = nl < nr;
+            const bool row_ok = t != a.t_rag || lane_rag_ok;
             const uint32_t wd[4] = {row_ok ? w_in.x : 0u, row_ok ? w_in.y : 0u,
                                     row_ok ? w_in.z : 0u, row_ok ? w_in.w : 0u};
             const float s4[4] = {s_in.x, s_in.y, s_in.z, s_in.w};
@@ -592,7 +763,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     for (int jj = 0; jj < GS; ++jj) pg += pj[gi * GS + jj];
                     acc[0] = __builtin_fmaf(sv[gi], (float)pg, acc[0]);
                     if (a.p_out && row_ok)
-                        atomicAdd(&a.p_out[(t * TILE_ROWS + nl) * a.kg + kb * NG + gi], pg);
+                        atomicAdd(&a.p_out[((int64_t)t * TILE_ROWS + nl) * a.kg + kb * NG + gi], pg);
                 }
             } else {
                 long av[4], bv[4];
@@ -621,20 +792,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         acc[rr] = __builtin_fmaf(sv[gi], (float)c[rr], acc[rr]);
                         const int mm = 4 * hl + rr;
                         if (a.p_out && mm < M && row_ok)
-                            a.p_out[((int64_t)mm * a.n + t * TILE_ROWS + nl) * a.kg +
+                            a.p_out[((int64_t)mm * a.n + (int64_t)t * TILE_ROWS + nl) * a.kg +
                                     kb * NG + gi] = c[rr];
                     }
                 }
             }
         }
-        if (i < jall && slot_i == a.spw - 1) {
+        if (cp.j < jn && cp.u == a.spw - 1) {
             // 4. tile epilogue: fixed-order sum of the waves' partials.  The partials
             //    buffer alternates between two halves, so one barrier per tile is enough
             //    (a wave cannot reuse a half before every thread passed the next barrier).
-            const int j = i / a.spw;
-            float* red = red_l + (j & 1) * (NW * 128);
+            float* red = red_l + (cp.j & 1) * (NW * 128);
             if (DOT4) {
-                red[(wv * 4 + hl) * 16 + nl] = acc[0];
+                // the four k-quarters of a row sit 16 lanes apart
+                float v = acc[0];
+                v += __shfl_xor(v, 16);
+                v += __shfl_xor(v, 32);
+                if (lane < 16) red[wv * 16 + nl] = v;
             } else {
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr) {
@@ -648,23 +822,21 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 const int ogrp = tid / (M * 16);
                 const int omm = (tid / 16) % M;
                 const int onn = tid & 15;
-                const int64_t ot = t_begin + ogrp + (int64_t)j * a.TW;
+                const int ot = t_begin + ogrp + cp.j * a.TW;
                 if (ot < t_end) {
                     float osum = 0.0f;
                     const int w0 = ogrp * a.KW;
                     if (DOT4) {
-                        for (int w = w0; w < w0 + a.KW; ++w)
-#pragma unroll
-                            for (int h = 0; h < 4; ++h) osum += red[(w * 4 + h) * 16 + onn];
+                        for (int w = w0; w < w0 + a.KW; ++w) osum += red[w * 16 + onn];
                     } else {
                         for (int w = w0; w < w0 + a.KW; ++w) osum += red[(w * 8 + omm) * 16 + onn];
                     }
                     if (a.S == 1) {
                         if (ot * TILE_ROWS + onn < a.n)
-                            a.y[(int64_t)omm * a.n + ot * TILE_ROWS + onn] = sm.sx[omm] * osum;
+                            a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * osum;
                     } else {
                         const u64 v = ((u64)sm.tag << 32) | __float_as_uint(osum);
-                        __hip_atomic_store(&a.part[((ot * a.S + s) * M + omm) * 16 + onn], v,
+                        __hip_atomic_store(&a.part[(((int64_t)ot * a.S + s) * M + omm) * 16 + onn], v,
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     }
                 }
@@ -672,24 +844,26 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
         }
+        advance(cp);
     };
 
     for (int base = 0; base < iters; base += PIPE) {
 #pragma unroll
         for (int d = 0; d < PIPE; ++d) {
-            const int i = base + d;
-            process(i, wbuf[d], hbuf[d], sbuf[d]);
-            load(i + PIPE, wbuf[d], hbuf[d], sbuf[d]);
+            process(wbuf[d], hbuf[d], sbuf[d]);
+            load(cl, wbuf[d], hbuf[d], sbuf[d]);
+            advance(cl);
         }
     }
 
     // 5. merge the slices' partials: the last workgroup of each tile adds them
     if (a.S > 1) {
+        const int ntile = t_end - t_begin;
         __syncthreads();
         for (int c0 = 0; c0 < ntile; c0 += kMaxTilesPerGroup) {
             const int nc = min(kMaxTilesPerGroup, ntile - c0);
             if (tid < nc) {
-                const int64_t tt = t_begin + c0 + tid;
+                const int tt = t_begin + c0 + tid;
                 const uint32_t old =
                     __hip_atomic_fetch_add(&a.cnt[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const int lst = (old == (uint32_t)(a.S - 1));
@@ -702,19 +876,20 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 if (!sm.last[ci]) continue;
                 const int omm = (e / 16) % M;
                 const int onn = e & 15;
-                const int64_t ot = t_begin + c0 + ci;
+                const int ot = t_begin + c0 + ci;
                 float tot = 0.0f;
                 for (int sl = 0; sl < a.S; ++sl) {
                     // Every partial was stored before its workgroup counted the tile, so its
                     // tag shows up shortly; the bound only guards against a hang (a missing
                     // partial would turn y into NaN rather than stall the GPU).
-                    const u64* p = &a.part[((ot * a.S + sl) * M + omm) * 16 + onn];
+                    const u64* p = &a.part[(((int64_t)ot * a.S + sl) * M + omm) * 16 + onn];
                     u64 v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     for (int it = 0; (uint32_t)(v >> 32) != sm.tag && it < (1 << 24); ++it)
                         v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     tot += ((uint32_t)(v >> 32) == sm.tag) ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
                 }
-                if (ot * TILE_ROWS + onn < a.n) a.y[(int64_t)omm * a.n + ot * TILE_ROWS + onn] = sm.sx[omm] * tot;
+                if (ot * TILE_ROWS + onn < a.n)
+                    a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * tot;
             }
             __syncthreads();
         }
@@ -789,7 +964,8 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     const bool dot4 = (m == 1);
     p.WPR = NW / m;                               // waves per activation row
     const int tpr = p.WPR * 64;
-    auto fits = [&](int s) { return (G.k / s) / 8 <= (int64_t)tpr * MO; };
+    // each thread quantises at most 16 activations of its row (four fp32 chunks)
+    auto fits = [&](int s) { return (G.k / s) / 16 <= (int64_t)tpr; };
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
         const size_t qs = dot4 ? (KS / 8) * 4 : (KS / G.g) * 8 * 4;
@@ -915,9 +1091,19 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.T = (int)G.T;
     a.KB = (int)G.KB;
     a.kg = (int)G.kg;
-    a.sb_row = (int)G.sb_row;
-    a.wsb_row = (int)G.wsb_row;
     a.tile_full = G.tile_full;
+    a.sbf = (int)(TILE_ROWS * G.sb_row);
+    a.swo = (int)(TILE_ROWS * G.wsb_row);
+    {
+        const int nr = (int)(G.n % TILE_ROWS);
+        const int ng = (int)(128 / G.g);
+        a.nr_last = nr ? nr : TILE_ROWS;
+        a.t_rag = nr ? (int)G.T - 1 : -1;
+        a.rag_w = (int64_t)(G.T - 1) * G.tile_full;
+        a.rag_s = a.rag_w + (int64_t)G.KB * a.nr_last * G.wsb_row;
+        a.rag_sbw = (int)(a.nr_last * G.wsb_row);
+        a.rag_sbs = a.nr_last * ng * 4;
+    }
     a.S = p.S;
     a.R = p.R;
     a.P = p.P;
@@ -929,13 +1115,29 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.WPR = p.WPR;
     a.ks = p.ks;
     a.spin_limit = c.spin_limit > 0 ? c.spin_limit : (1 << 20);
+    a.tq = (int)(G.T / p.R);
+    a.trem = (int)(G.T % p.R);
+    a.jn0 = (a.tq + p.TW - 1) / p.TW;
+    a.jn1 = (a.tq + 1 + p.TW - 1) / p.TW;
+    a.tstep = (int64_t)p.TW * G.tile_full - (int64_t)p.spw * a.sbf;
+    const int epc = (c.xt == 1) ? 8 : 4;           // activations per 16-byte chunk
+    const int nch = 16 / epc;                      // chunks per thread
+    a.cpr = p.KS / epc;
+    a.tpr = p.WPR * 64;
+    for (int w = 0; w < NW; ++w) {
+        const int m = w / p.WPR, wb = (w % p.WPR) * 64;
+        int nw = (m < c.m && a.cpr > wb) ? (a.cpr - wb + a.tpr - 1) / a.tpr : 0;
+        if (nw > nch) nw = nch;
+        a.wtab[w] = (uint32_t)((w / p.KW) | ((w % p.KW) << 5) | (m << 10) | ((w % p.WPR) << 14) |
+                               (nw << 19));
+    }
 
     if (p.lds > 64 * 1024) {
         e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)p.P), dim3(NT), p.lds, st, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.R, (unsigned)p.S), dim3(NT), p.lds, st, a);
     return hipGetLastError();
 }
 

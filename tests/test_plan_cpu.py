@@ -45,9 +45,11 @@ def covered(n, k, m, p):
     """Simulate the kernel's work assignment; count visits per (tile, super-block)."""
     T, KB = (n + 15) // 16, k // 128
     seen = np.zeros((T, KB), dtype=np.int64)
+    tq, trem = T // p["R"], T % p["R"]
     for blk in range(p["P"]):
         s, r = blk // p["R"], blk % p["R"]
-        t0, t1 = r * T // p["R"], (r + 1) * T // p["R"]
+        t0 = r * tq + min(r, trem)
+        t1 = t0 + tq + (1 if r < trem else 0)
         ntile = t1 - t0
         jn = (ntile + p["TW"] - 1) // p["TW"]
         for wv in range(NW):
