@@ -82,7 +82,7 @@ struct KArgs {
     int64_t rag_w, rag_s;   // byte offsets of the ragged tile's weights and scales
     int rag_sbw, rag_sbs;   // their bytes per super-block
     // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
-    // wave index within the row (14-18) and activation chunk steps (19-21)
+    // wave index within the row (14-18) and activation chunk steps (19-22)
     uint32_t wtab[NW];
 };
 
@@ -102,24 +102,6 @@ struct Smem {
 // --------------------------------------------------------------------------
 // activation helpers
 // --------------------------------------------------------------------------
-
-template <int XT>
-__device__ inline void load8(const void* base, int64_t off, float v[8]) {
-    if (XT == 0) {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
-        float4 a = p[0], b = p[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
-        uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[2 * i] = __uint_as_float(w[i] << 16);
-            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-    }
-}
 
 #pragma clang fp contract(off)
 
@@ -158,6 +140,42 @@ __device__ inline float silu_mul(float g, float u) {
 __device__ inline float rms_apply(float x, float r, float g) {
     float t = x * r;
     return t * g;
+}
+
+// q = clamp(rint(fp32(h / sx)), -127, 127) of E values (E = 4 or 8), packed as
+// int8 into E/4 dwords; returns their sum.  For sx > 0, |h| <= 127 sx so the
+// clamp never acts.  Adding 1.5 * 2^23 rounds a value of magnitude < 2^22 to
+// the nearest integer (ties to even) and leaves it in the low mantissa bits, so
+// the low byte of the sum's bit pattern is the int8 result.  t = h * inv with
+// inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here) of h/sx, and
+// fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t) equals
+// rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then (or
+// for a tiny sx) is the quotient formed by IEEE division.
+template <int E>
+__device__ inline int quant_chunk(const float* h, float sx, float inv, bool exact_row,
+                                  uint32_t pk[E / 4]) {
+    const float kRound = 12582912.0f;   // 1.5 * 2^23
+    uint32_t b[E];
+    bool redo = exact_row;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float t = h[e] * inv;
+        b[e] = __float_as_uint(t + kRound);
+        redo = redo || fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 2e-5f;
+    }
+    if (redo && sx > 0.0f) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) b[e] = __float_as_uint(h[e] / sx + kRound);
+    }
+    int sum = 0;
+#pragma unroll
+    for (int w = 0; w < E / 4; ++w) {
+        // bytes 0..3 <- low bytes of b[4w..4w+3]
+        pk[w] = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x0C0C0400u) |
+                __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x04000C0Cu);
+        sum = __builtin_amdgcn_sdot4((int)pk[w], 0x01010101, sum, false);
+    }
+    return sum;
 }
 
 #pragma clang fp contract(on)
@@ -224,10 +242,10 @@ __device__ inline double wave_sum(double v) {
 // row m = wave / WPR, chunk c = it + i * TPR for i < NCH.  `nw` counts the
 // iterations i in which the wave has at least one chunk, so a wave skips the
 // rest with a uniform branch.
-template <int XT>
+template <int XT, int EPT>
 struct Act {
     static constexpr int E = XT == 0 ? 4 : 8;      // elements per chunk
-    static constexpr int NCH = XT == 0 ? 4 : 2;    // chunks per thread (16 elements)
+    static constexpr int NCH = EPT / E;            // chunks per thread (EPT elements)
     static constexpr int ES = XT == 0 ? 4 : 2;     // bytes per element
     int m;      // row of this wave; >= M: the wave holds no activations
     int it;     // thread index within the row
@@ -236,43 +254,43 @@ struct Act {
     int nw;     // wave-uniform
 };
 
-template <int XT>
-__device__ inline Act<XT> act_map(const KArgs& a, uint32_t wt, int lane) {
-    Act<XT> am;
+template <int XT, int EPT>
+__device__ inline Act<XT, EPT> act_map(const KArgs& a, uint32_t wt, int lane) {
+    Act<XT, EPT> am;
     am.m = (wt >> 10) & 15;
     am.it = ((wt >> 14) & 31) * 64 + lane;
     am.tpr = a.tpr;
     am.cpr = a.cpr;
-    am.nw = (wt >> 19) & 7;
+    am.nw = (wt >> 19) & 15;
     return am;
 }
 
 // Raw 16-byte chunks of slice [k_lo, k_lo + KS) (SwiGLU: gate in xr, up in ur).
-template <int PRO, int XT>
-__device__ inline void load_act(const KArgs& a, const Act<XT>& am, int k_lo,
-                                uint4 xr[Act<XT>::NCH], uint4 ur[Act<XT>::NCH]) {
+template <int PRO, int XT, int EPT>
+__device__ inline void load_act(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
+                                uint4 xr[Act<XT, EPT>::NCH], uint4 ur[Act<XT, EPT>::NCH]) {
     const uint8_t* xb = static_cast<const uint8_t*>(a.x);
     const uint8_t* ub = static_cast<const uint8_t*>(a.x2);
 #pragma unroll
-    for (int i = 0; i < Act<XT>::NCH; ++i) {
+    for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
         xr[i] = make_uint4(0u, 0u, 0u, 0u);
         ur[i] = make_uint4(0u, 0u, 0u, 0u);
         if (i < am.nw) {
             const int c = am.it + i * am.tpr;
             const int cc = c < am.cpr ? c : 0;
-            const int64_t off = ((int64_t)am.m * a.ld + k_lo + (int64_t)cc * Act<XT>::E) * Act<XT>::ES;
+            const int64_t off = ((int64_t)am.m * a.ld + k_lo + (int64_t)cc * Act<XT, EPT>::E) * Act<XT, EPT>::ES;
             xr[i] = *reinterpret_cast<const uint4*>(xb + off);
             if (PRO == PRO_SWIGLU) ur[i] = *reinterpret_cast<const uint4*>(ub + off);
         }
     }
 }
 
-template <int XT>
-__device__ inline void load_gamma(const KArgs& a, const Act<XT>& am, int k_lo,
-                                  float g[Act<XT>::NCH * Act<XT>::E]) {
-    constexpr int E = Act<XT>::E;
+template <int XT, int EPT>
+__device__ inline void load_gamma(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
+                                  float g[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
+    constexpr int E = Act<XT, EPT>::E;
 #pragma unroll
-    for (int i = 0; i < Act<XT>::NCH; ++i) {
+    for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
 #pragma unroll
         for (int e = 0; e < E; ++e) g[i * E + e] = 0.0f;
         if (i < am.nw) {
@@ -290,12 +308,12 @@ __device__ inline void load_gamma(const KArgs& a, const Act<XT>& am, int k_lo,
 }
 
 // h values of the thread's chunks (SwiGLU applied); invalid elements are 0.
-template <int PRO, int XT>
-__device__ inline void finish_act(const Act<XT>& am, const uint4 xr[Act<XT>::NCH],
-                                  const uint4 ur[Act<XT>::NCH], float h[Act<XT>::NCH * Act<XT>::E]) {
-    constexpr int E = Act<XT>::E;
+template <int PRO, int XT, int EPT>
+__device__ inline void finish_act(const Act<XT, EPT>& am, const uint4 xr[Act<XT, EPT>::NCH],
+                                  const uint4 ur[Act<XT, EPT>::NCH], float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
+    constexpr int E = Act<XT, EPT>::E;
 #pragma unroll
-    for (int i = 0; i < Act<XT>::NCH; ++i) {
+    for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
         const bool ok = i < am.nw && am.it + i * am.tpr < am.cpr;
         const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
         const uint32_t uw[4] = {ur[i].x, ur[i].y, ur[i].z, ur[i].w};
@@ -315,18 +333,18 @@ __device__ inline void finish_act(const Act<XT>& am, const uint4 xr[Act<XT>::NCH
     }
 }
 
-template <int XT>
-__device__ inline double sum_sq(const float h[Act<XT>::NCH * Act<XT>::E]) {
+template <int XT, int EPT>
+__device__ inline double sum_sq(const float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
     double ss = 0.0;
 #pragma unroll
-    for (int j = 0; j < Act<XT>::NCH * Act<XT>::E; ++j) ss += (double)h[j] * (double)h[j];
+    for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) ss += (double)h[j] * (double)h[j];
     return ss;
 }
-template <int XT>
-__device__ inline float abs_max(const float h[Act<XT>::NCH * Act<XT>::E]) {
+template <int XT, int EPT>
+__device__ inline float abs_max(const float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
     float mx = 0.0f;
 #pragma unroll
-    for (int j = 0; j < Act<XT>::NCH * Act<XT>::E; ++j) mx = fmaxf(mx, fabsf(h[j]));
+    for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) mx = fmaxf(mx, fabsf(h[j]));
     return mx;
 }
 
@@ -387,27 +405,27 @@ __device__ inline float slices_max(const KArgs& a, const Smem& sm, int m) {
 // Statistics of slice `sl`, computed locally when its exchange word did not
 // arrive in time.  Same thread mapping and summation order as the workgroups
 // that own that slice, so the result is bit-identical.  All threads call it.
-template <int PRO, int XT>
+template <int PRO, int XT, int EPT>
 __device__ inline void slice_stat(const KArgs& a, Smem& sm, uint32_t wt, int lane, int wv, int sl,
                                   bool want_ss) {
-    constexpr int E = Act<XT>::E;
-    const Act<XT> am = act_map<XT>(a, wt, lane);
-    uint4 xr[Act<XT>::NCH], ur[Act<XT>::NCH];
-    float h[Act<XT>::NCH * E];
-    load_act<PRO, XT>(a, am, sl * a.KS, xr, ur);
-    finish_act<PRO, XT>(am, xr, ur, h);
+    constexpr int E = Act<XT, EPT>::E;
+    const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
+    uint4 xr[Act<XT, EPT>::NCH], ur[Act<XT, EPT>::NCH];
+    float h[Act<XT, EPT>::NCH * E];
+    load_act<PRO, XT, EPT>(a, am, sl * a.KS, xr, ur);
+    finish_act<PRO, XT, EPT>(am, xr, ur, h);
     if (want_ss) {
-        const double ss = wave_sum(sum_sq<XT>(h));
+        const double ss = wave_sum(sum_sq<XT, EPT>(h));
         if (lane == 0) sm.wd[wv] = ss;
     } else {
         if (PRO == PRO_RMSNORM) {
-            float g[Act<XT>::NCH * E];
-            load_gamma<XT>(a, am, sl * a.KS, g);
+            float g[Act<XT, EPT>::NCH * E];
+            load_gamma<XT, EPT>(a, am, sl * a.KS, g);
             const float r = (am.m < a.m) ? sm.rr[am.m] : 1.0f;
 #pragma unroll
-            for (int j = 0; j < Act<XT>::NCH * E; ++j) h[j] = rms_apply(h[j], r, g[j]);
+            for (int j = 0; j < Act<XT, EPT>::NCH * E; ++j) h[j] = rms_apply(h[j], r, g[j]);
         }
-        const float mx = wave_max(abs_max<XT>(h));
+        const float mx = wave_max(abs_max<XT, EPT>(h));
         if (lane == 0) sm.wf[wv] = mx;
     }
     __syncthreads();
@@ -483,8 +501,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __shared__ Smem sm;
     constexpr int NG = 4 / GS;                  // groups per super-block
     constexpr int OFF = (FMT == FMT_W6) ? 32 : 8;
-    constexpr int E = Act<XT>::E;
-    constexpr int NCH = Act<XT>::NCH;
+    // activations per thread: 32 only where the registers allow it
+    constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : 32;
+    constexpr int E = Act<XT, EPT>::E;
+    constexpr int NCH = Act<XT, EPT>::NCH;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -578,11 +598,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    order: a wave's loads complete in issue order, so anything waited on
     //    before the weights arrive must be issued before them)
     const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const Act<XT> am = act_map<XT>(a, wt, lane);
+    const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
     uint4 xr[NCH], ur[NCH];
     float gv[NCH * E];
-    load_act<PRO, XT>(a, am, k_lo, xr, ur);
-    if (PRO == PRO_RMSNORM) load_gamma<XT>(a, am, k_lo, gv);
+    load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
+    if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
     float4 sbuf[PIPE];
@@ -596,12 +616,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // 2. activation prologue: per-row statistics of h, then q into LDS
     if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
     float h[NCH * E];
-    finish_act<PRO, XT>(am, xr, ur, h);
+    finish_act<PRO, XT, EPT>(am, xr, ur, h);
     const int mrow = am.m < M ? am.m : 0;
     const bool row_lead = lane == 0 && am.m < M && am.it == 0;   // one thread per row
 
     if (PRO == PRO_RMSNORM) {
-        const double ss = wave_sum(sum_sq<XT>(h));
+        const double ss = wave_sum(sum_sq<XT, EPT>(h));
         if (lane == 0) sm.wd[wv] = ss;
         __syncthreads();
         double tot;
@@ -611,7 +631,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             if (poller) exchange_poll(a, sm, lane, s, true);
             __syncthreads();
             for (int sl = 0; sl < a.S; ++sl)
-                if (sm.miss[sl]) slice_stat<PRO, XT>(a, sm, wt, lane, wv, sl, true);
+                if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, true);
             tot = slices_sum(a, sm, mrow);
         }
         const float ms = (float)(tot / (double)a.k);
@@ -624,7 +644,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     }
     float amx;
     {
-        const float mx = wave_max(abs_max<XT>(h));
+        const float mx = wave_max(abs_max<XT, EPT>(h));
         if (lane == 0) sm.wf[wv] = mx;
         __syncthreads();
         if (a.S == 1) {
@@ -633,7 +653,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             if (poller) exchange_poll(a, sm, lane, s, false);
             __syncthreads();
             for (int sl = 0; sl < a.S; ++sl)
-                if (sm.miss[sl]) slice_stat<PRO, XT>(a, sm, wt, lane, wv, sl, false);
+                if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, false);
             amx = slices_max(a, sm, mrow);
         }
     }
@@ -644,13 +664,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         if (a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
     }
 
-    // quantise this slice into LDS, with the sums of q that undo the weights'
-    // offset: per octet (M = 1) or per weight group and row (M >= 2).
-    // q = clamp(rint(fp32(h / sx)), -127, 127) bit-exactly: t = h * inv with
-    // inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here) of h/sx, and
-    // fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t) equals
-    // rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then
-    // (or for a tiny sx) is the quotient formed by IEEE division.
+    // quantise this slice into LDS, with -OFF times the sums of q (the term that
+    // undoes the weights' offset): per octet (M = 1) or per weight group and row
+    // (M >= 2)
     {
         constexpr int L = DOT4 ? 8 / E : (32 * GS) / E;      // chunks per summed run
         const bool exact_row = sx < 2.3509887e-38f;           // 2^-125: 1/sx may not be normal
@@ -659,27 +675,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             if (i < am.nw) {
                 const int c = am.it + i * am.tpr;
                 const bool ok = c < am.cpr;
-                float rq[E];
-                bool redo = exact_row;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float t = h[i * E + e] * inv;
-                    rq[e] = __builtin_rintf(t);
-                    redo = redo || fabsf(t - rq[e]) > 0.49998f;
-                }
-                if (redo && sx > 0.0f) {
-#pragma unroll
-                    for (int e = 0; e < E; ++e) rq[e] = __builtin_rintf(h[i * E + e] / sx);
-                }
                 uint32_t pk[E / 4];
-                int sum = 0;
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const int qi = (int)fminf(fmaxf(rq[e], -127.0f), 127.0f);
-                    sum += qi;
-                    if (e % 4 == 0) pk[e / 4] = 0u;
-                    pk[e / 4] |= (uint32_t)(qi & 0xFF) << (8 * (e % 4));
-                }
+                const int sum = quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
                 const int gsum = lane_group_sum<L>(sum);
                 if (ok) {
                     int8_t* dst = q_l + am.m * a.ks + c * E;
@@ -694,8 +691,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[0], pk[E / 4 - 1]);
                     }
                     if (c % L == 0) {
-                        if (DOT4) qs_l[c / L] = gsum;
-                        else qs_l[(c / L) * 8 + am.m] = gsum;
+                        if (DOT4) qs_l[c / L] = -OFF * gsum;
+                        else qs_l[(c / L) * 8 + am.m] = -OFF * gsum;
                     }
                 }
             }
@@ -752,7 +749,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 for (int j = 0; j < 4; ++j) {
                     const int k0 = kbase + 32 * j + 8 * hl;
                     const uint2 qv = *reinterpret_cast<const uint2*>(q_l + k0);
-                    int c = -OFF * qs_l[k0 >> 3];
+                    int c = qs_l[k0 >> 3];
                     c = __builtin_amdgcn_sdot4((int)hi[j], (int)qv.y, c, false);
                     pj[j] = __builtin_amdgcn_sdot4((int)lo[j], (int)qv.x, c, false);
                 }
@@ -780,8 +777,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     v4i c = {0, 0, 0, 0};
                     if (hl < 2) {
                         const int4 qv = *reinterpret_cast<const int4*>(qs_l + ggl * 8 + 4 * hl);
-                        c[0] = -OFF * qv.x; c[1] = -OFF * qv.y;
-                        c[2] = -OFF * qv.z; c[3] = -OFF * qv.w;
+                        c[0] = qv.x; c[1] = qv.y; c[2] = qv.z; c[3] = qv.w;
                     }
 #pragma unroll
                     for (int jj = 0; jj < GS; ++jj)
@@ -956,67 +952,94 @@ int g_split_override = 0;
 // launch planning (pure host logic)
 // ---------------------------------------------------------------------------
 
+namespace {
+
+// Waves of a workgroup: TW tile groups x KW waves along k (KW divides the
+// slice's KBs super-blocks).  Each wave walks ceil(tiles / TW) tile steps of
+// KBs / KW super-blocks; the split with the fewest slots per wave wins, then
+// the one with the fewest tile steps (each ends with a workgroup barrier).
+// Returns the slots per wave.
+int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int& KW, int& TW) {
+    KW = 1;
+    TW = 1;
+    int64_t best_slots = -1, best_steps = -1;
+    for (int kw = 1; kw <= nwa && KBs > 0; ++kw) {
+        if (KBs % kw != 0) continue;
+        int tw = nwa / kw;
+        while (tw > 1 && tw * m * 16 > NT) --tw;      // the epilogue uses one thread per output
+        if (tw > tiles_per_wg) tw = tiles_per_wg;
+        const int64_t steps = (tiles_per_wg + tw - 1) / tw;
+        const int64_t slots = steps * (KBs / kw);
+        if (best_slots < 0 || slots < best_slots || (slots == best_slots && steps < best_steps)) {
+            best_slots = slots;
+            best_steps = steps;
+            KW = kw;
+            TW = tw;
+        }
+    }
+    return best_slots;
+}
+
+int workgroups_per_slice(int cus, int S, int T) {
+    int R = cus / S;
+    if (R > T) R = T;
+    return R < 1 ? 1 : R;
+}
+
+}  // namespace
+
 Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     Plan p;
-    (void)pro;
     const int KB = (int)G.KB;
     const int T = (int)G.T;
     const bool dot4 = (m == 1);
     p.WPR = NW / m;                               // waves per activation row
     const int tpr = p.WPR * 64;
-    // each thread quantises at most 16 activations of its row (four fp32 chunks)
-    auto fits = [&](int s) { return (G.k / s) / 16 <= (int64_t)tpr; };
+    // each thread quantises at most 16 activations of its row, 32 for M >= 2
+    // without a prologue (the kernel's register budget)
+    const int ept = (dot4 || pro != PRO_NONE) ? 16 : 32;
+    p.ept = ept;
+    auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
         const size_t qs = dot4 ? (KS / 8) * 4 : (KS / G.g) * 8 * 4;
         return (size_t)m * (KS + 32) + qs + 2 * (size_t)NW * 128 * 4;
     };
     const size_t kLdsMax = 150 * 1024;
+    auto valid = [&](int s) { return s >= 1 && s <= SMAX && KB % s == 0 && fits(s) && lds_of(s) <= kLdsMax; };
     int S = 1;
     if (split_override > 0) {
         S = split_override;
-    } else {
-        // the smallest divisor of KB whose slice fits the thread layout and LDS, and
-        // for M > 1 keeps each workgroup's quantisation work (M x K/S) small
-        const int64_t want = (m == 1) ? ((int64_t)1 << 40) : 12288;
-        for (S = 1; S < SMAX; ++S) {
-            if (KB % S != 0) continue;
-            if (fits(S) && lds_of(S) <= kLdsMax && (int64_t)m * (G.k / S) <= want) break;
+    } else if (!valid(1)) {
+        // The slice must fit the thread layout and LDS.  Among the K-splits that
+        // do, the cheapest: weight slots per wave plus the cross-slice exchange
+        // and merge, priced at about 4 + S/4 slots (ties: fewer slices).
+        int64_t best = -1;
+        for (int s = 2; s <= SMAX; ++s) {
+            if (!valid(s)) continue;
+            const int R = workgroups_per_slice(cus, s, T);
+            int kw, tw;
+            const int64_t slots = split_waves(KB / s, (T + R - 1) / R, m, NW - 1, kw, tw);
+            const int64_t cost = 4 * slots + 16 + s;
+            if (best < 0 || cost < best) {
+                best = cost;
+                S = s;
+            }
         }
-        while (S > 1 && KB % S != 0) --S;
     }
     p.S = S;
     p.KBs = (S > 0 && KB % S == 0) ? KB / S : 0;
     p.KS = (S > 0) ? (int)(G.k / S) : 0;
-    int R = (S > 0) ? cus / S : 1;
-    if (R > T) R = T;
-    if (R < 1) R = 1;
+    const int R = (S > 0) ? workgroups_per_slice(cus, S, T) : 1;
     p.R = R;
-    // waves: TW tile groups x KW waves along k (KW divides the slice's
-    // super-blocks); with S > 1 one wave is reserved for the exchange
-    const int nwa = (S > 1) ? NW - 1 : NW;
-    const int tiles_per_wg = (T + R - 1) / R;
-    p.KW = 1;
-    p.TW = 1;
-    int best = -1;
-    for (int kw = 1; kw <= nwa && p.KBs > 0; ++kw) {
-        if (p.KBs % kw != 0) continue;
-        int tw = nwa / kw;
-        while (tw > 1 && tw * m * 16 > NT) --tw;      // the epilogue uses one thread per output
-        const int used = kw * (tw < tiles_per_wg ? tw : tiles_per_wg);
-        if (used > best) {                           // ties: fewer, longer tile flushes
-            best = used;
-            p.KW = kw;
-            p.TW = tw;
-        }
-    }
+    // with S > 1 one wave is reserved for the exchange
+    split_waves(p.KBs, (T + R - 1) / R, m, (S > 1) ? NW - 1 : NW, p.KW, p.TW);
     p.spw = p.KW > 0 ? p.KBs / p.KW : 0;
     p.P = S * R;
     p.ks = p.KS + 32;
     p.lds = (S > 0) ? lds_of(S) : 0;
     p.part_floats = (S > 1) ? (size_t)T * S * m * 16 : 0;
-    p.ok = S >= 1 && S <= SMAX && KB % S == 0 && p.KBs >= 1 && fits(S) && p.spw >= 1 &&
-           p.lds <= kLdsMax && p.P >= 1 && m >= 1 && m <= 8;
+    p.ok = valid(S) && p.KBs >= 1 && p.spw >= 1 && p.P >= 1 && m >= 1 && m <= 8;
     return p;
 }
 
@@ -1121,7 +1144,7 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.jn1 = (a.tq + 1 + p.TW - 1) / p.TW;
     a.tstep = (int64_t)p.TW * G.tile_full - (int64_t)p.spw * a.sbf;
     const int epc = (c.xt == 1) ? 8 : 4;           // activations per 16-byte chunk
-    const int nch = 16 / epc;                      // chunks per thread
+    const int nch = p.ept / epc;                   // chunks per thread
     a.cpr = p.KS / epc;
     a.tpr = p.WPR * 64;
     for (int w = 0; w < NW; ++w) {

@@ -288,7 +288,8 @@ def test_forced_split_matches_oracle(split, pro, reset_hooks):
         p = sk.gemm_plan(n, k, g, 0, m, prologue=pro)
         sk.set_split(split)
         tpr = (16 // m) * 64
-        if (k // split) // 8 > tpr * 2:
+        ept = 16 if (m == 1 or pro != sk.PRO_NONE) else 32     # activations per thread
+        if (k // split) // ept > tpr:
             with pytest.raises(sk.SkError):
                 run_prologue(w, pro, k, m, 72 + m)
             continue

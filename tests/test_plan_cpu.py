@@ -9,7 +9,7 @@ import pytest
 
 import gemm_sk_repack_amd as sk
 
-NW, MO = 16, 2
+NW = 16
 
 SHAPES = [
     # n, k, g, fmt
@@ -32,7 +32,8 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert p["KBs"] == KB // S and p["KS"] == k // S
     assert p["P"] == S * p["R"] and p["P"] <= 256 and 1 <= p["R"] <= T
     assert p["WPR"] == NW // m
-    assert p["KS"] // 8 <= p["WPR"] * 64 * MO              # the slice fits the registers
+    ept = 16 if (m == 1 or pro != sk.PRO_NONE) else 32     # activations per thread
+    assert p["KS"] // ept <= p["WPR"] * 64                 # the slice fits the registers
     assert p["TW"] * p["KW"] <= NW and p["TW"] * m * 16 <= NW * 64
     assert p["spw"] * p["KW"] == p["KBs"]
     assert p["lds"] <= 150 * 1024
