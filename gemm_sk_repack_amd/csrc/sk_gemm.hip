@@ -538,59 +538,74 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int qs_n = DOT4 ? (a.KS >> 3) : (a.KS / (32 * GS)) * 8;
     float* red_l = reinterpret_cast<float*>(qs_l + qs_n);
 
+    // Slots: the wave's weight stream is a sequence of super-blocks, spw per tile
+    // step; tile step j is tile t_begin + tg + j * TW.  Slots [0, nvalid) hold
+    // work; every wave walks jall slots (the tile barriers); the rest of the
+    // load stream reads stand-in bytes at the start of the weight.
+    const int ntile = t_end - t_begin;
+    const int jw = (active && tg < ntile) ? (ntile - tg + a.TW - 1) / a.TW : 0;
+    const int nvalid = jw * a.spw;
+    const int jall = jn * a.spw;
+
     // Per-lane byte offsets inside a super-block: a full tile (16 rows) and the
-    // weight's ragged last tile (nr_last rows; its lanes nl >= nr_last idle).
+    // weight's ragged last tile (nr_last rows; its lanes nl >= nr_last read
+    // offset 0 and feed only their own, never stored, row).  Offsets of a full
+    // tile stay inside the weight's first super-block, so a stand-in slot can
+    // read them from base 0.
     const int nr_rag = a.nr_last;
     const bool lane_rag_ok = nl < nr_rag;
-    const int lw_full = lane * 16, lw_rag = (hl * nr_rag + nl) * 16;
-    const int lh_full = 16 * 64 + lane * 8, lh_rag = nr_rag * 64 + (hl * nr_rag + nl) * 8;
-    const int ls = nl * NG * 4;
+    const int lw_full = lane * 16, lw_rag = lane_rag_ok ? (hl * nr_rag + nl) * 16 : 0;
+    const int lh_full = 16 * 64 + lane * 8, lh_rag = lane_rag_ok ? nr_rag * 64 + (hl * nr_rag + nl) * 8 : 0;
+    const int ls_full = nl * NG * 4, ls_rag = lane_rag_ok ? nl * NG * 4 : 0;
 
-    // A position in the wave's slot sequence: tile-group step j, super-block u
-    // of the wave's k-part, tile t and the full-tile byte offset of the slot.
-    struct Cur {
-        int j, u, t;
-        int64_t off;
-    };
-    auto start = [&]() {
-        Cur c;
-        c.j = 0;
-        c.u = 0;
-        c.t = t_begin + tg;
-        c.off = (int64_t)c.t * a.tile_full + (int64_t)kbw * a.sbf;
-        return c;
-    };
-    auto advance = [&](Cur& c) {
-        c.off += a.sbf;
-        if (++c.u == a.spw) {
-            c.u = 0;
-            ++c.j;
-            c.t += a.TW;
-            c.off += a.tstep;
+    // Load-side cursor: the next slot's index, super-block within the tile
+    // step, tile step, byte offsets of its weights and scales, their per-slot
+    // strides and the lane offsets of its tile kind.
+    int li = 0, lu = 0, lj = 0;
+    int64_t lwo = 0, lso = 0;
+    int lwst = 0, lsst = 0;
+    bool lrag = false;
+    auto tile_setup = [&]() {          // for tile step lj, super-block 0
+        const int t = t_begin + tg + lj * a.TW;
+        lrag = t == a.t_rag;
+        if (lrag) {
+            lwo = a.rag_w + (int64_t)kbw * a.rag_sbw;
+            lso = a.rag_s + (int64_t)kbw * a.rag_sbs;
+            lwst = a.rag_sbw;
+            lsst = a.rag_sbs;
+        } else {
+            lwo = (int64_t)t * a.tile_full + (int64_t)kbw * a.sbf;
+            lso = lwo + a.swo;
+            lwst = a.sbf;
+            lsst = a.sbf;
         }
     };
-    // The slot at c into registers.  Every wave issues the same load
-    // instructions; a slot outside the work reads the weight's first bytes, so
-    // the compiler's wait counts are exact.
-    auto load = [&](const Cur& c, uint4& w4, uint2& h2, float4& sv) {
-        const bool valid = active && c.j < jn && c.t < t_end;
-        const int kb = kbw + c.u;
-        const bool rag = c.t == a.t_rag;
-        const int64_t wp = rag ? a.rag_w + (int64_t)kb * a.rag_sbw : c.off;
-        const int64_t sp = rag ? a.rag_s + (int64_t)kb * a.rag_sbs : c.off + a.swo;
-        const bool ok = valid && (!rag || lane_rag_ok);
-        const int64_t woff = ok ? wp + (rag ? lw_rag : lw_full) : 0;
-        const int64_t hoff = ok ? wp + (rag ? lh_rag : lh_full) : 0;
-        const int64_t soff = ok ? sp + ls : 0;
-        w4 = *reinterpret_cast<const uint4*>(a.data + woff);
-        if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(a.data + hoff);
+    tile_setup();
+    // The next slot into registers, then advance.  Every wave issues the same
+    // load instructions, so the compiler's wait counts are exact.
+    auto load_next = [&](uint4& w4, uint2& h2, float4& sv) {
+        const bool valid = li < nvalid;
+        const uint8_t* wb = a.data + (valid ? lwo : 0);
+        const uint8_t* sb = a.data + (valid ? lso : 0);
+        const int lw = lrag ? lw_rag : lw_full;
+        const int ls = lrag ? ls_rag : ls_full;
+        w4 = *reinterpret_cast<const uint4*>(wb + lw);
+        if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (lrag ? lh_rag : lh_full));
         if (NG == 4) {
-            sv = *reinterpret_cast<const float4*>(a.data + soff);
+            sv = *reinterpret_cast<const float4*>(sb + ls);
         } else if (NG == 2) {
-            const float2 v = *reinterpret_cast<const float2*>(a.data + soff);
+            const float2 v = *reinterpret_cast<const float2*>(sb + ls);
             sv = make_float4(v.x, v.y, 0.0f, 0.0f);
         } else {
-            sv = make_float4(*reinterpret_cast<const float*>(a.data + soff), 0.0f, 0.0f, 0.0f);
+            sv = make_float4(*reinterpret_cast<const float*>(sb + ls), 0.0f, 0.0f, 0.0f);
+        }
+        ++li;
+        lwo += lwst;
+        lso += lsst;
+        if (++lu == a.spw) {
+            lu = 0;
+            ++lj;
+            if (li < nvalid) tile_setup();
         }
     };
 
@@ -606,12 +621,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
     float4 sbuf[PIPE];
-    Cur cl = start();                           // next slot to load
 #pragma unroll
-    for (int d = 0; d < PRIME; ++d) {
-        load(cl, wbuf[d], hbuf[d], sbuf[d]);
-        advance(cl);
-    }
+    for (int d = 0; d < PRIME; ++d) load_next(wbuf[d], hbuf[d], sbuf[d]);
 
     // 2. activation prologue: per-row statistics of h, then q into LDS
     if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
@@ -679,7 +690,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 const int sum = quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
                 const int gsum = lane_group_sum<L>(sum);
                 if (ok) {
-                    int8_t* dst = q_l + am.m * a.ks + c * E;
+                    // LDS order: in each 128-k super-block, octet 4j + h is stored at
+                    // position 4h + j, so a lane's four octets are contiguous
+                    const int o = (c * E) >> 3, ow = o & 15;
+                    const int pos = (o >> 4) * 128 + ((ow & 3) * 4 + (ow >> 2)) * 8 + ((c * E) & 7);
+                    int8_t* dst = q_l + am.m * a.ks + pos;
                     if (E == 4) {
                         *reinterpret_cast<uint32_t*>(dst) = pk[0];
                     } else {
@@ -691,7 +706,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[0], pk[E / 4 - 1]);
                     }
                     if (c % L == 0) {
-                        if (DOT4) qs_l[c / L] = -OFF * gsum;
+                        if (DOT4) qs_l[(o >> 4) * 16 + (ow & 3) * 4 + (ow >> 2)] = -OFF * gsum;
                         else qs_l[(c / L) * 8 + am.m] = -OFF * gsum;
                     }
                 }
@@ -701,38 +716,39 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __syncthreads();
 
 #pragma unroll
-    for (int d = PRIME; d < PIPE; ++d) {
-        load(cl, wbuf[d], hbuf[d], sbuf[d]);
-        advance(cl);
-    }
+    for (int d = PRIME; d < PIPE; ++d) load_next(wbuf[d], hbuf[d], sbuf[d]);
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int ml = nl;   // A-operand row (activation row m) of this lane
-    const int jall = jn * a.spw;
     const int iters = (jall + PIPE - 1) / PIPE * PIPE;
-    Cur cp = start();                           // next slot to consume
-    // consume the slot at cp (weights w_in/h_in, scales s_in), then the tile
-    // epilogue when it is the last super-block of its tile
+    // Consume-side cursor: slot index, super-block within the tile step, tile
+    // step, and the slot's super-block within the slice.
+    int pi = 0, pu = 0, pj = 0, kbr = kw * a.spw;
+    // consume the next slot (weights w_in/h_in, scales s_in), then the tile
+    // epilogue when it is the last super-block of its tile step
     auto process = [&](const uint4 w_in, const uint2 h_in, const float4 s_in) {
-        const int t = cp.t;
-        if (active && cp.j < jn && t < t_end) {
-            const int kbr = kw * a.spw + cp.u;           // super-block within the slice
+        // Every slot's registers count as read here, valid or not, so the
+        // compiler waits for exactly this slot's loads (a skipped read would
+        // leave them pending when the next load reuses the registers).
+        if (FMT == FMT_W6) __asm__ volatile("" ::"v"(w_in.x), "v"(h_in.x), "v"(s_in.x));
+        else __asm__ volatile("" ::"v"(w_in.x), "v"(s_in.x));
+        if (pi < nvalid) {
+            const int t = t_begin + tg + pj * a.TW;
             const int kb = kb_lo + kbr;
+            // Lanes of rows past the weight's end (ragged last tile) hold
+            // stand-in bytes; they only ever feed their own row's sums, which are
+            // never stored.
             const bool row_ok = t != a.t_rag || lane_rag_ok;
-            const uint32_t wd[4] = {row_ok ? w_in.x : 0u, row_ok ? w_in.y : 0u,
-                                    row_ok ? w_in.z : 0u, row_ok ? w_in.w : 0u};
-            const float s4[4] = {s_in.x, s_in.y, s_in.z, s_in.w};
-            float sv[NG];
-#pragma unroll
-            for (int g = 0; g < NG; ++g) sv[g] = row_ok ? s4[g] : 0.0f;
+            const uint32_t wd[4] = {w_in.x, w_in.y, w_in.z, w_in.w};
+            const float sv[4] = {s_in.x, s_in.y, s_in.z, s_in.w};
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 lo[j] = wd[j] & 0x0F0F0F0Fu;
                 hi[j] = (wd[j] >> 4) & 0x0F0F0F0Fu;
                 if (FMT == FMT_W6) {
-                    const uint32_t hd = row_ok ? ((j < 2) ? h_in.x : h_in.y) : 0u;
+                    const uint32_t hd = (j < 2) ? h_in.x : h_in.y;
                     if ((j & 1) == 0) {
                         lo[j] |= (hd << 4) & 0x30303030u;
                         hi[j] |= (hd << 2) & 0x30303030u;
@@ -743,34 +759,47 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 }
             }
             const int kbase = kbr * 128;          // slice-relative k of this super-block
+            // q of this lane: octet hl of each 32-k block j, stored contiguously
+            const uint4* qp = reinterpret_cast<const uint4*>(q_l + (DOT4 ? 0 : ml * a.ks) + kbase + hl * 32);
             if (DOT4) {
-                int pj[4];
+                const uint4 q01 = qp[0], q23 = qp[1];
+                const uint32_t qw[8] = {q01.x, q01.y, q01.z, q01.w, q23.x, q23.y, q23.z, q23.w};
+                const int4 cs = *reinterpret_cast<const int4*>(qs_l + kbr * 16 + hl * 4);
+                const int c0[4] = {cs.x, cs.y, cs.z, cs.w};
+                int part[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int k0 = kbase + 32 * j + 8 * hl;
-                    const uint2 qv = *reinterpret_cast<const uint2*>(q_l + k0);
-                    int c = qs_l[k0 >> 3];
-                    c = __builtin_amdgcn_sdot4((int)hi[j], (int)qv.y, c, false);
-                    pj[j] = __builtin_amdgcn_sdot4((int)lo[j], (int)qv.x, c, false);
+                    const int c = __builtin_amdgcn_sdot4((int)hi[j], (int)qw[2 * j + 1], c0[j], false);
+                    part[j] = __builtin_amdgcn_sdot4((int)lo[j], (int)qw[2 * j], c, false);
                 }
+                int pg[NG];
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                    int pg = 0;
+                    pg[gi] = 0;
 #pragma unroll
-                    for (int jj = 0; jj < GS; ++jj) pg += pj[gi * GS + jj];
-                    acc[0] = __builtin_fmaf(sv[gi], (float)pg, acc[0]);
-                    if (a.p_out && row_ok)
-                        atomicAdd(&a.p_out[((int64_t)t * TILE_ROWS + nl) * a.kg + kb * NG + gi], pg);
+                    for (int jj = 0; jj < GS; ++jj) pg[gi] += part[gi * GS + jj];
+                    acc[0] = __builtin_fmaf(sv[gi], (float)pg[gi], acc[0]);
+                }
+                if (a.p_out) {        // debug export: this lane's share of each group partial
+                    if (row_ok) {
+#pragma unroll
+                        for (int gi = 0; gi < NG; ++gi)
+                            atomicAdd(&a.p_out[((int64_t)t * TILE_ROWS + nl) * a.kg + kb * NG + gi], pg[gi]);
+                    }
                 }
             } else {
-                long av[4], bv[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    bv[j] = (long)((uint64_t)lo[j] | ((uint64_t)hi[j] << 32));
-                    av[j] = (ml < M) ? *reinterpret_cast<const long*>(
-                                           q_l + ml * a.ks + kbase + 32 * j + 8 * hl)
-                                     : 0L;
+                uint4 q01 = make_uint4(0u, 0u, 0u, 0u), q23 = q01;
+                if (ml < M) {
+                    q01 = qp[0];
+                    q23 = qp[1];
                 }
+                const long av[4] = {(long)((uint64_t)q01.x | ((uint64_t)q01.y << 32)),
+                                    (long)((uint64_t)q01.z | ((uint64_t)q01.w << 32)),
+                                    (long)((uint64_t)q23.x | ((uint64_t)q23.y << 32)),
+                                    (long)((uint64_t)q23.z | ((uint64_t)q23.w << 32))};
+                long bv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = (long)((uint64_t)lo[j] | ((uint64_t)hi[j] << 32));
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     const int ggl = kbr * NG + gi;    // slice-relative group
@@ -784,21 +813,24 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[gi * GS + jj],
                                                                  bv[gi * GS + jj], c, 0, 0, 0);
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        acc[rr] = __builtin_fmaf(sv[gi], (float)c[rr], acc[rr]);
-                        const int mm = 4 * hl + rr;
-                        if (a.p_out && mm < M && row_ok)
-                            a.p_out[((int64_t)mm * a.n + (int64_t)t * TILE_ROWS + nl) * a.kg +
-                                    kb * NG + gi] = c[rr];
+                    for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(sv[gi], (float)c[rr], acc[rr]);
+                    if (a.p_out) {    // debug export of the group partials
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int mm = 4 * hl + rr;
+                            if (mm < M && row_ok)
+                                a.p_out[((int64_t)mm * a.n + (int64_t)t * TILE_ROWS + nl) * a.kg +
+                                        kb * NG + gi] = c[rr];
+                        }
                     }
                 }
             }
         }
-        if (cp.j < jn && cp.u == a.spw - 1) {
+        if (pu == a.spw - 1 && pi < jall) {
             // 4. tile epilogue: fixed-order sum of the waves' partials.  The partials
             //    buffer alternates between two halves, so one barrier per tile is enough
             //    (a wave cannot reuse a half before every thread passed the next barrier).
-            float* red = red_l + (cp.j & 1) * (NW * 128);
+            float* red = red_l + (pj & 1) * (NW * 128);
             if (DOT4) {
                 // the four k-quarters of a row sit 16 lanes apart
                 float v = acc[0];
@@ -818,7 +850,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 const int ogrp = tid / (M * 16);
                 const int omm = (tid / 16) % M;
                 const int onn = tid & 15;
-                const int ot = t_begin + ogrp + cp.j * a.TW;
+                const int ot = t_begin + ogrp + pj * a.TW;
                 if (ot < t_end) {
                     float osum = 0.0f;
                     const int w0 = ogrp * a.KW;
@@ -840,21 +872,25 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
         }
-        advance(cp);
+        ++pi;
+        ++kbr;
+        if (++pu == a.spw) {
+            pu = 0;
+            ++pj;
+            kbr -= a.spw;
+        }
     };
 
     for (int base = 0; base < iters; base += PIPE) {
 #pragma unroll
         for (int d = 0; d < PIPE; ++d) {
             process(wbuf[d], hbuf[d], sbuf[d]);
-            load(cl, wbuf[d], hbuf[d], sbuf[d]);
-            advance(cl);
+            load_next(wbuf[d], hbuf[d], sbuf[d]);
         }
     }
 
     // 5. merge the slices' partials: the last workgroup of each tile adds them
     if (a.S > 1) {
-        const int ntile = t_end - t_begin;
         __syncthreads();
         for (int c0 = 0; c0 < ntile; c0 += kMaxTilesPerGroup) {
             const int nc = min(kMaxTilesPerGroup, ntile - c0);
