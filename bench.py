@@ -38,6 +38,25 @@ PEAK_GBPS = 8000.0
 SHAPES = [("qkv", 6144, 4096), ("o", 4096, 4096), ("gate_up", 24576, 4096), ("down", 4096, 12288)]
 GROUP = 32
 CONFIG_ID = 1          # seed recipe: 1000*config + 10*linear + tensor id
+COPY_PROBE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_w4_g32_decoder_layer_hbm_traffic.md")
+
+
+def measured_traffic(kernel_key: str):
+    """HBM bytes per launch of `kernel_key` from the committed counter summary, or
+    None when that summary was taken on a different kernel source."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    src = open(os.path.join(ROOT, "gemm_sk_repack_amd", "csrc", "sk_gemm.hip"), "rb").read()
+    m = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or m.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    m = re.search(r"traffic_bytes_per_launch\[" + re.escape(kernel_key) + r"\]:\s*([0-9]+)", text)
+    return int(m.group(1)) if m else None
 
 
 def log(*a):
@@ -56,6 +75,12 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=10, help="rotated weight copies per linear")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true", help="skip the per-shape M sweep")
+    ap.add_argument("--profile-calls", type=int, default=0,
+                    help="run this many eager steps (no graphs, no timing) and exit: the "
+                         "workload for rocprofv3 kernel traces and counters")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="copy a 256 MiB device buffer 5 times and exit: the known-size "
+                         "kernel that calibrates the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures the skinny GEMM on one GPU; --gpus above 1 is not supported "
@@ -69,6 +94,14 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 copies of {COPY_PROBE_BYTES} bytes")
+        return 0
     R = args.copies
     if R % 2:
         R += 1
@@ -110,6 +143,13 @@ def main() -> int:
             call(name, 8, 2 * s + 1)
 
     step_bytes = sum(alg_bytes(n, k, m) for _, n, k in SHAPES for m in (1, 8))
+
+    if args.profile_calls:
+        for s in range(args.profile_calls):
+            step(s)
+        torch.cuda.synchronize()
+        log(f"profile run: {args.profile_calls} eager steps of {2 * len(SHAPES)} calls")
+        return 0
 
     # ---------------- warmup (eager), then capture the timed steps ----------------
     for s in range(args.warmup):
@@ -180,7 +220,7 @@ def main() -> int:
     achieved = dom_b / (dom_us * 1e-6) / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-        "frac": round(achieved / PEAK_GBPS, 4), "traffic": None,
+        "frac": round(achieved / PEAK_GBPS, 4), "traffic": measured_traffic(f"m{dom_m}"),
         "kernel": ("gemm_kernel<W4, no prologue, f32, G32, dot4> (all M=1 calls)" if dom_m == 1
                    else "gemm_kernel<W4, no prologue, f32, G32, MFMA> (all M=8 calls)"),
         "bytes_per_launch": dom_b // len(SHAPES),
