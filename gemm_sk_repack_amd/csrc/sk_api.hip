@@ -84,7 +84,6 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
         return SK_ERR_ALIGN;
     if (w->layout != SK_LAYOUT_STREAM) return SK_ERR_LAYOUT;
     const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
-    if (w->format == SK_W4_CODEBOOK) return SK_ERR_UNSUPPORTED;
     if (!sk::gemm_plan_ok(G, m, prologue)) return SK_ERR_UNSUPPORTED;
 
     hipStream_t st = static_cast<hipStream_t>(stream);

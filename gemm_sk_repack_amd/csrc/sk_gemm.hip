@@ -50,9 +50,12 @@ constexpr int SMAX = 32;       // largest number of K-slices
 constexpr int kMaxTilesPerGroup = 64;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned long long u64;
 struct KArgs {
     const uint8_t* data;
+    const float* codebook;  // 16 levels (codebook format only)
     const void* x;
     const void* x2;
     int64_t ld;
@@ -179,6 +182,12 @@ __device__ inline int quant_chunk(const float* h, float sx, float inv, bool exac
 }
 
 #pragma clang fp contract(on)
+
+// bf16 bits of f, rounded to nearest even (finite inputs)
+__device__ inline uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 
 // ---- cross-lane reductions (DPP within 16-lane rows, then the four rows) ----
 template <int CTRL>
@@ -499,7 +508,8 @@ template <int FMT, int PRO, int XT, int GS, bool DOT4>
 __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ Smem sm;
-    constexpr int NG = 4 / GS;                  // groups per super-block
+    constexpr bool CB = FMT == FMT_CB;          // codebook levels instead of integer weights
+    constexpr int NG = (GS == 0) ? 8 : 4 / GS;  // groups per super-block (GS = 0: G = 16)
     constexpr int OFF = (FMT == FMT_W6) ? 32 : 8;
     // activations per thread: 32 only where the registers allow it
     constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : 32;
@@ -533,9 +543,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const bool active = tg < a.TW && !poller;
 
     // LDS: [q: M x ks int8][sums of q][wave partials, two halves]
-    int8_t* q_l = reinterpret_cast<int8_t*>(lds);
-    int32_t* qs_l = reinterpret_cast<int32_t*>(lds + (size_t)M * a.ks);
-    const int qs_n = DOT4 ? (a.KS >> 3) : (a.KS / (32 * GS)) * 8;
+    // (codebook: [16 levels as bf16 hi|lo pairs][q as bf16: M x ks bytes][wave partials])
+    uint32_t* lut_l = reinterpret_cast<uint32_t*>(lds);
+    int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
+    int32_t* qs_l = reinterpret_cast<int32_t*>(q_l + (size_t)M * a.ks);
+    const int qs_n = CB ? 0 : DOT4 ? (a.KS >> 3) : (a.KS / (32 * (GS ? GS : 1))) * 8;
     float* red_l = reinterpret_cast<float*>(qs_l + qs_n);
 
     // Slots: the wave's weight stream is a sequence of super-blocks, spw per tile
@@ -583,7 +595,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     tile_setup();
     // The next slot into registers, then advance.  Every wave issues the same
     // load instructions, so the compiler's wait counts are exact.
-    auto load_next = [&](uint4& w4, uint2& h2, float4& sv) {
+    auto load_next = [&](uint4& w4, uint2& h2, float4& sv, float4& sv2) {
         const bool valid = li < nvalid;
         const uint8_t* wb = a.data + (valid ? lwo : 0);
         const uint8_t* sb = a.data + (valid ? lso : 0);
@@ -591,7 +603,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         const int ls = lrag ? ls_rag : ls_full;
         w4 = *reinterpret_cast<const uint4*>(wb + lw);
         if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (lrag ? lh_rag : lh_full));
-        if (NG == 4) {
+        if (NG == 8) {
+            sv = *reinterpret_cast<const float4*>(sb + ls);
+            sv2 = *reinterpret_cast<const float4*>(sb + ls + 16);
+        } else if (NG == 4) {
             sv = *reinterpret_cast<const float4*>(sb + ls);
         } else if (NG == 2) {
             const float2 v = *reinterpret_cast<const float2*>(sb + ls);
@@ -620,12 +635,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
-    float4 sbuf[PIPE];
+    float4 sbuf[PIPE], sbuf2[PIPE];
 #pragma unroll
-    for (int d = 0; d < PRIME; ++d) load_next(wbuf[d], hbuf[d], sbuf[d]);
+    for (int d = 0; d < PRIME; ++d) load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
 
     // 2. activation prologue: per-row statistics of h, then q into LDS
     if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
+    if (CB && tid < 16) {
+        // each level as a bf16 pair hi + lo (|level - hi - lo| <= 2^-17 |level|)
+        const float v = a.codebook[tid];
+        const uint32_t hi = bf16_rne(v);
+        const uint32_t lo = bf16_rne(v - __uint_as_float(hi << 16));
+        lut_l[tid] = hi | (lo << 16);
+    }
     float h[NCH * E];
     finish_act<PRO, XT, EPT>(am, xr, ur, h);
     const int mrow = am.m < M ? am.m : 0;
@@ -679,7 +701,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // undoes the weights' offset): per octet (M = 1) or per weight group and row
     // (M >= 2)
     {
-        constexpr int L = DOT4 ? 8 / E : (32 * GS) / E;      // chunks per summed run
+        constexpr int L = CB ? 1 : DOT4 ? 8 / E : (32 * GS) / E;   // chunks per summed run
         const bool exact_row = sx < 2.3509887e-38f;           // 2^-125: 1/sx may not be normal
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
@@ -688,24 +710,42 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 const bool ok = c < am.cpr;
                 uint32_t pk[E / 4];
                 const int sum = quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
-                const int gsum = lane_group_sum<L>(sum);
+                const int gsum = CB ? 0 : lane_group_sum<L>(sum);
                 if (ok) {
                     // LDS order: in each 128-k super-block, octet 4j + h is stored at
                     // position 4h + j, so a lane's four octets are contiguous
                     const int o = (c * E) >> 3, ow = o & 15;
                     const int pos = (o >> 4) * 128 + ((ow & 3) * 4 + (ow >> 2)) * 8 + ((c * E) & 7);
-                    int8_t* dst = q_l + am.m * a.ks + pos;
-                    if (E == 4) {
-                        *reinterpret_cast<uint32_t*>(dst) = pk[0];
+                    if (CB) {
+                        // bf16 copies of q (exact: |q| <= 127), two per dword
+                        uint32_t hb[E / 2];
+#pragma unroll
+                        for (int e2 = 0; e2 < E / 2; ++e2) {
+                            const int q0 = (int)(int8_t)(pk[(2 * e2) / 4] >> (8 * ((2 * e2) % 4)));
+                            const int q1 = (int)(int8_t)(pk[(2 * e2 + 1) / 4] >> (8 * ((2 * e2 + 1) % 4)));
+                            hb[e2] = (__float_as_uint((float)q0) >> 16) |
+                                     (__float_as_uint((float)q1) & 0xFFFF0000u);
+                        }
+                        uint8_t* dst = reinterpret_cast<uint8_t*>(q_l) + am.m * a.ks + pos * 2;
+                        if (E == 4) {
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0], hb[1]);
+                        } else {
+                            *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[E / 2 - 1]);
+                        }
                     } else {
-                        *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[E / 4 - 1]);
+                        int8_t* dst = q_l + am.m * a.ks + pos;
+                        if (E == 4) {
+                            *reinterpret_cast<uint32_t*>(dst) = pk[0];
+                        } else {
+                            *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[E / 4 - 1]);
+                        }
                     }
                     if (a.q_out && r == 0) {
                         int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
                         if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[0];
                         else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[0], pk[E / 4 - 1]);
                     }
-                    if (c % L == 0) {
+                    if (!CB && c % L == 0) {
                         if (DOT4) qs_l[(o >> 4) * 16 + (ow & 3) * 4 + (ow >> 2)] = -OFF * gsum;
                         else qs_l[(c / L) * 8 + am.m] = -OFF * gsum;
                     }
@@ -716,7 +756,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __syncthreads();
 
 #pragma unroll
-    for (int d = PRIME; d < PIPE; ++d) load_next(wbuf[d], hbuf[d], sbuf[d]);
+    for (int d = PRIME; d < PIPE; ++d) load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -727,7 +767,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     int pi = 0, pu = 0, pj = 0, kbr = kw * a.spw;
     // consume the next slot (weights w_in/h_in, scales s_in), then the tile
     // epilogue when it is the last super-block of its tile step
-    auto process = [&](const uint4 w_in, const uint2 h_in, const float4 s_in) {
+    auto process = [&](const uint4 w_in, const uint2 h_in, const float4 s_in, const float4 s_in2) {
         // Every slot's registers count as read here, valid or not, so the
         // compiler waits for exactly this slot's loads (a skipped read would
         // leave them pending when the next load reuses the registers).
@@ -761,7 +801,62 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const int kbase = kbr * 128;          // slice-relative k of this super-block
             // q of this lane: octet hl of each 32-k block j, stored contiguously
             const uint4* qp = reinterpret_cast<const uint4*>(q_l + (DOT4 ? 0 : ml * a.ks) + kbase + hl * 32);
-            if (DOT4) {
+            if (CB) {
+                // Codebook: each level is hi + lo in bf16, so the per-group sum of
+                // level * q is two bf16 MFMAs with fp32 accumulation (products exact).
+                // A = q as bf16 (row ml, octet hl of block j); B = the levels of this
+                // lane's 8 codes, built from the 16-entry table in LDS.
+                const uint4* qbp = reinterpret_cast<const uint4*>(
+                    reinterpret_cast<const uint8_t*>(q_l) + ml * a.ks + (kbase + hl * 32) * 2);
+                const float sv8[8] = {s_in.x, s_in.y, s_in.z, s_in.w, s_in2.x, s_in2.y, s_in2.z, s_in2.w};
+                v4f cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 qa = (ml < M) ? qbp[j] : make_uint4(0u, 0u, 0u, 0u);
+                    uint32_t ent[8];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        ent[c] = lut_l[(wd[j] >> (8 * c)) & 15u];          // element c
+                        ent[c + 4] = lut_l[(wd[j] >> (8 * c + 4)) & 15u];  // element c + 4
+                    }
+                    uint4 bh, bl;                 // elements (0,1) (2,3) (4,5) (6,7)
+                    bh.x = __builtin_amdgcn_perm(ent[1], ent[0], 0x05040100u);
+                    bh.y = __builtin_amdgcn_perm(ent[3], ent[2], 0x05040100u);
+                    bh.z = __builtin_amdgcn_perm(ent[5], ent[4], 0x05040100u);
+                    bh.w = __builtin_amdgcn_perm(ent[7], ent[6], 0x05040100u);
+                    bl.x = __builtin_amdgcn_perm(ent[1], ent[0], 0x07060302u);
+                    bl.y = __builtin_amdgcn_perm(ent[3], ent[2], 0x07060302u);
+                    bl.z = __builtin_amdgcn_perm(ent[5], ent[4], 0x07060302u);
+                    bl.w = __builtin_amdgcn_perm(ent[7], ent[6], 0x07060302u);
+                    const bf16x8 B_hi = __builtin_bit_cast(bf16x8, bh);
+                    const bf16x8 B_lo = __builtin_bit_cast(bf16x8, bl);
+                    if (NG == 8) {
+                        // G = 16: octets 0-1 of the block are group 2j, octets 2-3 group 2j+1
+                        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+                        const bf16x8 A_e = __builtin_bit_cast(bf16x8, hl < 2 ? qa : z);
+                        const bf16x8 A_o = __builtin_bit_cast(bf16x8, hl < 2 ? z : qa);
+                        v4f ce = {0.0f, 0.0f, 0.0f, 0.0f}, co = ce;
+                        ce = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_e, B_hi, ce, 0, 0, 0);
+                        ce = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_e, B_lo, ce, 0, 0, 0);
+                        co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_o, B_hi, co, 0, 0, 0);
+                        co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_o, B_lo, co, 0, 0, 0);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            acc[rr] = __builtin_fmaf(sv8[2 * j], ce[rr], acc[rr]);
+                            acc[rr] = __builtin_fmaf(sv8[2 * j + 1], co[rr], acc[rr]);
+                        }
+                    } else {
+                        const bf16x8 A = __builtin_bit_cast(bf16x8, qa);
+                        cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B_hi, cg, 0, 0, 0);
+                        cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B_lo, cg, 0, 0, 0);
+                        if ((j + 1) % (GS ? GS : 1) == 0) {
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(sv[j / (GS ? GS : 1)], cg[rr], acc[rr]);
+                            cg = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                        }
+                    }
+                }
+            } else if (DOT4) {
                 const uint4 q01 = qp[0], q23 = qp[1];
                 const uint32_t qw[8] = {q01.x, q01.y, q01.z, q01.w, q23.x, q23.y, q23.z, q23.w};
                 const int4 cs = *reinterpret_cast<const int4*>(qs_l + kbr * 16 + hl * 4);
@@ -884,8 +979,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     for (int base = 0; base < iters; base += PIPE) {
 #pragma unroll
         for (int d = 0; d < PIPE; ++d) {
-            process(wbuf[d], hbuf[d], sbuf[d]);
-            load_next(wbuf[d], hbuf[d], sbuf[d]);
+            process(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+            load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
         }
     }
 
@@ -943,13 +1038,21 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 
 typedef void (*KernelFn)(KArgs);
 
+// The codebook runs on MFMA for every M and alone has G = 16 (GS = 0).
 template <int FMT, int PRO, int XT, int GS>
 KernelFn pick_dot(bool dot4) {
-    return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true> : gemm_kernel<FMT, PRO, XT, GS, false>;
+    if constexpr (FMT == FMT_CB) {
+        return gemm_kernel<FMT, PRO, XT, GS, false>;
+    } else {
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true> : gemm_kernel<FMT, PRO, XT, GS, false>;
+    }
 }
 template <int FMT, int PRO, int XT>
 KernelFn pick_gs(int gs, bool dot4) {
     switch (gs) {
+        case 0:
+            if constexpr (FMT == FMT_CB) return pick_dot<FMT, PRO, XT, 0>(dot4);
+            return nullptr;
         case 1: return pick_dot<FMT, PRO, XT, 1>(dot4);
         case 2: return pick_dot<FMT, PRO, XT, 2>(dot4);
         default: return pick_dot<FMT, PRO, XT, 4>(dot4);
@@ -968,7 +1071,11 @@ KernelFn pick_pro(int pro, int xt, int gs, bool dot4) {
     }
 }
 KernelFn pick(int fmt, int pro, int xt, int gs, bool dot4) {
-    return fmt == FMT_W6 ? pick_pro<FMT_W6>(pro, xt, gs, dot4) : pick_pro<FMT_W4>(pro, xt, gs, dot4);
+    switch (fmt) {
+        case FMT_W6: return pick_pro<FMT_W6>(pro, xt, gs, dot4);
+        case FMT_CB: return pick_pro<FMT_CB>(pro, xt, gs, dot4);
+        default: return pick_pro<FMT_W4>(pro, xt, gs, dot4);
+    }
 }
 
 struct DevState {
@@ -1028,18 +1135,21 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     Plan p;
     const int KB = (int)G.KB;
     const int T = (int)G.T;
-    const bool dot4 = (m == 1);
+    const bool cb = G.fmt == FMT_CB;
+    const bool dot4 = (m == 1) && !cb;
     p.WPR = NW / m;                               // waves per activation row
     const int tpr = p.WPR * 64;
     // each thread quantises at most 16 activations of its row, 32 for M >= 2
     // without a prologue (the kernel's register budget)
-    const int ept = (dot4 || pro != PRO_NONE) ? 16 : 32;
+    const int ept = (dot4 || pro != PRO_NONE || cb) ? 16 : 32;
     p.ept = ept;
     auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
+        const size_t red = 2 * (size_t)NW * 128 * 4;
+        if (cb) return 64 + (size_t)m * (2 * KS + 64) + red;      // levels, bf16 q, partials
         const size_t qs = dot4 ? (KS / 8) * 4 : (KS / G.g) * 8 * 4;
-        return (size_t)m * (KS + 32) + qs + 2 * (size_t)NW * 128 * 4;
+        return (size_t)m * (KS + 32) + qs + red;
     };
     const size_t kLdsMax = 150 * 1024;
     auto valid = [&](int s) { return s >= 1 && s <= SMAX && KB % s == 0 && fits(s) && lds_of(s) <= kLdsMax; };
@@ -1072,7 +1182,7 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     split_waves(p.KBs, (T + R - 1) / R, m, (S > 1) ? NW - 1 : NW, p.KW, p.TW);
     p.spw = p.KW > 0 ? p.KBs / p.KW : 0;
     p.P = S * R;
-    p.ks = p.KS + 32;
+    p.ks = cb ? 2 * p.KS + 64 : p.KS + 32;
     p.lds = (S > 0) ? lds_of(S) : 0;
     p.part_floats = (S > 1) ? (size_t)T * S * m * 16 : 0;
     p.ok = valid(S) && p.KBs >= 1 && p.spw >= 1 && p.P >= 1 && m >= 1 && m <= 8;
@@ -1126,12 +1236,14 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
         }
     }
 
-    const bool dot4 = (c.m == 1);
-    const int gs = (int)(G.g / 32);
+    const bool dot4 = (c.m == 1) && G.fmt != FMT_CB;
+    const int gs = (int)(G.g / 32);                // 0 for the codebook's G = 16
     KernelFn fn = pick(G.fmt, c.prologue, c.xt, gs, dot4);
+    if (!fn) return hipErrorInvalidValue;
 
     KArgs a;
     a.data = c.data;
+    a.codebook = c.codebook;
     a.x = c.x;
     a.x2 = c.x2;
     a.ld = c.ld;

@@ -149,6 +149,9 @@ sk_status sk_unrepack_w4a8(sk_weight* w, void* stream);
  * the float levels) with q, where (q, sx) = per-row int8 quantisation of x
  * (sx = absmax/127, q = round-half-even(x/sx) clamped to +-127, all-zero row
  * -> sx = 0), done inside the launch [FMT activations].
+ * Codebook: each level enters as the sum of two bf16 values (hi + lo, within
+ * 2^-17 of the float level) multiplied by q exactly and summed in fp32, so P
+ * is a float close to sum(level * q) rather than an exact integer.
  *   w  : repacked SK_W4_SYM or SK_W4_CODEBOOK weight
  *   x  : device [M][K], row-major, dtype xt (SK_F32 or SK_BF16), 16-byte aligned
  *   m  : 1..8

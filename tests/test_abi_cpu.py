@@ -110,8 +110,10 @@ def test_backend_restrictions():
     assert gemm(W(k=256, g=16, layout=1)) == sk.SK_ERR_UNSUPPORTED       # W4 sym G=16
     assert gemm(W(k=256, g=8, layout=1)) == sk.SK_ERR_UNSUPPORTED        # G < 16
     assert gemm(W(k=20480, g=32, layout=1)) == sk.SK_ERR_UNSUPPORTED     # K too large
-    # the codebook GEMM is not built yet
-    assert gemm(W(fmt=1, g=16, layout=1, cb=FAKE)) == sk.SK_ERR_UNSUPPORTED
+    # the codebook GEMM has a launch plan for every supported group size
+    for g in (16, 32, 64, 128):
+        for m in (1, 8):
+            assert sk.gemm_plan(12288, 4096, g, sk.SK_W4_CODEBOOK, m)["status"] == sk.SK_OK
 
 
 def test_failed_call_leaves_descriptor_unchanged():

@@ -51,7 +51,8 @@ def assert_y_close(y, ref, tol=TOL):
 def check_call(w, buf, fmt, n, k, g, h_dev, h_ref, m):
     y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_NONE, h_dev, want_partials=(fmt != 1))
     torch.cuda.synchronize()
-    ref = O.reference(fmt, buf, n, k, g, h_ref, None)
+    cb = w.codebook.cpu().numpy() if fmt == 1 else None
+    ref = O.reference(fmt, buf, n, k, g, h_ref, cb)
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), ref["q"])
     if p is not None:
@@ -105,6 +106,11 @@ GEMM_CASES = [
     (2, 300, 1024, 64, (1, 4, 8)),
     (2, 33, 256, 32, (1, 8)),
     (2, 64, 512, 128, (1, 8)),
+    (1, 1024, 1024, 16, (1, 2, 8)),
+    (1, 300, 512, 32, (1, 8)),
+    (1, 48, 256, 64, (1, 3)),
+    (1, 33, 384, 128, (1, 8)),
+    (1, 2048, 4096, 16, (1, 8)),
 ]
 
 
@@ -337,3 +343,53 @@ def test_back_to_back_calls_in_one_graph(reset_hooks):
         for y in ys:
             assert_y_close(y.cpu().numpy(), ref)
         assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
+
+
+@pytest.mark.parametrize("pro", [sk.PRO_RMSNORM, sk.PRO_SWIGLU])
+@pytest.mark.parametrize("m", [1, 8])
+def test_codebook_with_prologues(pro, m):
+    n, k, g = 200, 1024, 16
+    w, buf = gpu_weight(1, n, k, g, 81)
+    sk.sk_repack_w4a8(w)
+    if pro == sk.PRO_SWIGLU:
+        gu = np.concatenate([S.activations(82, m, k), S.activations(83, m, k)], axis=1)
+        dev = torch.from_numpy(np.ascontiguousarray(gu)).cuda()
+        y, q, sx, _ = sk.sk_debug_gemm(w, pro, dev[:, :k], x2=dev[:, k:], want_partials=False)
+        y_pub = sk.sk_gemm_fused_swiglu(w, dev[:, :k], dev[:, k:])
+        h = O.prologue_swiglu(gu[:, :k], gu[:, k:])
+    else:
+        x = S.activations(84, m, k)
+        gam = S.gamma(85, k)
+        xd, gd = torch.from_numpy(x).cuda(), torch.from_numpy(gam).cuda()
+        y, q, sx, _ = sk.sk_debug_gemm(w, pro, xd, gamma=gd, eps=1e-6, want_partials=False)
+        y_pub = sk.sk_gemm_fused_rmsnorm(w, xd, gd, 1e-6)
+        h = O.prologue_rmsnorm(x, gam, 1e-6)
+    torch.cuda.synchronize()
+    ref = O.reference(1, buf, n, k, g, h, w.codebook.cpu().numpy())
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    assert_y_close(y.cpu().numpy(), ref)
+    assert torch.equal(y, y_pub)
+
+
+def test_codebook_of_integer_levels_equals_w4():
+    """A codebook holding the levels -8..7 is the plain W4 weight (same codes,
+    levels u - 8), so its output equals the W4 path's up to fp32 rounding."""
+    n, k, g = 256, 2048, 32
+    vals, s, buf = S.make_weight(0, n, k, g, 91, 92)
+    w4 = sk.QuantWeight(torch.from_numpy(buf.copy()).cuda(), n, k, g, 0)
+    # the same values as unsigned indices u = w + 8
+    u = (vals + 8).astype(np.uint8)
+    cb_buf = S.canonical_buffer(S.pack_u4(u), s)
+    cb = torch.arange(-8, 8, dtype=torch.float32).cuda()
+    wc = sk.QuantWeight(torch.from_numpy(cb_buf).cuda(), n, k, g, 1, cb)
+    sk.sk_repack_w4a8(w4)
+    sk.sk_repack_w4a8(wc)
+    for m in (1, 8):
+        x = torch.from_numpy(S.activations(93 + m, m, k)).cuda()
+        y4 = sk.sk_gemm_w4a8(w4, x)
+        yc = sk.sk_gemm_w4a8(wc, x)
+        torch.cuda.synchronize()
+        ref = O.reference(0, buf, n, k, g, x.cpu().numpy())
+        assert_y_close(y4.cpu().numpy(), ref)
+        assert_y_close(yc.cpu().numpy(), ref)
