@@ -67,6 +67,114 @@ def alg_bytes(n: int, k: int, m: int, g: int = GROUP, xbytes: int = 4) -> int:
     return n * k // 2 + n * (k // g) * 4 + m * k * xbytes + m * n * 4
 
 
+def time_graph(torch, stream, fn, calls):
+    """µs per call of `calls` invocations of fn(i) captured in one HIP graph (median of 3).
+    One eager call first: a call that grows the library's workspace must not be captured."""
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    t = []
+    for _ in range(3):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        t.append(a.elapsed_time(b) * 1e3 / calls)
+    return float(np.median(t))
+
+
+def time_variants(torch, sk, S, dev, stream):
+    """The other workloads: fused prologues at hidden 4096, the W6 / codebook /
+    lm_head formats at K = 4096, and one 27B-class layer (bf16 activations) whose
+    64-layer step time is extrapolated from that layer."""
+    rows = []
+
+    def weight_copies(fmt, n, k, g, cfg, li):
+        _, _, buf = S.make_weight(fmt, n, k, g, S.seed_of(cfg, li, S.TENSOR_W),
+                                  S.seed_of(cfg, li, S.TENSOR_S))
+        cb = (torch.from_numpy(S.codebook(S.seed_of(cfg, li, S.TENSOR_CB))).to(dev)
+              if fmt == sk.SK_W4_CODEBOOK else None)
+        base = sk.QuantWeight(torch.from_numpy(buf).to(dev), n, k, g, fmt, cb)
+        sk.sk_repack_w4a8(base)
+        copies = [base]
+        # more than 1 GiB of distinct weight bytes between two reads of one copy
+        for _ in range(max(1, -(-(5 << 28) // buf.nbytes)) - 1):
+            c = sk.QuantWeight(base.data.clone(), n, k, g, fmt, cb)
+            c.desc.layout = sk.SK_LAYOUT_STREAM
+            copies.append(c)
+        return copies, buf.nbytes
+
+    def record(group, name, n, k, g, fmt, m, us, nbytes, extra=0, xbytes=4):
+        alg = nbytes + (64 if fmt == sk.SK_W4_CODEBOOK else 0) + m * k * xbytes + m * n * 4 + extra
+        rows.append({"group": group, "linear": name, "n": n, "k": k, "g": g,
+                     "format": {0: "W4", 1: "W4 codebook", 2: "W6"}[fmt], "m": m,
+                     "us_per_call": round(us, 3), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
+                     "frac_peak": round(alg / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)})
+        log(f"{group:10s} {name:12s} M={m}: {us:8.3f} us/call {rows[-1]['GBps']:7.1f} GB/s")
+
+    # fused prologues at hidden 4096
+    cps, nb = weight_copies(sk.SK_W4_SYM, 6144, 4096, 32, 3, 0)
+    gam = torch.from_numpy(S.gamma(S.seed_of(3, 0, S.TENSOR_GAMMA), 4096)).to(dev)
+    for m in (1, 3, 8):
+        x = torch.from_numpy(S.activations(S.seed_of(3, 0, S.TENSOR_X), m, 4096)).to(dev)
+        y = torch.empty((m, 6144), dtype=torch.float32, device=dev)
+        us = time_graph(torch, stream, lambda i: sk.sk_gemm_fused_rmsnorm(
+            cps[i % len(cps)], x, gam, 1e-6, y=y), 4 * len(cps))
+        record("fused", "rmsnorm+qkv", 6144, 4096, 32, 0, m, us, nb, extra=4096 * 4)
+    cps, nb = weight_copies(sk.SK_W4_SYM, 4096, 12288, 32, 3, 1)
+    for m in (1, 3, 8):
+        gu = torch.from_numpy(np.concatenate(
+            [S.activations(S.seed_of(3, 1, S.TENSOR_GATE), m, 12288),
+             S.activations(S.seed_of(3, 1, S.TENSOR_UP), m, 12288)], axis=1)).to(dev)
+        y = torch.empty((m, 4096), dtype=torch.float32, device=dev)
+        us = time_graph(torch, stream, lambda i: sk.sk_gemm_fused_swiglu(
+            cps[i % len(cps)], gu[:, :12288], gu[:, 12288:], y=y), 4 * len(cps))
+        record("fused", "swiglu+down", 4096, 12288, 32, 0, m, us, nb, extra=m * 12288 * 4,
+               xbytes=4)
+    del cps
+    # formats at K = 4096
+    for li, (name, fmt, n, g) in enumerate([("w6_g64", sk.SK_W6_SYM, 12288, 64),
+                                            ("codebook_g16", sk.SK_W4_CODEBOOK, 12288, 16),
+                                            ("lm_head", sk.SK_W4_SYM, 151936, 32)]):
+        cps, nb = weight_copies(fmt, n, 4096, g, 4, li)
+        for m in (1, 8):
+            x = torch.from_numpy(S.activations(S.seed_of(4, li, S.TENSOR_X), m, 4096)).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            fn = sk.sk_gemm_w6a8 if fmt == sk.SK_W6_SYM else sk.sk_gemm_w4a8
+            us = time_graph(torch, stream, lambda i: fn(cps[i % len(cps)], x, y=y),
+                            max(8, 2 * len(cps)))
+            record("formats", name, n, 4096, g, fmt, m, us, nb)
+        del cps
+    # one 27B-class layer, bf16 activations; the 64-layer step is 64 x the layer
+    layer = [("qkv", 7168, 5120), ("o", 5120, 5120), ("gate_up", 34816, 5120),
+             ("down", 5120, 17408)]
+    for m in (1, 8):
+        tot_us = tot_b = 0.0
+        for li, (name, n, k) in enumerate(layer):
+            cps, nb = weight_copies(sk.SK_W4_SYM, n, k, 32, 2, li)
+            bits = S.to_bf16_bits(S.activations(S.seed_of(2, li, S.TENSOR_X), m, k))
+            x = torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            us = time_graph(torch, stream, lambda i: sk.sk_gemm_w4a8(cps[i % len(cps)], x, y=y),
+                            4 * len(cps))
+            record("27b_layer", name, n, k, 32, 0, m, us, nb, xbytes=2)
+            tot_us += us
+            tot_b += nb + m * k * 2 + m * n * 4
+            del cps
+        rows.append({"group": "27b_step_extrapolated", "m": m, "layers": 64,
+                     "us_per_step": round(64 * tot_us, 1),
+                     "GBps": round(tot_b / (tot_us * 1e-6) / 1e9, 1),
+                     "note": "64 x the measured layer (lm_head excluded)"})
+    return rows
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -78,6 +186,9 @@ def main() -> int:
     ap.add_argument("--profile-calls", type=int, default=0,
                     help="run this many eager steps (no graphs, no timing) and exit: the "
                          "workload for rocprofv3 kernel traces and counters")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the other workloads (fused prologues, W6 / codebook / "
+                         "lm_head formats, the 27B-class layer) and add them as `variants`")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy a 256 MiB device buffer 5 times and exit: the known-size "
                          "kernel that calibrates the HBM byte counters")
@@ -244,6 +355,8 @@ def main() -> int:
                           f"({len(os.sched_getaffinity(0))} cores visible)")}
         log(f"cpu oracle: {cpu_s:.1f}s for one step -> {cpu['value']} GB/s")
 
+    variants = time_variants(torch, sk, S, dev, stream) if args.variants else None
+
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -272,6 +385,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if variants is not None:
+        out["variants"] = variants
     print(json.dumps(out), flush=True)
     return 0
 
