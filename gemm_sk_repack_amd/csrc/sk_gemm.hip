@@ -146,7 +146,7 @@ __device__ inline float rms_apply(float x, float r, float g) {
 }
 
 // q = clamp(rint(fp32(h / sx)), -127, 127) of E values (E = 4 or 8), packed as
-// int8 into E/4 dwords; returns their sum.  For sx > 0, |h| <= 127 sx so the
+// int8 into E/4 dwords.  For sx > 0, |h| <= 127 sx so the
 // clamp never acts.  Adding 1.5 * 2^23 rounds a value of magnitude < 2^22 to
 // the nearest integer (ties to even) and leaves it in the low mantissa bits, so
 // the low byte of the sum's bit pattern is the int8 result.  t = h * inv with
@@ -155,7 +155,7 @@ __device__ inline float rms_apply(float x, float r, float g) {
 // rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then (or
 // for a tiny sx) is the quotient formed by IEEE division.
 template <int E>
-__device__ inline int quant_chunk(const float* h, float sx, float inv, bool exact_row,
+__device__ inline void quant_chunk(const float* h, float sx, float inv, bool exact_row,
                                   uint32_t pk[E / 4]) {
     const float kRound = 12582912.0f;   // 1.5 * 2^23
     uint32_t b[E];
@@ -170,15 +170,12 @@ __device__ inline int quant_chunk(const float* h, float sx, float inv, bool exac
 #pragma unroll
         for (int e = 0; e < E; ++e) b[e] = __float_as_uint(h[e] / sx + kRound);
     }
-    int sum = 0;
 #pragma unroll
     for (int w = 0; w < E / 4; ++w) {
         // bytes 0..3 <- low bytes of b[4w..4w+3]
         pk[w] = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x0C0C0400u) |
                 __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x04000C0Cu);
-        sum = __builtin_amdgcn_sdot4((int)pk[w], 0x01010101, sum, false);
     }
-    return sum;
 }
 
 #pragma clang fp contract(on)
@@ -198,18 +195,6 @@ constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
 constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within 8 lanes
 constexpr int DPP_MIRROR = 0x140;   // lane i <-> 15 - i within 16 lanes
-
-// Sum over aligned groups of L lanes (L = 1, 2, 4, 8, 16, 32); every lane of a
-// group gets the group's sum.  Integer adds, so the order does not matter.
-template <int L>
-__device__ inline int lane_group_sum(int v) {
-    if (L >= 2) v += dpp<DPP_XOR1>(v);
-    if (L >= 4) v += dpp<DPP_XOR2>(v);
-    if (L >= 8) v += dpp<DPP_HMIRROR>(v);
-    if (L >= 16) v += dpp<DPP_MIRROR>(v);
-    if (L >= 32) v += __builtin_amdgcn_ds_swizzle(v, 0x401F);   // lane ^ 16 within 32
-    return v;
-}
 
 // Max over the wave (wave-uniform result).
 __device__ inline float wave_max(float v) {
@@ -510,7 +495,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __shared__ Smem sm;
     constexpr bool CB = FMT == FMT_CB;          // codebook levels instead of integer weights
     constexpr int NG = (GS == 0) ? 8 : 4 / GS;  // groups per super-block (GS = 0: G = 16)
-    constexpr int OFF = (FMT == FMT_W6) ? 32 : 8;
+    // The weight bytes fed to the dot products hold w scaled by 16 (W4: the
+    // nibble in the byte's top half) or 4 (W6: the 6 bits in the top of the
+    // byte), so sign extension is free; the sums are scaled back at the store.
+    constexpr int WSH = (FMT == FMT_W6) ? 2 : 4;
+    constexpr float KINV = CB ? 1.0f : (FMT == FMT_W6) ? 0.25f : 0.0625f;
     // activations per thread: 32 only where the registers allow it
     constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : 32;
     constexpr int E = Act<XT, EPT>::E;
@@ -546,9 +535,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // (codebook: [16 levels as bf16 hi|lo pairs][q as bf16: M x ks bytes][wave partials])
     uint32_t* lut_l = reinterpret_cast<uint32_t*>(lds);
     int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
-    int32_t* qs_l = reinterpret_cast<int32_t*>(q_l + (size_t)M * a.ks);
-    const int qs_n = CB ? 0 : DOT4 ? (a.KS >> 3) : (a.KS / (32 * (GS ? GS : 1))) * 8;
-    float* red_l = reinterpret_cast<float*>(qs_l + qs_n);
+    float* red_l = reinterpret_cast<float*>(q_l + (size_t)M * a.ks);
 
     // Slots: the wave's weight stream is a sequence of super-blocks, spw per tile
     // step; tile step j is tile t_begin + tg + j * TW.  Slots [0, nvalid) hold
@@ -697,11 +684,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         if (a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
     }
 
-    // quantise this slice into LDS, with -OFF times the sums of q (the term that
-    // undoes the weights' offset): per octet (M = 1) or per weight group and row
-    // (M >= 2)
+    // quantise this slice into LDS
     {
-        constexpr int L = CB ? 1 : DOT4 ? 8 / E : (32 * GS) / E;   // chunks per summed run
         const bool exact_row = sx < 2.3509887e-38f;           // 2^-125: 1/sx may not be normal
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
@@ -709,8 +693,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 const int c = am.it + i * am.tpr;
                 const bool ok = c < am.cpr;
                 uint32_t pk[E / 4];
-                const int sum = quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
-                const int gsum = CB ? 0 : lane_group_sum<L>(sum);
+                quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
                 if (ok) {
                     // LDS order: in each 128-k super-block, octet 4j + h is stored at
                     // position 4h + j, so a lane's four octets are contiguous
@@ -745,10 +728,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[0];
                         else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[0], pk[E / 4 - 1]);
                     }
-                    if (!CB && c % L == 0) {
-                        if (DOT4) qs_l[(o >> 4) * 16 + (ow & 3) * 4 + (ow >> 2)] = -OFF * gsum;
-                        else qs_l[(c / L) * 8 + am.m] = -OFF * gsum;
-                    }
                 }
             }
         }
@@ -782,20 +761,20 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const bool row_ok = t != a.t_rag || lane_rag_ok;
             const uint32_t wd[4] = {w_in.x, w_in.y, w_in.z, w_in.w};
             const float sv[4] = {s_in.x, s_in.y, s_in.z, s_in.w};
+            // lo[j] / hi[j]: the bytes of codes e = 0..3 / 4..7 of octet hl of block j,
+            // each as a signed byte equal to w << WSH
             uint32_t lo[4], hi[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                lo[j] = wd[j] & 0x0F0F0F0Fu;
-                hi[j] = (wd[j] >> 4) & 0x0F0F0F0Fu;
                 if (FMT == FMT_W6) {
                     const uint32_t hd = (j < 2) ? h_in.x : h_in.y;
-                    if ((j & 1) == 0) {
-                        lo[j] |= (hd << 4) & 0x30303030u;
-                        hi[j] |= (hd << 2) & 0x30303030u;
-                    } else {
-                        lo[j] |= hd & 0x30303030u;
-                        hi[j] |= (hd >> 2) & 0x30303030u;
-                    }
+                    const uint32_t hlo = (j & 1) ? (hd << 2) : (hd << 6);   // bits 4-5 of code c
+                    const uint32_t hhi = (j & 1) ? hd : (hd << 4);          // bits 4-5 of code c + 4
+                    lo[j] = ((wd[j] << 2) & 0x3C3C3C3Cu) | (hlo & 0xC0C0C0C0u);
+                    hi[j] = ((wd[j] >> 2) & 0x3C3C3C3Cu) | (hhi & 0xC0C0C0C0u);
+                } else {
+                    lo[j] = (wd[j] << 4) & 0xF0F0F0F0u;
+                    hi[j] = wd[j] & 0xF0F0F0F0u;
                 }
             }
             const int kbase = kbr * 128;          // slice-relative k of this super-block
@@ -859,12 +838,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             } else if (DOT4) {
                 const uint4 q01 = qp[0], q23 = qp[1];
                 const uint32_t qw[8] = {q01.x, q01.y, q01.z, q01.w, q23.x, q23.y, q23.z, q23.w};
-                const int4 cs = *reinterpret_cast<const int4*>(qs_l + kbr * 16 + hl * 4);
-                const int c0[4] = {cs.x, cs.y, cs.z, cs.w};
                 int part[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int c = __builtin_amdgcn_sdot4((int)hi[j], (int)qw[2 * j + 1], c0[j], false);
+                    const int c = __builtin_amdgcn_sdot4((int)hi[j], (int)qw[2 * j + 1], 0, false);
                     part[j] = __builtin_amdgcn_sdot4((int)lo[j], (int)qw[2 * j], c, false);
                 }
                 int pg[NG];
@@ -879,7 +856,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     if (row_ok) {
 #pragma unroll
                         for (int gi = 0; gi < NG; ++gi)
-                            atomicAdd(&a.p_out[((int64_t)t * TILE_ROWS + nl) * a.kg + kb * NG + gi], pg[gi]);
+                            atomicAdd(&a.p_out[((int64_t)t * TILE_ROWS + nl) * a.kg + kb * NG + gi],
+                                      pg[gi] >> WSH);
                     }
                 }
             } else {
@@ -897,12 +875,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 for (int j = 0; j < 4; ++j) bv[j] = (long)((uint64_t)lo[j] | ((uint64_t)hi[j] << 32));
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                    const int ggl = kbr * NG + gi;    // slice-relative group
                     v4i c = {0, 0, 0, 0};
-                    if (hl < 2) {
-                        const int4 qv = *reinterpret_cast<const int4*>(qs_l + ggl * 8 + 4 * hl);
-                        c[0] = qv.x; c[1] = qv.y; c[2] = qv.z; c[3] = qv.w;
-                    }
 #pragma unroll
                     for (int jj = 0; jj < GS; ++jj)
                         c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[gi * GS + jj],
@@ -915,7 +888,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                             const int mm = 4 * hl + rr;
                             if (mm < M && row_ok)
                                 a.p_out[((int64_t)mm * a.n + (int64_t)t * TILE_ROWS + nl) * a.kg +
-                                        kb * NG + gi] = c[rr];
+                                        kb * NG + gi] = c[rr] >> WSH;
                         }
                     }
                 }
@@ -956,7 +929,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     }
                     if (a.S == 1) {
                         if (ot * TILE_ROWS + onn < a.n)
-                            a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * osum;
+                            a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (osum * KINV);
                     } else {
                         const u64 v = ((u64)sm.tag << 32) | __float_as_uint(osum);
                         __hip_atomic_store(&a.part[(((int64_t)ot * a.S + s) * M + omm) * 16 + onn], v,
@@ -1016,7 +989,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     tot += ((uint32_t)(v >> 32) == sm.tag) ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
                 }
                 if (ot * TILE_ROWS + onn < a.n)
-                    a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * tot;
+                    a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (tot * KINV);
             }
             __syncthreads();
         }
@@ -1148,8 +1121,7 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
         const size_t KS = (size_t)(G.k / s);
         const size_t red = 2 * (size_t)NW * 128 * 4;
         if (cb) return 64 + (size_t)m * (2 * KS + 64) + red;      // levels, bf16 q, partials
-        const size_t qs = dot4 ? (KS / 8) * 4 : (KS / G.g) * 8 * 4;
-        return (size_t)m * (KS + 32) + qs + red;
+        return (size_t)m * (KS + 32) + red;
     };
     const size_t kLdsMax = 150 * 1024;
     auto valid = [&](int s) { return s >= 1 && s <= SMAX && KB % s == 0 && fits(s) && lds_of(s) <= kLdsMax; };

@@ -19,9 +19,10 @@
 //     holds the 8 codes of row n at k = 128*kb + 32*j + 8*h + e, e = 0..7, as
 //     byte c = u(e=c) | u(e=c+4) << 4, so masking with 0x0F0F0F0F gives codes
 //     e = 0..3 and (>>4) & 0x0F0F0F0F gives e = 4..7, one per byte.
-//     u = w + 8 (offset binary) for W4, u = index for the codebook.
+//     u = w & 15 (two's complement, as in the canonical bytes) for W4,
+//     u = index for the codebook.
 //   W6: nr*64 bytes "low plane" laid out exactly as W4 but holding the low 4
-//     bits of u = w + 32; then nr*32 bytes "high plane": 8-byte chunk (h, n)
+//     bits of u = w & 63 (two's complement); then nr*32 bytes "high plane": 8-byte chunk (h, n)
 //     at nr*64 + (h*nr + n)*8 with two dwords; dword i covers j0 = 2i and
 //     j1 = 2i+1 of chunk (h, n): byte c = hi(j0,c) | hi(j0,c+4) << 2 |
 //     hi(j1,c) << 4 | hi(j1,c+4) << 6 with hi = u >> 4 (2 bits).
@@ -196,20 +197,20 @@ SK_HD void w4_unit_pos(const Geom& G, int64_t nr, int64_t u, int64_t* src, int64
     *dst = sb_w_rel(G, nr, kb) + (h * nr + n) * 16 + 4 * j;      // lane chunk dword
 }
 // canonical dword (little-endian bytes b0..b3: codes 2c, 2c+1) -> stream dword
-SK_HD uint32_t w4_encode(uint32_t s, uint32_t flip) {
+SK_HD uint32_t w4_encode(uint32_t s) {
     uint32_t d = 0;
     for (int c = 0; c < 4; ++c) {
-        uint32_t lo = ((s >> (8 * ((c) >> 1) + 4 * ((c) & 1))) & 0xF) ^ flip;       // code c
-        uint32_t hi = ((s >> (8 * ((c + 4) >> 1) + 4 * ((c + 4) & 1))) & 0xF) ^ flip; // code c+4
+        uint32_t lo = (s >> (8 * ((c) >> 1) + 4 * ((c) & 1))) & 0xF;       // code c
+        uint32_t hi = (s >> (8 * ((c + 4) >> 1) + 4 * ((c + 4) & 1))) & 0xF; // code c+4
         d |= (lo | (hi << 4)) << (8 * c);
     }
     return d;
 }
-SK_HD uint32_t w4_decode(uint32_t d, uint32_t flip) {
+SK_HD uint32_t w4_decode(uint32_t d) {
     uint32_t code[8];
     for (int c = 0; c < 4; ++c) {
-        code[c] = ((d >> (8 * c)) & 0xF) ^ flip;
-        code[c + 4] = ((d >> (8 * c + 4)) & 0xF) ^ flip;
+        code[c] = (d >> (8 * c)) & 0xF;
+        code[c + 4] = (d >> (8 * c + 4)) & 0xF;
     }
     uint32_t s = 0;
     for (int c = 0; c < 4; ++c) s |= (code[2 * c] | (code[2 * c + 1] << 4)) << (8 * c);
@@ -233,20 +234,20 @@ SK_HD void w6_unit_pos(const Geom& G, int64_t nr, int64_t u, int64_t* src0, int6
     *dlo1 = sb + (h * nr + n) * 16 + 4 * j1;
     *dhi = sb + nr * 64 + (h * nr + n) * 8 + 4 * i;
 }
-// 6 canonical bytes (two 24-bit LE words) -> 8 offset-binary codes u = w + 32
+// 6 canonical bytes (two 24-bit LE words) -> 8 codes u = w & 63
 SK_HD void w6_codes(const uint8_t* b, uint32_t* u) {
     uint32_t w0 = b[0] | (b[1] << 8) | (b[2] << 16);
     uint32_t w1 = b[3] | (b[4] << 8) | (b[5] << 16);
     for (int r = 0; r < 4; ++r) {
-        u[r] = ((w0 >> (6 * r)) & 0x3F) ^ 0x20;
-        u[r + 4] = ((w1 >> (6 * r)) & 0x3F) ^ 0x20;
+        u[r] = (w0 >> (6 * r)) & 0x3F;
+        u[r + 4] = (w1 >> (6 * r)) & 0x3F;
     }
 }
 SK_HD void w6_bytes(const uint32_t* u, uint8_t* b) {
     uint32_t w0 = 0, w1 = 0;
     for (int r = 0; r < 4; ++r) {
-        w0 |= ((u[r] ^ 0x20) & 0x3F) << (6 * r);
-        w1 |= ((u[r + 4] ^ 0x20) & 0x3F) << (6 * r);
+        w0 |= (u[r] & 0x3F) << (6 * r);
+        w1 |= (u[r + 4] & 0x3F) << (6 * r);
     }
     b[0] = w0 & 0xFF; b[1] = (w0 >> 8) & 0xFF; b[2] = (w0 >> 16) & 0xFF;
     b[3] = w1 & 0xFF; b[4] = (w1 >> 8) & 0xFF; b[5] = (w1 >> 16) & 0xFF;

@@ -61,7 +61,6 @@ __global__ __launch_bounds__(kReorderThreads) void tile_reorder_kernel(uint8_t* 
     const int64_t nr = tile_rows(G, t);
     uint8_t* tb = data + t * G.tile_full;
     const int tid = threadIdx.x;
-    const uint32_t flip = (FMT == FMT_W4) ? 8u : 0u;
 
     constexpr int kMaxWUnits = max_w_units<FMT>();
     uint32_t wr[kMaxWUnits][FMT == FMT_W6 ? 3 : 1];
@@ -109,7 +108,7 @@ __global__ __launch_bounds__(kReorderThreads) void tile_reorder_kernel(uint8_t* 
             if (u < U) {
                 int64_t s, d;
                 w4_unit_pos(G, nr, u, &s, &d);
-                wr[r][0] = INV ? w4_decode(ld32(tb + d), flip) : w4_encode(ld32(tb + s), flip);
+                wr[r][0] = INV ? w4_decode(ld32(tb + d)) : w4_encode(ld32(tb + s));
             }
         }
     }
@@ -246,7 +245,6 @@ bool repack_host(uint8_t* data, const Geom& G, bool inverse) {
         }
     };
     auto reorder = [&](bool inv) {
-        const uint32_t flip = (G.fmt == FMT_W4) ? 8u : 0u;
         for (int64_t t = 0; t < G.T; ++t) {
             const int64_t nr = tile_rows(G, t);
             uint8_t* tb = data + t * G.tile_full;
@@ -282,8 +280,8 @@ bool repack_host(uint8_t* data, const Geom& G, bool inverse) {
                 for (int64_t u = 0; u < w4_units(G, nr); ++u) {
                     int64_t s, d;
                     w4_unit_pos(G, nr, u, &s, &d);
-                    if (!inv) w32(d, w4_encode(r32(s), flip));
-                    else w32(s, w4_decode(r32(d), flip));
+                    if (!inv) w32(d, w4_encode(r32(s)));
+                    else w32(s, w4_decode(r32(d)));
                 }
             }
             for (int64_t u = 0; u < s_units(G, nr); ++u) {

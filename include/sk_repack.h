@@ -128,8 +128,8 @@ const char* sk_status_string(sk_status s);
  * their group scales sit together in the order the GEMM workgroups consume
  * them.  Every format is accepted (the name follows the W4A8 case).
  * No device memory is allocated: the permutation is done with in-place
- * rotations and an in-register per-tile reorder.  Weight codes are re-encoded
- * to offset binary (w + 8, w + 32) so the kernels unpack them with masks.
+ * rotations and an in-register per-tile reorder.  Weight codes keep their
+ * two's-complement values; only their positions change.
  * On success sets w->layout = SK_LAYOUT_STREAM (the host struct is updated at
  * enqueue time; the bytes are ready when the stream reaches this point).
  * Errors: NULL, SHAPE, ALIGN, FORMAT, LAYOUT (already repacked), UNSUPPORTED, HIP.

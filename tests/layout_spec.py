@@ -2,8 +2,8 @@
 (numpy, vectorised).  Test infrastructure: the library's repack, on host and on
 GPU, must produce exactly these bytes from the canonical buffer.
 
-Definition (16-row tiles, 128-k super-blocks; u = w + 8 for W4, the index for
-the codebook, w + 32 for W6):
+Definition (16-row tiles, 128-k super-blocks; u = w & 15 for W4, the index for
+the codebook, w & 63 for W6, i.e. the canonical two's-complement codes):
   * tile t at t * tile_full bytes; a full tile is KB super-blocks, each
     [weights | scales]; the ragged last tile stores all KB weight parts, then
     all KB scale parts;
@@ -26,11 +26,11 @@ import oracle as O
 def _codes(fmt, buf, n, k, g):
     vals, s = O.split_canonical(buf, fmt, n, k, g)
     if fmt == 0:
-        u = vals + 8
+        u = vals & 15
     elif fmt == 1:
         u = vals
     else:
-        u = vals + 32
+        u = vals & 63
     return u.astype(np.uint8), s
 
 
