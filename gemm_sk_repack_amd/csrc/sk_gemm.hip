@@ -263,16 +263,18 @@ __device__ inline Act<XT, EPT> act_map(const KArgs& a, uint32_t wt, int lane) {
 template <int PRO, int XT, int EPT>
 __device__ inline void load_act(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
                                 uint4 xr[Act<XT, EPT>::NCH], uint4 ur[Act<XT, EPT>::NCH]) {
-    const uint8_t* xb = static_cast<const uint8_t*>(a.x);
-    const uint8_t* ub = static_cast<const uint8_t*>(a.x2);
+    constexpr int CB = Act<XT, EPT>::E * Act<XT, EPT>::ES;     // 16 bytes per chunk
+    // the row's slice start (wave-uniform) and this thread's byte offsets in it
+    const int64_t row = ((int64_t)am.m * a.ld + k_lo) * Act<XT, EPT>::ES;
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + row;
+    const uint8_t* ub = static_cast<const uint8_t*>(a.x2) + row;
 #pragma unroll
     for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
         xr[i] = make_uint4(0u, 0u, 0u, 0u);
         ur[i] = make_uint4(0u, 0u, 0u, 0u);
         if (i < am.nw) {
             const int c = am.it + i * am.tpr;
-            const int cc = c < am.cpr ? c : 0;
-            const int64_t off = ((int64_t)am.m * a.ld + k_lo + (int64_t)cc * Act<XT, EPT>::E) * Act<XT, EPT>::ES;
+            const int off = c < am.cpr ? c * CB : 0;
             xr[i] = *reinterpret_cast<const uint4*>(xb + off);
             if (PRO == PRO_SWIGLU) ur[i] = *reinterpret_cast<const uint4*>(ub + off);
         }
@@ -687,6 +689,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // quantise this slice into LDS
     {
         const bool exact_row = sx < 2.3509887e-38f;           // 2^-125: 1/sx may not be normal
+        // LDS order: in each 128-k super-block, octet 4j + h is stored at position
+        // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
+        // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
+        // is chunk 0's plus i whole super-blocks.
+        const int c0 = am.it;
+        const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
+        const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
+        const int pstep = am.tpr * E;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             if (i < am.nw) {
@@ -695,10 +705,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 uint32_t pk[E / 4];
                 quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
                 if (ok) {
-                    // LDS order: in each 128-k super-block, octet 4j + h is stored at
-                    // position 4h + j, so a lane's four octets are contiguous
-                    const int o = (c * E) >> 3, ow = o & 15;
-                    const int pos = (o >> 4) * 128 + ((ow & 3) * 4 + (ow >> 2)) * 8 + ((c * E) & 7);
+                    const int pos = pos0 + i * pstep;
                     if (CB) {
                         // bf16 copies of q (exact: |q| <= 127), two per dword
                         uint32_t hb[E / 2];
