@@ -145,37 +145,19 @@ __device__ inline float rms_apply(float x, float r, float g) {
     return t * g;
 }
 
-// q = clamp(rint(fp32(h / sx)), -127, 127) of E values (E = 4 or 8), packed as
-// int8 into E/4 dwords.  For sx > 0, |h| <= 127 sx so the
-// clamp never acts.  Adding 1.5 * 2^23 rounds a value of magnitude < 2^22 to
+// Activation codes q = clamp(rint(fp32(h / sx)), -127, 127), packed as int8
+// four to a dword.  For sx > 0, |h| <= 127 sx so the clamp never acts.  Adding 1.5 * 2^23 rounds a value of magnitude < 2^22 to
 // the nearest integer (ties to even) and leaves it in the low mantissa bits, so
 // the low byte of the sum's bit pattern is the int8 result.  t = h * inv with
 // inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here) of h/sx, and
 // fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t) equals
 // rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then (or
 // for a tiny sx) is the quotient formed by IEEE division.
-template <int E>
-__device__ inline void quant_chunk(const float* h, float sx, float inv, bool exact_row,
-                                  uint32_t pk[E / 4]) {
-    const float kRound = 12582912.0f;   // 1.5 * 2^23
-    uint32_t b[E];
-    bool redo = exact_row;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const float t = h[e] * inv;
-        b[e] = __float_as_uint(t + kRound);
-        redo = redo || fabsf(__builtin_amdgcn_fractf(t) - 0.5f) < 2e-5f;
-    }
-    if (redo && sx > 0.0f) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) b[e] = __float_as_uint(h[e] / sx + kRound);
-    }
-#pragma unroll
-    for (int w = 0; w < E / 4; ++w) {
-        // bytes 0..3 <- low bytes of b[4w..4w+3]
-        pk[w] = __builtin_amdgcn_perm(b[4 * w + 1], b[4 * w], 0x0C0C0400u) |
-                __builtin_amdgcn_perm(b[4 * w + 3], b[4 * w + 2], 0x04000C0Cu);
-    }
+constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr float kTieBand = 2e-5f;
+// bytes 0..3 <- low bytes of b0..b3
+__device__ inline uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
 }
 
 #pragma clang fp contract(on)
@@ -373,6 +355,20 @@ __device__ inline float combine_f(const KArgs& a, const Smem& sm, int m) {
             if (4 * q + k >= lo && 4 * q + k < hi) s = fmaxf(s, e[k]);
     }
     return s;
+}
+// Max over the waves of row m (m wave-uniform): lane k of each 16-lane row
+// takes wave k's value, and a max within the row leaves the result in every
+// lane.  Values are >= 0, so 0 stands in for waves of other rows.
+__device__ inline float row_max(const KArgs& a, const Smem& sm, int m, int lane) {
+    const int k = lane & 15;
+    const int lo = m * a.WPR;
+    const float w = sm.wf[k];
+    float v = (k >= lo && k < lo + a.WPR) ? w : 0.0f;
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_HMIRROR>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_MIRROR>(__float_as_int(v))));
+    return v;
 }
 // Row m's statistic over all slices (S > 1), slices in ascending order.
 __device__ inline double slices_sum(const KArgs& a, const Smem& sm, int m) {
@@ -670,7 +666,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         if (lane == 0) sm.wf[wv] = mx;
         __syncthreads();
         if (a.S == 1) {
-            amx = combine_f(a, sm, mrow);
+            amx = row_max(a, sm, mrow, lane);
         } else {
             if (poller) exchange_poll(a, sm, lane, s, false);
             __syncthreads();
@@ -686,9 +682,27 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         if (a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
     }
 
-    // quantise this slice into LDS
-    {
-        const bool exact_row = sx < 2.3509887e-38f;           // 2^-125: 1/sx may not be normal
+    // quantise this slice into LDS (straight-line code: it runs once per
+    // launch, so every instruction of it is a cold instruction-cache fetch)
+    if (am.nw > 0) {
+        // codes of all elements first; the exact division, rarely needed, is one
+        // out-of-line block for the whole thread
+        uint32_t b[NCH * E];
+        float dev = 1.0f;           // min over elements of |fract(t) - 0.5|
+#pragma unroll
+        for (int j = 0; j < NCH * E; ++j) {
+            const float t = h[j] * inv;
+            b[j] = __float_as_uint(t + kRoundMagic);
+            dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
+        }
+        // 2^-125: 1/sx may not be normal
+        if (__builtin_expect((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f, 0)) {
+#pragma unroll
+            for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+        }
+        uint32_t pk[NCH * E / 4];
+#pragma unroll
+        for (int w = 0; w < NCH * E / 4; ++w) pk[w] = pack_low_bytes(b[4 * w], b[4 * w + 1], b[4 * w + 2], b[4 * w + 3]);
         // LDS order: in each 128-k super-block, octet 4j + h is stored at position
         // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
         // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
@@ -699,42 +713,39 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         const int pstep = am.tpr * E;
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
-            if (i < am.nw) {
-                const int c = am.it + i * am.tpr;
-                const bool ok = c < am.cpr;
-                uint32_t pk[E / 4];
-                quant_chunk<E>(h + i * E, sx, inv, exact_row, pk);
-                if (ok) {
-                    const int pos = pos0 + i * pstep;
-                    if (CB) {
-                        // bf16 copies of q (exact: |q| <= 127), two per dword
-                        uint32_t hb[E / 2];
+            const uint32_t* pc = pk + i * (E / 4);
+            const bool ok = i < am.nw && am.it + i * am.tpr < am.cpr;
+            const int pos = pos0 + i * pstep;
+            if (CB) {
+                // bf16 copies of q (exact: |q| <= 127), two per dword
+                uint32_t hb[E / 2];
 #pragma unroll
-                        for (int e2 = 0; e2 < E / 2; ++e2) {
-                            const int q0 = (int)(int8_t)(pk[(2 * e2) / 4] >> (8 * ((2 * e2) % 4)));
-                            const int q1 = (int)(int8_t)(pk[(2 * e2 + 1) / 4] >> (8 * ((2 * e2 + 1) % 4)));
-                            hb[e2] = (__float_as_uint((float)q0) >> 16) |
-                                     (__float_as_uint((float)q1) & 0xFFFF0000u);
-                        }
-                        uint8_t* dst = reinterpret_cast<uint8_t*>(q_l) + am.m * a.ks + pos * 2;
-                        if (E == 4) {
-                            *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0], hb[1]);
-                        } else {
-                            *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[E / 2 - 1]);
-                        }
-                    } else {
-                        int8_t* dst = q_l + am.m * a.ks + pos;
-                        if (E == 4) {
-                            *reinterpret_cast<uint32_t*>(dst) = pk[0];
-                        } else {
-                            *reinterpret_cast<uint2*>(dst) = make_uint2(pk[0], pk[E / 4 - 1]);
-                        }
-                    }
-                    if (a.q_out && r == 0) {
-                        int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
-                        if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[0];
-                        else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[0], pk[E / 4 - 1]);
-                    }
+                for (int e2 = 0; e2 < E / 2; ++e2) {
+                    const int q0 = (int)(int8_t)(pc[(2 * e2) / 4] >> (8 * ((2 * e2) % 4)));
+                    const int q1 = (int)(int8_t)(pc[(2 * e2 + 1) / 4] >> (8 * ((2 * e2 + 1) % 4)));
+                    hb[e2] = (__float_as_uint((float)q0) >> 16) | (__float_as_uint((float)q1) & 0xFFFF0000u);
+                }
+                uint8_t* dst = reinterpret_cast<uint8_t*>(q_l) + am.m * a.ks + pos * 2;
+                if (ok) {
+                    if (E == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0], hb[1]);
+                    else *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[E / 2 - 1]);
+                }
+            } else {
+                int8_t* dst = q_l + am.m * a.ks + pos;
+                if (ok) {
+                    if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pc[0];
+                    else *reinterpret_cast<uint2*>(dst) = make_uint2(pc[0], pc[E / 4 - 1]);
+                }
+            }
+        }
+        if (a.q_out && r == 0) {          // debug export of q
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = am.it + i * am.tpr;
+                if (i < am.nw && c < am.cpr) {
+                    int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
+                    if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[i];
+                    else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[2 * i], pk[2 * i + 1]);
                 }
             }
         }
@@ -1162,6 +1173,12 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     p.spw = p.KW > 0 ? p.KBs / p.KW : 0;
     p.P = S * R;
     p.ks = cb ? 2 * p.KS + 64 : p.KS + 32;
+    // only as many waves per row as the slice needs: the activation work then
+    // sits in the waves that start first, and the other waves skip it
+    {
+        const int need = (p.KS + ept * 64 - 1) / (ept * 64);
+        if (need >= 1 && need < p.WPR) p.WPR = need;
+    }
     p.lds = (S > 0) ? lds_of(S) : 0;
     p.part_floats = (S > 1) ? (size_t)T * S * m * 16 : 0;
     p.ok = valid(S) && p.KBs >= 1 && p.spw >= 1 && p.P >= 1 && m >= 1 && m <= 8;

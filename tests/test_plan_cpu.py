@@ -31,8 +31,9 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert 1 <= S <= 32 and KB % S == 0
     assert p["KBs"] == KB // S and p["KS"] == k // S
     assert p["P"] == S * p["R"] and p["P"] <= 256 and 1 <= p["R"] <= T
-    assert p["WPR"] == NW // m
-    ept = 16 if (m == 1 or pro != sk.PRO_NONE) else 32     # activations per thread
+    ept = 16 if (m == 1 or pro != sk.PRO_NONE or fmt == sk.SK_W4_CODEBOOK) else 32
+    # waves per activation row: as many as the slice needs, at most NW / M
+    assert p["WPR"] == min(NW // m, -(-p["KS"] // (ept * 64)))
     assert p["KS"] // ept <= p["WPR"] * 64                 # the slice fits the registers
     assert p["TW"] * p["KW"] <= NW and p["TW"] * m * 16 <= NW * 64
     assert p["spw"] * p["KW"] == p["KBs"]
