@@ -241,6 +241,16 @@ __device__ inline Act<XT, EPT> act_map(const KArgs& a, uint32_t wt, int lane) {
     return am;
 }
 
+// Chunk index of a thread's i-th chunk.  The wave-uniform part goes through
+// readfirstlane so it stays a scalar added to the lane's index: folded into a
+// 64-bit multiply-add instead, the unused high half of its addend can land on
+// a register a load is still filling, and the wait for it would serialise the
+// activation loads.
+template <int XT, int EPT>
+__device__ inline int chunk_of(const Act<XT, EPT>& am, int i) {
+    return am.it + __builtin_amdgcn_readfirstlane(i * am.tpr);
+}
+
 // Raw 16-byte chunks of slice [k_lo, k_lo + KS) (SwiGLU: gate in xr, up in ur).
 template <int PRO, int XT, int EPT>
 __device__ inline void load_act(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
@@ -255,7 +265,7 @@ __device__ inline void load_act(const KArgs& a, const Act<XT, EPT>& am, int k_lo
         xr[i] = make_uint4(0u, 0u, 0u, 0u);
         ur[i] = make_uint4(0u, 0u, 0u, 0u);
         if (i < am.nw) {
-            const int c = am.it + i * am.tpr;
+            const int c = chunk_of(am, i);
             const int off = c < am.cpr ? c * CB : 0;
             xr[i] = *reinterpret_cast<const uint4*>(xb + off);
             if (PRO == PRO_SWIGLU) ur[i] = *reinterpret_cast<const uint4*>(ub + off);
@@ -272,7 +282,7 @@ __device__ inline void load_gamma(const KArgs& a, const Act<XT, EPT>& am, int k_
 #pragma unroll
         for (int e = 0; e < E; ++e) g[i * E + e] = 0.0f;
         if (i < am.nw) {
-            const int c = am.it + i * am.tpr;
+            const int c = chunk_of(am, i);
             const int cc = c < am.cpr ? c : 0;
             const float4* gp = reinterpret_cast<const float4*>(a.gamma + k_lo + (int64_t)cc * E);
 #pragma unroll
@@ -292,7 +302,7 @@ __device__ inline void finish_act(const Act<XT, EPT>& am, const uint4 xr[Act<XT,
     constexpr int E = Act<XT, EPT>::E;
 #pragma unroll
     for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
-        const bool ok = i < am.nw && am.it + i * am.tpr < am.cpr;
+        const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
         const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
         const uint32_t uw[4] = {ur[i].x, ur[i].y, ur[i].z, ur[i].w};
 #pragma unroll
@@ -714,7 +724,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 #pragma unroll
         for (int i = 0; i < NCH; ++i) {
             const uint32_t* pc = pk + i * (E / 4);
-            const bool ok = i < am.nw && am.it + i * am.tpr < am.cpr;
+            const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
             const int pos = pos0 + i * pstep;
             if (CB) {
                 // bf16 copies of q (exact: |q| <= 127), two per dword
@@ -741,7 +751,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         if (a.q_out && r == 0) {          // debug export of q
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
-                const int c = am.it + i * am.tpr;
+                const int c = chunk_of(am, i);
                 if (i < am.nw && c < am.cpr) {
                     int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
                     if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[i];
