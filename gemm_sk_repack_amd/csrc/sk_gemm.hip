@@ -518,19 +518,30 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int nl = lane & 15;
     const int hl = lane >> 4;
     const int M = a.m;
+    const int r = blockIdx.x;
+    const int s = blockIdx.y;
+    const int k_lo = s * a.KS;
+
+    // 1. the activations first: they head the longest dependency chain (x ->
+    //    statistics -> q -> every dot product), so their loads go out before
+    //    any other address arithmetic; then the call's tag and the weight stream
+    //    (a wave's loads complete in issue order)
+    const uint32_t wt = a.wtab[wv];
+    const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
+    uint4 xr[NCH], ur[NCH];
+    float gv[NCH * E];
+    load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
+    if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
+    const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
     // wave wv works on tile group tg (every TW-th tile) and super-blocks
     // [kw * spw, (kw + 1) * spw) of the slice
-    const int r = blockIdx.x;
-    const int s = blockIdx.y;
-    const int k_lo = s * a.KS;
     const int kb_lo = s * a.KBs;
     const bool big = r < a.trem;
     const int t_begin = r * a.tq + (big ? r : a.trem);
     const int t_end = t_begin + a.tq + (big ? 1 : 0);
     const int jn = big ? a.jn1 : a.jn0;         // tiles per group, padded
-    const uint32_t wt = a.wtab[wv];
     const int tg = wt & 31;
     const int kw = (wt >> 5) & 31;
     const int kbw = kb_lo + kw * a.spw;
@@ -550,7 +561,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // work; every wave walks jall slots (the tile barriers); the rest of the
     // load stream reads stand-in bytes at the start of the weight.
     const int ntile = t_end - t_begin;
-    const int jw = (active && tg < ntile) ? (ntile - tg + a.TW - 1) / a.TW : 0;
+    // tiles tg, tg + TW, ... below ntile: jn = ceil(ntile / TW) of them, one
+    // fewer for the groups past the last step's share
+    const int jw = active ? jn - (tg >= ntile - (jn - 1) * a.TW ? 1 : 0) : 0;
     const int nvalid = jw * a.spw;
     const int jall = jn * a.spw;
 
@@ -575,17 +588,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     auto tile_setup = [&]() {          // for tile step lj, super-block 0
         const int t = t_begin + tg + lj * a.TW;
         lrag = t == a.t_rag;
-        if (lrag) {
-            lwo = a.rag_w + (int64_t)kbw * a.rag_sbw;
-            lso = a.rag_s + (int64_t)kbw * a.rag_sbs;
-            lwst = a.rag_sbw;
-            lsst = a.rag_sbs;
-        } else {
-            lwo = (int64_t)t * a.tile_full + (int64_t)kbw * a.sbf;
-            lso = lwo + a.swo;
-            lwst = a.sbf;
-            lsst = a.sbf;
-        }
+        const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kbw * a.sbf;
+        lwo = lrag ? a.rag_w + (int64_t)kbw * a.rag_sbw : wo;
+        lso = lrag ? a.rag_s + (int64_t)kbw * a.rag_sbs : wo + a.swo;
+        lwst = lrag ? a.rag_sbw : a.sbf;
+        lsst = lrag ? a.rag_sbs : a.sbf;
     };
     tile_setup();
     // The next slot into registers, then advance.  Every wave issues the same
@@ -619,15 +626,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
     };
 
-    // 1. the call's tag, the activations, then the weight stream (in this
-    //    order: a wave's loads complete in issue order, so anything waited on
-    //    before the weights arrive must be issued before them)
-    const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
-    uint4 xr[NCH], ur[NCH];
-    float gv[NCH * E];
-    load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
-    if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
     float4 sbuf[PIPE], sbuf2[PIPE];
@@ -772,9 +770,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // Consume-side cursor: slot index, super-block within the tile step, tile
     // step, and the slot's super-block within the slice.
     int pi = 0, pu = 0, pj = 0, kbr = kw * a.spw;
-    // consume the next slot (weights w_in/h_in, scales s_in), then the tile
-    // epilogue when it is the last super-block of its tile step
-    auto process = [&](const uint4 w_in, const uint2 h_in, const float4 s_in, const float4 s_in2) {
+    // Sums of the tile steps that end inside a group of PIPE slots; their
+    // epilogues run after the group, from a single copy of the code (it runs
+    // once per tile step, so unrolled copies would only be more cold fetches).
+    float sav[PIPE][4];
+    uint32_t ended = 0;     // bit d: slot d of the group ended a tile step
+    int pje = 0;            // tile step of the next epilogue
+    // consume the next slot (group position d, weights w_in/h_in, scales s_in)
+    auto process = [&](const int d, const uint4 w_in, const uint2 h_in, const float4 s_in, const float4 s_in2) {
         // Every slot's registers count as read here, valid or not, so the
         // compiler waits for exactly this slot's loads (a skipped read would
         // leave them pending when the next load reuses the registers).
@@ -923,50 +926,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             }
         }
         if (pu == a.spw - 1 && pi < jall) {
-            // 4. tile epilogue: fixed-order sum of the waves' partials.  The partials
-            //    buffer alternates between two halves, so one barrier per tile is enough
-            //    (a wave cannot reuse a half before every thread passed the next barrier).
-            float* red = red_l + (pj & 1) * (NW * 128);
-            if (DOT4) {
-                // the four k-quarters of a row sit 16 lanes apart
-                float v = acc[0];
-                v += __shfl_xor(v, 16);
-                v += __shfl_xor(v, 32);
-                if (lane < 16) red[wv * 16 + nl] = v;
-            } else {
+            // last super-block of its tile step: park the sums for the epilogue
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int mm = 4 * hl + rr;
-                    if (mm < M) red[(wv * 8 + mm) * 16 + nl] = acc[rr];
-                }
+            for (int rr = 0; rr < 4; ++rr) {
+                sav[d][rr] = acc[rr];
+                acc[rr] = 0.0f;
             }
-            __syncthreads();
-            const int nout = a.TW * M * 16;
-            if (tid < nout) {
-                const int ogrp = tid / (M * 16);
-                const int omm = (tid / 16) % M;
-                const int onn = tid & 15;
-                const int ot = t_begin + ogrp + pj * a.TW;
-                if (ot < t_end) {
-                    float osum = 0.0f;
-                    const int w0 = ogrp * a.KW;
-                    if (DOT4) {
-                        for (int w = w0; w < w0 + a.KW; ++w) osum += red[w * 16 + onn];
-                    } else {
-                        for (int w = w0; w < w0 + a.KW; ++w) osum += red[(w * 8 + omm) * 16 + onn];
-                    }
-                    if (a.S == 1) {
-                        if (ot * TILE_ROWS + onn < a.n)
-                            a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (osum * KINV);
-                    } else {
-                        const u64 v = ((u64)sm.tag << 32) | __float_as_uint(osum);
-                        __hip_atomic_store(&a.part[(((int64_t)ot * a.S + s) * M + omm) * 16 + onn], v,
-                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                }
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
+            ended |= 1u << d;
         }
         ++pi;
         ++kbr;
@@ -977,11 +943,72 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
     };
 
+    // 4. tile epilogue of tile step j with this lane's sums v4: fixed-order sum
+    //    of the waves' partials.  The partials buffer alternates between two
+    //    halves, so one barrier per tile is enough (a wave cannot reuse a half
+    //    before every thread passed the next barrier).
+    auto tile_epilogue = [&](const float* v4, const int j) {
+        float* red = red_l + (j & 1) * (NW * 128);
+        if (DOT4) {
+            // the four k-quarters of a row sit 16 lanes apart
+            float v = v4[0];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (lane < 16) red[wv * 16 + nl] = v;
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int mm = 4 * hl + rr;
+                if (mm < M) red[(wv * 8 + mm) * 16 + nl] = v4[rr];
+            }
+        }
+        __syncthreads();
+        const int nout = a.TW * M * 16;
+        if (tid < nout) {
+            const int ogrp = tid / (M * 16);
+            const int omm = (tid / 16) % M;
+            const int onn = tid & 15;
+            const int ot = t_begin + ogrp + j * a.TW;
+            if (ot < t_end) {
+                float osum = 0.0f;
+                const int w0 = ogrp * a.KW;
+                if (DOT4) {
+                    for (int w = w0; w < w0 + a.KW; ++w) osum += red[w * 16 + onn];
+                } else {
+                    for (int w = w0; w < w0 + a.KW; ++w) osum += red[(w * 8 + omm) * 16 + onn];
+                }
+                if (a.S == 1) {
+                    if (ot * TILE_ROWS + onn < a.n)
+                        a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (osum * KINV);
+                } else {
+                    const u64 v = ((u64)sm.tag << 32) | __float_as_uint(osum);
+                    __hip_atomic_store(&a.part[(((int64_t)ot * a.S + s) * M + omm) * 16 + onn], v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    };
+
     for (int base = 0; base < iters; base += PIPE) {
 #pragma unroll
         for (int d = 0; d < PIPE; ++d) {
-            process(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+            process(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
             load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+        }
+        // epilogues of the tile steps that ended in this group, in order
+#pragma clang loop unroll(disable)
+        while (ended) {
+            const int d = __builtin_ctz(ended);
+            ended &= ended - 1;
+            float v[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                v[rr] = sav[0][rr];
+#pragma unroll
+                for (int dd = 1; dd < PIPE; ++dd) v[rr] = (d == dd) ? sav[dd][rr] : v[rr];
+            }
+            tile_epilogue(v, pje);
+            ++pje;
         }
     }
 
