@@ -1,0 +1,1120 @@
+// sk_gemm_kernel.h -- the skinny quantized GEMM kernel for gfx950 (MI355X).
+//
+//   y[m][n] = sx[m] * sum_j s[n][j] * P[m][n][j],   m < M <= 8,
+//   P[m][n][j] = sum_{k in group j} w[n][k] * q[m][k]          (exact int32)
+//
+// ("Doubling the LLM token rate in ComfyUI", section on optimizing linear
+// kernels; "Comfy quantization formats", sections on weight formats and on
+// activations.)  One launch does everything.  The grid holds one 1024-thread
+// workgroup per compute unit; workgroup p works on K-slice s = p / R of the
+// weight (S slices) for a contiguous range of 16-row tiles, so it needs the
+// activations of its own slice only.
+//
+//  1. Load this thread's activations first (they head the longest chain:
+//     x -> statistics -> q -> every dot product), then the first PRIME
+//     super-blocks of the weight stream.  Every load is unconditional (an
+//     out-of-range slot reads a harmless in-bounds address), so the number of
+//     outstanding loads is known at compile time and waiting for the
+//     activations never waits for the weight stream.
+//  2. Activation prologue while the weights are in flight: optional RMSNorm or
+//     SwiGLU; per-row statistics.  With S > 1 the full-row sum of squares and
+//     absmax are exchanged between slices through tagged device-scope words
+//     (one wave publishes and polls; the wait is bounded and a time-out falls
+//     back to computing the missing slices locally).  Then sx = absmax/127 and
+//     q = rint(h/sx) -> int8 in LDS.  This code runs once per launch, so it is
+//     kept short and straight: every instruction of it is a cold fetch.
+//  3. Stream the tiles through a register pipeline of PIPE slots.  Weight
+//     codes are two's complement; the bytes fed to the dot products hold
+//     w << 4 (W4) or w << 2 (W6), so the integer sums are the exact per-group
+//     partials times 16 or 4 (undone by a power of two at the store).  M >= 2
+//     uses v_mfma_i32_16x16x32_i8 (q = A operand, M padded to 16; weights =
+//     B); M = 1 uses v_dot4_i32_i8.  Each partial is scaled by its FP32 group
+//     scale and accumulated in fp32.
+//  4. Per tile, the waves' sums are added in a fixed order through LDS.  With
+//     S = 1 the workgroup writes y.  Otherwise it stores a tagged partial; at
+//     the end, the last of a tile's S workgroups to arrive adds the S
+//     partials in slice order and writes y.  No floating-point atomics and no
+//     cache-flushing fences: results are deterministic.
+//
+// Included by one translation unit per weight format and build flavour, each
+// instantiating its kernels (sk_gemm_*.hip); the launch logic is in sk_gemm.hip.
+#ifndef SK_GEMM_KERNEL_H
+#define SK_GEMM_KERNEL_H
+
+#include <hip/hip_runtime.h>
+
+#include "sk_internal.h"
+
+namespace sk {
+
+
+constexpr int NW = 16;         // waves per workgroup
+constexpr int NT = NW * 64;    // threads per workgroup
+constexpr int PIPE = 4;        // super-blocks in flight per wave
+constexpr int PRIME = 2;       // of which issued before the activation prologue
+constexpr int SMAX = 32;       // largest number of K-slices
+constexpr int kMaxTilesPerGroup = 64;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned long long u64;
+struct KArgs {
+    const uint8_t* data;
+    const float* codebook;  // 16 levels (codebook format only)
+    const void* x;
+    const void* x2;
+    int64_t ld;
+    const float* gamma;
+    float eps;
+    float* y;
+    int8_t* q_out;
+    float* sx_out;
+    int32_t* p_out;
+    WsHeader* ws;
+    uint32_t* cnt;
+    u64* part;
+    int n, k, m;
+    int T, KB, kg;
+    int S, R, P, TW, KW, spw, KBs, KS, WPR, ks;
+    int spin_limit;
+    // tiles of block r: [r * tq + min(r, trem), ... + tq + (r < trem)); jn1 / jn0
+    // = tiles per tile group, rounded up, for the two block sizes
+    int tq, trem, jn0, jn1;
+    // stream-layout addressing: full tiles (16 rows) and the ragged last tile
+    int64_t tile_full;      // bytes per full tile
+    int64_t tstep;          // TW * tile_full - spw * sbf: from a tile's last slot to the next tile
+    int sbf, swo;           // bytes per super-block of a full tile; offset of its scales
+    int cpr, tpr;           // activation chunks per row of the slice; threads per row
+    int t_rag;              // index of the ragged tile, -1 if N % 16 == 0
+    int nr_last;            // rows of the ragged tile (16 if none)
+    int64_t rag_w, rag_s;   // byte offsets of the ragged tile's weights and scales
+    int rag_sbw, rag_sbs;   // their bytes per super-block
+    // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
+    // wave index within the row (14-18) and activation chunk steps (19-22)
+    uint32_t wtab[NW];
+};
+
+struct Smem {
+    alignas(16) double wd[NW];          // per-wave values
+    alignas(16) float wf[NW];
+    alignas(16) double exd[8 * SMAX];   // [row][slice] statistics of the slices
+    alignas(16) float exf[8 * SMAX];
+    float sx[8];
+    float inv[8];
+    float rr[8];
+    int miss[SMAX];
+    uint32_t tag;
+    int last[kMaxTilesPerGroup];
+};
+
+typedef void (*KernelFn)(KArgs);
+
+// One picker per (format, debug exports) translation unit.
+KernelFn pick_kernel_w4(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_w6(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_cb(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_w4_dbg(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_w6_dbg(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_cb_dbg(int pro, int xt, int gs, bool dot4);
+
+namespace {
+
+
+// --------------------------------------------------------------------------
+// activation helpers
+// --------------------------------------------------------------------------
+
+#pragma clang fp contract(off)
+
+// e^x as one fixed fp32 operation sequence: Cody-Waite reduction by ln 2 split
+// into a short high part and a low part, degree-7 Taylor polynomial of e^r on
+// |r| <= ln2/2 in Horner form, then scaling by 2^n in two exact-then-rounded
+// steps.  Each operation is rounded separately (no contraction).
+__device__ inline float sk_expf(float x) {
+    if (x >= 89.0f) return __builtin_inff();
+    if (x <= -104.0f) return 0.0f;
+    const float kLog2e = (float)1.4426950408889634;
+    const float kLn2Hi = 0.693359375f;
+    const float kLn2Lo = (float)(0.6931471805599453 - 0.693359375);
+    float n = __builtin_rintf(x * kLog2e);
+    float r = (x - n * kLn2Hi) - n * kLn2Lo;
+    float p = (float)(1.0 / 5040.0);
+    p = p * r + (float)(1.0 / 720.0);
+    p = p * r + (float)(1.0 / 120.0);
+    p = p * r + (float)(1.0 / 24.0);
+    p = p * r + (float)(1.0 / 6.0);
+    p = p * r + 0.5f;
+    p = p * r + 1.0f;
+    p = p * r + 1.0f;
+    int ni = (int)n;
+    int e1 = ni >> 1;          // floor(n / 2)
+    int e2 = ni - e1;
+    return (p * __int_as_float((e1 + 127) << 23)) * __int_as_float((e2 + 127) << 23);
+}
+
+__device__ inline float silu_mul(float g, float u) {
+    float den = 1.0f + sk_expf(-g);
+    float s = g / den;
+    return s * u;
+}
+
+__device__ inline float rms_apply(float x, float r, float g) {
+    float t = x * r;
+    return t * g;
+}
+
+// Activation codes q = clamp(rint(fp32(h / sx)), -127, 127), packed as int8
+// four to a dword.  For sx > 0, |h| <= 127 sx so the clamp never acts.  Adding 1.5 * 2^23 rounds a value of magnitude < 2^22 to
+// the nearest integer (ties to even) and leaves it in the low mantissa bits, so
+// the low byte of the sum's bit pattern is the int8 result.  t = h * inv with
+// inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here) of h/sx, and
+// fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t) equals
+// rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then (or
+// for a tiny sx) is the quotient formed by IEEE division.
+constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
+constexpr float kTieBand = 2e-5f;
+// bytes 0..3 <- low bytes of b0..b3
+__device__ inline uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+    return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
+}
+
+#pragma clang fp contract(on)
+
+// bf16 bits of f, rounded to nearest even (finite inputs)
+__device__ inline uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- cross-lane reductions (DPP within 16-lane rows, then the four rows) ----
+template <int CTRL>
+__device__ inline int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int DPP_HMIRROR = 0x141;  // lane i <-> 7 - i within 8 lanes
+constexpr int DPP_MIRROR = 0x140;   // lane i <-> 15 - i within 16 lanes
+
+// Max over the wave (wave-uniform result).
+__device__ inline float wave_max(float v) {
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_HMIRROR>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_MIRROR>(__float_as_int(v))));
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+template <int CTRL>
+__device__ inline double dpp_d(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp<CTRL>((int)(b & 0xFFFFFFFFll));
+    const int hi = dpp<CTRL>((int)(b >> 32));
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ inline double readlane_d(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane((int)(b & 0xFFFFFFFFll), l);
+    const int hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+    return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+// Sum over the wave in one fixed tree order (wave-uniform result).
+__device__ inline double wave_sum(double v) {
+    v += dpp_d<DPP_XOR1>(v);
+    v += dpp_d<DPP_XOR2>(v);
+    v += dpp_d<DPP_HMIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
+// Thread -> activation mapping.  Each thread holds up to NCH 16-byte chunks of
+// its row's slice (a chunk is 4 fp32 or 8 bf16 elements): WPR waves per row,
+// row m = wave / WPR, chunk c = it + i * TPR for i < NCH.  `nw` counts the
+// iterations i in which the wave has at least one chunk, so a wave skips the
+// rest with a uniform branch.
+template <int XT, int EPT>
+struct Act {
+    static constexpr int E = XT == 0 ? 4 : 8;      // elements per chunk
+    static constexpr int NCH = EPT / E;            // chunks per thread (EPT elements)
+    static constexpr int ES = XT == 0 ? 4 : 2;     // bytes per element
+    int m;      // row of this wave; >= M: the wave holds no activations
+    int it;     // thread index within the row
+    int tpr;    // threads per row
+    int cpr;    // chunks per row of the slice
+    int nw;     // wave-uniform
+};
+
+template <int XT, int EPT>
+__device__ inline Act<XT, EPT> act_map(const KArgs& a, uint32_t wt, int lane) {
+    Act<XT, EPT> am;
+    am.m = (wt >> 10) & 15;
+    am.it = ((wt >> 14) & 31) * 64 + lane;
+    am.tpr = a.tpr;
+    am.cpr = a.cpr;
+    am.nw = (wt >> 19) & 15;
+    return am;
+}
+
+// Chunk index of a thread's i-th chunk.  The wave-uniform part goes through
+// readfirstlane so it stays a scalar added to the lane's index: folded into a
+// 64-bit multiply-add instead, the unused high half of its addend can land on
+// a register a load is still filling, and the wait for it would serialise the
+// activation loads.
+template <int XT, int EPT>
+__device__ inline int chunk_of(const Act<XT, EPT>& am, int i) {
+    return am.it + __builtin_amdgcn_readfirstlane(i * am.tpr);
+}
+
+// Raw 16-byte chunks of slice [k_lo, k_lo + KS) (SwiGLU: gate in xr, up in ur).
+template <int PRO, int XT, int EPT>
+__device__ inline void load_act(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
+                                uint4 xr[Act<XT, EPT>::NCH], uint4 ur[Act<XT, EPT>::NCH]) {
+    constexpr int CB = Act<XT, EPT>::E * Act<XT, EPT>::ES;     // 16 bytes per chunk
+    // the row's slice start (wave-uniform) and this thread's byte offsets in it
+    const int64_t row = ((int64_t)am.m * a.ld + k_lo) * Act<XT, EPT>::ES;
+    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + row;
+    const uint8_t* ub = static_cast<const uint8_t*>(a.x2) + row;
+#pragma unroll
+    for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
+        xr[i] = make_uint4(0u, 0u, 0u, 0u);
+        ur[i] = make_uint4(0u, 0u, 0u, 0u);
+        if (i < am.nw) {
+            const int c = chunk_of(am, i);
+            const int off = c < am.cpr ? c * CB : 0;
+            xr[i] = *reinterpret_cast<const uint4*>(xb + off);
+            if (PRO == PRO_SWIGLU) ur[i] = *reinterpret_cast<const uint4*>(ub + off);
+        }
+    }
+}
+
+template <int XT, int EPT>
+__device__ inline void load_gamma(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
+                                  float g[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
+    constexpr int E = Act<XT, EPT>::E;
+#pragma unroll
+    for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) g[i * E + e] = 0.0f;
+        if (i < am.nw) {
+            const int c = chunk_of(am, i);
+            const int cc = c < am.cpr ? c : 0;
+            const float4* gp = reinterpret_cast<const float4*>(a.gamma + k_lo + (int64_t)cc * E);
+#pragma unroll
+            for (int v = 0; v < E / 4; ++v) {
+                const float4 t = gp[v];
+                g[i * E + 4 * v] = t.x; g[i * E + 4 * v + 1] = t.y;
+                g[i * E + 4 * v + 2] = t.z; g[i * E + 4 * v + 3] = t.w;
+            }
+        }
+    }
+}
+
+// h values of the thread's chunks (SwiGLU applied); invalid elements are 0.
+template <int PRO, int XT, int EPT>
+__device__ inline void finish_act(const Act<XT, EPT>& am, const uint4 xr[Act<XT, EPT>::NCH],
+                                  const uint4 ur[Act<XT, EPT>::NCH], float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
+    constexpr int E = Act<XT, EPT>::E;
+#pragma unroll
+    for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
+        const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
+        const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+        const uint32_t uw[4] = {ur[i].x, ur[i].y, ur[i].z, ur[i].w};
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float xv, uv;
+            if (XT == 0) {
+                xv = __uint_as_float(xw[e]);
+                uv = __uint_as_float(uw[e]);
+            } else {
+                xv = __uint_as_float((e & 1) ? (xw[e >> 1] & 0xFFFF0000u) : (xw[e >> 1] << 16));
+                uv = __uint_as_float((e & 1) ? (uw[e >> 1] & 0xFFFF0000u) : (uw[e >> 1] << 16));
+            }
+            const float v = (PRO == PRO_SWIGLU) ? silu_mul(xv, uv) : xv;
+            h[i * E + e] = ok ? v : 0.0f;
+        }
+    }
+}
+
+template <int XT, int EPT>
+__device__ inline double sum_sq(const float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
+    double ss = 0.0;
+#pragma unroll
+    for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) ss += (double)h[j] * (double)h[j];
+    return ss;
+}
+template <int XT, int EPT>
+__device__ inline float abs_max(const float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) mx = fmaxf(mx, fabsf(h[j]));
+    return mx;
+}
+
+// A row's slice statistic from its waves' values, in wave order.
+__device__ inline double combine_d(const KArgs& a, const Smem& sm, int m) {
+    const int lo = m * a.WPR, hi = lo + a.WPR;
+    const double2* p = reinterpret_cast<const double2*>(sm.wd);
+    double v[NW];
+#pragma unroll
+    for (int q = 0; q < NW / 2; ++q) {
+        const double2 t = p[q];
+        v[2 * q] = t.x;
+        v[2 * q + 1] = t.y;
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s = (w >= lo && w < hi) ? s + v[w] : s;
+    return s;
+}
+__device__ inline float combine_f(const KArgs& a, const Smem& sm, int m) {
+    const int lo = m * a.WPR, hi = lo + a.WPR;
+    const float4* p = reinterpret_cast<const float4*>(sm.wf);
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NW / 4; ++q) {
+        const float4 t = p[q];
+        const float e[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (4 * q + k >= lo && 4 * q + k < hi) s = fmaxf(s, e[k]);
+    }
+    return s;
+}
+// Max over the waves of row m (m wave-uniform): lane k of each 16-lane row
+// takes wave k's value, and a max within the row leaves the result in every
+// lane.  Values are >= 0, so 0 stands in for waves of other rows.
+__device__ inline float row_max(const KArgs& a, const Smem& sm, int m, int lane) {
+    const int k = lane & 15;
+    const int lo = m * a.WPR;
+    const float w = sm.wf[k];
+    float v = (k >= lo && k < lo + a.WPR) ? w : 0.0f;
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_XOR2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_HMIRROR>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp<DPP_MIRROR>(__float_as_int(v))));
+    return v;
+}
+// Row m's statistic over all slices (S > 1), slices in ascending order.
+__device__ inline double slices_sum(const KArgs& a, const Smem& sm, int m) {
+    const double2* p = reinterpret_cast<const double2*>(sm.exd + m * SMAX);
+    double s = 0.0;
+    for (int q = 0; q < a.S; q += 2) {
+        const double2 t = p[q >> 1];
+        s += t.x;
+        if (q + 1 < a.S) s += t.y;
+    }
+    return s;
+}
+__device__ inline float slices_max(const KArgs& a, const Smem& sm, int m) {
+    const float4* p = reinterpret_cast<const float4*>(sm.exf + m * SMAX);
+    float s = 0.0f;
+    for (int q = 0; q < a.S; q += 4) {
+        const float4 t = p[q >> 2];
+        s = fmaxf(s, t.x);
+        if (q + 1 < a.S) s = fmaxf(s, t.y);
+        if (q + 2 < a.S) s = fmaxf(s, t.z);
+        if (q + 3 < a.S) s = fmaxf(s, t.w);
+    }
+    return s;
+}
+
+// Statistics of slice `sl`, computed locally when its exchange word did not
+// arrive in time.  Same thread mapping and summation order as the workgroups
+// that own that slice, so the result is bit-identical.  All threads call it.
+template <int PRO, int XT, int EPT>
+__device__ inline void slice_stat(const KArgs& a, Smem& sm, uint32_t wt, int lane, int wv, int sl,
+                                  bool want_ss) {
+    constexpr int E = Act<XT, EPT>::E;
+    const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
+    uint4 xr[Act<XT, EPT>::NCH], ur[Act<XT, EPT>::NCH];
+    float h[Act<XT, EPT>::NCH * E];
+    load_act<PRO, XT, EPT>(a, am, sl * a.KS, xr, ur);
+    finish_act<PRO, XT, EPT>(am, xr, ur, h);
+    if (want_ss) {
+        const double ss = wave_sum(sum_sq<XT, EPT>(h));
+        if (lane == 0) sm.wd[wv] = ss;
+    } else {
+        if (PRO == PRO_RMSNORM) {
+            float g[Act<XT, EPT>::NCH * E];
+            load_gamma<XT, EPT>(a, am, sl * a.KS, g);
+            const float r = (am.m < a.m) ? sm.rr[am.m] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < Act<XT, EPT>::NCH * E; ++j) h[j] = rms_apply(h[j], r, g[j]);
+        }
+        const float mx = wave_max(abs_max<XT, EPT>(h));
+        if (lane == 0) sm.wf[wv] = mx;
+    }
+    __syncthreads();
+    if (threadIdx.x < a.m) {
+        if (want_ss) sm.exd[threadIdx.x * SMAX + sl] = combine_d(a, sm, threadIdx.x);
+        else sm.exf[threadIdx.x * SMAX + sl] = combine_f(a, sm, threadIdx.x);
+    }
+    __syncthreads();
+}
+
+// Exchange this slice's per-row value with the other slices (S > 1), run by
+// the poller wave only, after the waves' values are in sm.wd / sm.wf.  Every
+// word carries the call's tag in its high half, so no fence is needed: a
+// reader simply waits until all words show the tag.  absmax: one word
+// (tag | float bits).  Sum of squares (double): two words (tag | high half),
+// (tag | low half).
+__device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, bool is_ss) {
+    const uint32_t tag = sm.tag;
+    if (lane < a.m) {
+        const int slot = s * 8 + lane;
+        if (is_ss) {
+            const double v = combine_d(a, sm, lane);
+            sm.exd[lane * SMAX + s] = v;
+            const u64 bits = (u64)__double_as_longlong(v);
+            __hip_atomic_store(&a.ws->ssh[slot], ((u64)tag << 32) | (bits >> 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ws->ssl[slot], ((u64)tag << 32) | (bits & 0xFFFFFFFFull),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            const float v = combine_f(a, sm, lane);
+            sm.exf[lane * SMAX + s] = v;
+            __hip_atomic_store(&a.ws->amax[slot], ((u64)tag << 32) | __float_as_uint(v),
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    if (lane < SMAX) sm.miss[lane] = 0;
+    for (int j = lane; j < a.S * a.m; j += 64) {
+        const int sl = j / a.m, mm = j % a.m;
+        const int slot = sl * 8 + mm;
+        if (sl == s) continue;
+        bool ok = false;
+        for (int it = 0; it < a.spin_limit; ++it) {
+            if (is_ss) {
+                const u64 hi = __hip_atomic_load(&a.ws->ssh[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const u64 lo = __hip_atomic_load(&a.ws->ssl[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(hi >> 32) == tag && (uint32_t)(lo >> 32) == tag) {
+                    sm.exd[mm * SMAX + sl] = __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) |
+                                                                    (lo & 0xFFFFFFFFull)));
+                    ok = true;
+                    break;
+                }
+            } else {
+                const u64 v = __hip_atomic_load(&a.ws->amax[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if ((uint32_t)(v >> 32) == tag) {
+                    sm.exf[mm * SMAX + sl] = __uint_as_float((uint32_t)v);
+                    ok = true;
+                    break;
+                }
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        if (!ok) sm.miss[sl] = 1;          // every writer stores the same value
+    }
+}
+
+// --------------------------------------------------------------------------
+// the kernel
+// --------------------------------------------------------------------------
+
+template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG>
+__global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    __shared__ Smem sm;
+    constexpr bool CB = FMT == FMT_CB;          // codebook levels instead of integer weights
+    constexpr int NG = (GS == 0) ? 8 : 4 / GS;  // groups per super-block (GS = 0: G = 16)
+    // The weight bytes fed to the dot products hold w scaled by 16 (W4: the
+    // nibble in the byte's top half) or 4 (W6: the 6 bits in the top of the
+    // byte), so sign extension is free; the sums are scaled back at the store.
+    constexpr int WSH = (FMT == FMT_W6) ? 2 : 4;
+    constexpr float KINV = CB ? 1.0f : (FMT == FMT_W6) ? 0.25f : 0.0625f;
+    // activations per thread: 32 only where the registers allow it
+    constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : 32;
+    constexpr int E = Act<XT, EPT>::E;
+    constexpr int NCH = Act<XT, EPT>::NCH;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int nl = lane & 15;
+    const int hl = lane >> 4;
+    const int M = a.m;
+    const int r = blockIdx.x;
+    const int s = blockIdx.y;
+    const int k_lo = s * a.KS;
+
+    // 1. the activations first: they head the longest dependency chain (x ->
+    //    statistics -> q -> every dot product), so their loads go out before
+    //    any other address arithmetic; then the call's tag and the weight stream
+    //    (a wave's loads complete in issue order)
+    const uint32_t wt = a.wtab[wv];
+    const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
+    uint4 xr[NCH], ur[NCH];
+    float gv[NCH * E];
+    load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
+    if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
+    const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
+    // wave wv works on tile group tg (every TW-th tile) and super-blocks
+    // [kw * spw, (kw + 1) * spw) of the slice
+    const int kb_lo = s * a.KBs;
+    const bool big = r < a.trem;
+    const int t_begin = r * a.tq + (big ? r : a.trem);
+    const int t_end = t_begin + a.tq + (big ? 1 : 0);
+    const int jn = big ? a.jn1 : a.jn0;         // tiles per group, padded
+    const int tg = wt & 31;
+    const int kw = (wt >> 5) & 31;
+    const int kbw = kb_lo + kw * a.spw;
+    // With S > 1 the last wave only runs the cross-slice exchange: it never has
+    // weight loads in flight, so its polls are not queued behind them.
+    const bool poller = (a.S > 1) && (wv == NW - 1);
+    const bool active = tg < a.TW && !poller;
+
+    // LDS: [q: M x ks int8][sums of q][wave partials, two halves]
+    // (codebook: [16 levels as bf16 hi|lo pairs][q as bf16: M x ks bytes][wave partials])
+    uint32_t* lut_l = reinterpret_cast<uint32_t*>(lds);
+    int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
+    float* red_l = reinterpret_cast<float*>(q_l + (size_t)M * a.ks);
+
+    // Slots: the wave's weight stream is a sequence of super-blocks, spw per tile
+    // step; tile step j is tile t_begin + tg + j * TW.  Slots [0, nvalid) hold
+    // work; every wave walks jall slots (the tile barriers); the rest of the
+    // load stream reads stand-in bytes at the start of the weight.
+    const int ntile = t_end - t_begin;
+    // tiles tg, tg + TW, ... below ntile: jn = ceil(ntile / TW) of them, one
+    // fewer for the groups past the last step's share
+    const int jw = active ? jn - (tg >= ntile - (jn - 1) * a.TW ? 1 : 0) : 0;
+    const int nvalid = jw * a.spw;
+    const int jall = jn * a.spw;
+
+    // Per-lane byte offsets inside a super-block: a full tile (16 rows) and the
+    // weight's ragged last tile (nr_last rows; its lanes nl >= nr_last read
+    // offset 0 and feed only their own, never stored, row).  Offsets of a full
+    // tile stay inside the weight's first super-block, so a stand-in slot can
+    // read them from base 0.
+    const int nr_rag = a.nr_last;
+    const bool lane_rag_ok = nl < nr_rag;
+    const int lw_full = lane * 16, lw_rag = lane_rag_ok ? (hl * nr_rag + nl) * 16 : 0;
+    const int lh_full = 16 * 64 + lane * 8, lh_rag = lane_rag_ok ? nr_rag * 64 + (hl * nr_rag + nl) * 8 : 0;
+    const int ls_full = nl * NG * 4, ls_rag = lane_rag_ok ? nl * NG * 4 : 0;
+
+    // Load-side cursor: the next slot's index, super-block within the tile
+    // step, tile step, byte offsets of its weights and scales, their per-slot
+    // strides and the lane offsets of its tile kind.
+    int li = 0, lu = 0, lj = 0;
+    int64_t lwo = 0, lso = 0;
+    int lwst = 0, lsst = 0;
+    bool lrag = false;
+    auto tile_setup = [&]() {          // for tile step lj, super-block 0
+        const int t = t_begin + tg + lj * a.TW;
+        lrag = t == a.t_rag;
+        const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kbw * a.sbf;
+        lwo = lrag ? a.rag_w + (int64_t)kbw * a.rag_sbw : wo;
+        lso = lrag ? a.rag_s + (int64_t)kbw * a.rag_sbs : wo + a.swo;
+        lwst = lrag ? a.rag_sbw : a.sbf;
+        lsst = lrag ? a.rag_sbs : a.sbf;
+    };
+    tile_setup();
+    // The next slot into registers, then advance.  Every wave issues the same
+    // load instructions, so the compiler's wait counts are exact.
+    auto load_next = [&](uint4& w4, uint2& h2, float4& sv, float4& sv2) {
+        const bool valid = li < nvalid;
+        const uint8_t* wb = a.data + (valid ? lwo : 0);
+        const uint8_t* sb = a.data + (valid ? lso : 0);
+        const int lw = lrag ? lw_rag : lw_full;
+        const int ls = lrag ? ls_rag : ls_full;
+        w4 = *reinterpret_cast<const uint4*>(wb + lw);
+        if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (lrag ? lh_rag : lh_full));
+        if (NG == 8) {
+            sv = *reinterpret_cast<const float4*>(sb + ls);
+            sv2 = *reinterpret_cast<const float4*>(sb + ls + 16);
+        } else if (NG == 4) {
+            sv = *reinterpret_cast<const float4*>(sb + ls);
+        } else if (NG == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(sb + ls);
+            sv = make_float4(v.x, v.y, 0.0f, 0.0f);
+        } else {
+            sv = make_float4(*reinterpret_cast<const float*>(sb + ls), 0.0f, 0.0f, 0.0f);
+        }
+        ++li;
+        lwo += lwst;
+        lso += lsst;
+        if (++lu == a.spw) {
+            lu = 0;
+            ++lj;
+            if (li < nvalid) tile_setup();
+        }
+    };
+
+    uint4 wbuf[PIPE];
+    uint2 hbuf[PIPE];
+    float4 sbuf[PIPE], sbuf2[PIPE];
+#pragma unroll
+    for (int d = 0; d < PRIME; ++d) load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+
+    // 2. activation prologue: per-row statistics of h, then q into LDS
+    if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
+    if (CB && tid < 16) {
+        // each level as a bf16 pair hi + lo (|level - hi - lo| <= 2^-17 |level|)
+        const float v = a.codebook[tid];
+        const uint32_t hi = bf16_rne(v);
+        const uint32_t lo = bf16_rne(v - __uint_as_float(hi << 16));
+        lut_l[tid] = hi | (lo << 16);
+    }
+    float h[NCH * E];
+    finish_act<PRO, XT, EPT>(am, xr, ur, h);
+    const int mrow = am.m < M ? am.m : 0;
+    const bool row_lead = lane == 0 && am.m < M && am.it == 0;   // one thread per row
+
+    if (PRO == PRO_RMSNORM) {
+        const double ss = wave_sum(sum_sq<XT, EPT>(h));
+        if (lane == 0) sm.wd[wv] = ss;
+        __syncthreads();
+        double tot;
+        if (a.S == 1) {
+            tot = combine_d(a, sm, mrow);
+        } else {
+            if (poller) exchange_poll(a, sm, lane, s, true);
+            __syncthreads();
+            for (int sl = 0; sl < a.S; ++sl)
+                if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, true);
+            tot = slices_sum(a, sm, mrow);
+        }
+        const float ms = (float)(tot / (double)a.k);
+        const float d = ms + a.eps;
+        const float sd = (float)__builtin_sqrt((double)d);   // correctly rounded fp32 sqrt
+        const float rr = (float)(1.0 / (double)sd);          // correctly rounded fp32 1/x
+        if (row_lead) sm.rr[am.m] = rr;
+#pragma unroll
+        for (int j = 0; j < NCH * E; ++j) h[j] = rms_apply(h[j], rr, gv[j]);
+    }
+    float amx;
+    {
+        const float mx = wave_max(abs_max<XT, EPT>(h));
+        if (lane == 0) sm.wf[wv] = mx;
+        __syncthreads();
+        if (a.S == 1) {
+            amx = row_max(a, sm, mrow, lane);
+        } else {
+            if (poller) exchange_poll(a, sm, lane, s, false);
+            __syncthreads();
+            for (int sl = 0; sl < a.S; ++sl)
+                if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, false);
+            amx = slices_max(a, sm, mrow);
+        }
+    }
+    const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
+    const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+    if (row_lead) {
+        sm.sx[am.m] = sx;
+        if (DBG && a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
+    }
+
+    // quantise this slice into LDS (straight-line code: it runs once per
+    // launch, so every instruction of it is a cold instruction-cache fetch)
+    if (am.nw > 0) {
+        // codes of all elements first; the exact division, rarely needed, is one
+        // out-of-line block for the whole thread
+        uint32_t b[NCH * E];
+        float dev = 1.0f;           // min over elements of |fract(t) - 0.5|
+#pragma unroll
+        for (int j = 0; j < NCH * E; ++j) {
+            const float t = h[j] * inv;
+            b[j] = __float_as_uint(t + kRoundMagic);
+            dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
+        }
+        // 2^-125: 1/sx may not be normal
+        if (__builtin_expect((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f, 0)) {
+#pragma unroll
+            for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+        }
+        uint32_t pk[NCH * E / 4];
+#pragma unroll
+        for (int w = 0; w < NCH * E / 4; ++w) pk[w] = pack_low_bytes(b[4 * w], b[4 * w + 1], b[4 * w + 2], b[4 * w + 3]);
+        // LDS order: in each 128-k super-block, octet 4j + h is stored at position
+        // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
+        // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
+        // is chunk 0's plus i whole super-blocks.
+        const int c0 = am.it;
+        const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
+        const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
+        const int pstep = am.tpr * E;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+            const uint32_t* pc = pk + i * (E / 4);
+            const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
+            const int pos = pos0 + i * pstep;
+            if (CB) {
+                // bf16 copies of q (exact: |q| <= 127), two per dword
+                uint32_t hb[E / 2];
+#pragma unroll
+                for (int e2 = 0; e2 < E / 2; ++e2) {
+                    const int q0 = (int)(int8_t)(pc[(2 * e2) / 4] >> (8 * ((2 * e2) % 4)));
+                    const int q1 = (int)(int8_t)(pc[(2 * e2 + 1) / 4] >> (8 * ((2 * e2 + 1) % 4)));
+                    hb[e2] = (__float_as_uint((float)q0) >> 16) | (__float_as_uint((float)q1) & 0xFFFF0000u);
+                }
+                uint8_t* dst = reinterpret_cast<uint8_t*>(q_l) + am.m * a.ks + pos * 2;
+                if (ok) {
+                    if (E == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0], hb[1]);
+                    else *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[E / 2 - 1]);
+                }
+            } else {
+                int8_t* dst = q_l + am.m * a.ks + pos;
+                if (ok) {
+                    if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pc[0];
+                    else *reinterpret_cast<uint2*>(dst) = make_uint2(pc[0], pc[E / 4 - 1]);
+                }
+            }
+        }
+        if (DBG && a.q_out && r == 0) {          // debug export of q
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                const int c = chunk_of(am, i);
+                if (i < am.nw && c < am.cpr) {
+                    int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
+                    if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[i];
+                    else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[2 * i], pk[2 * i + 1]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int d = PRIME; d < PIPE; ++d) load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+
+    // 3. stream the weights: a register pipeline of PIPE slots in flight
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    const int ml = nl;   // A-operand row (activation row m) of this lane
+    const int iters = (jall + PIPE - 1) / PIPE * PIPE;
+    // Consume-side cursor: slot index, super-block within the tile step, tile
+    // step, and the slot's super-block within the slice.
+    int pi = 0, pu = 0, pj = 0, kbr = kw * a.spw;
+    // Sums of the tile steps that end inside a group of PIPE slots; their
+    // epilogues run after the group, from a single copy of the code (it runs
+    // once per tile step, so unrolled copies would only be more cold fetches).
+    float sav[PIPE][4];
+    uint32_t ended = 0;     // bit d: slot d of the group ended a tile step
+    int pje = 0;            // tile step of the next epilogue
+    // consume the next slot (group position d, weights w_in/h_in, scales s_in)
+    auto process = [&](const int d, const uint4 w_in, const uint2 h_in, const float4 s_in, const float4 s_in2) {
+        // Every slot's registers count as read here, valid or not, so the
+        // compiler waits for exactly this slot's loads (a skipped read would
+        // leave them pending when the next load reuses the registers).
+        if (FMT == FMT_W6) __asm__ volatile("" ::"v"(w_in.x), "v"(h_in.x), "v"(s_in.x));
+        else __asm__ volatile("" ::"v"(w_in.x), "v"(s_in.x));
+        if (pi < nvalid) {
+            const int t = t_begin + tg + pj * a.TW;
+            const int kb = kb_lo + kbr;
+            // Lanes of rows past the weight's end (ragged last tile) hold
+            // stand-in bytes; they only ever feed their own row's sums, which are
+            // never stored.
+            const bool row_ok = t != a.t_rag || lane_rag_ok;
+            const uint32_t wd[4] = {w_in.x, w_in.y, w_in.z, w_in.w};
+            const float sv[4] = {s_in.x, s_in.y, s_in.z, s_in.w};
+            // lo[j] / hi[j]: the bytes of codes e = 0..3 / 4..7 of octet hl of block j,
+            // each as a signed byte equal to w << WSH
+            uint32_t lo[4], hi[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (FMT == FMT_W6) {
+                    const uint32_t hd = (j < 2) ? h_in.x : h_in.y;
+                    const uint32_t hlo = (j & 1) ? (hd << 2) : (hd << 6);   // bits 4-5 of code c
+                    const uint32_t hhi = (j & 1) ? hd : (hd << 4);          // bits 4-5 of code c + 4
+                    lo[j] = ((wd[j] << 2) & 0x3C3C3C3Cu) | (hlo & 0xC0C0C0C0u);
+                    hi[j] = ((wd[j] >> 2) & 0x3C3C3C3Cu) | (hhi & 0xC0C0C0C0u);
+                } else {
+                    lo[j] = (wd[j] << 4) & 0xF0F0F0F0u;
+                    hi[j] = wd[j] & 0xF0F0F0F0u;
+                }
+            }
+            const int kbase = kbr * 128;          // slice-relative k of this super-block
+            // q of this lane: octet hl of each 32-k block j, stored contiguously
+            const uint4* qp = reinterpret_cast<const uint4*>(q_l + (DOT4 ? 0 : ml * a.ks) + kbase + hl * 32);
+            if (CB) {
+                // Codebook: each level is hi + lo in bf16, so the per-group sum of
+                // level * q is two bf16 MFMAs with fp32 accumulation (products exact).
+                // A = q as bf16 (row ml, octet hl of block j); B = the levels of this
+                // lane's 8 codes, built from the 16-entry table in LDS.
+                const uint4* qbp = reinterpret_cast<const uint4*>(
+                    reinterpret_cast<const uint8_t*>(q_l) + ml * a.ks + (kbase + hl * 32) * 2);
+                const float sv8[8] = {s_in.x, s_in.y, s_in.z, s_in.w, s_in2.x, s_in2.y, s_in2.z, s_in2.w};
+                v4f cg = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint4 qa = (ml < M) ? qbp[j] : make_uint4(0u, 0u, 0u, 0u);
+                    uint32_t ent[8];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        ent[c] = lut_l[(wd[j] >> (8 * c)) & 15u];          // element c
+                        ent[c + 4] = lut_l[(wd[j] >> (8 * c + 4)) & 15u];  // element c + 4
+                    }
+                    uint4 bh, bl;                 // elements (0,1) (2,3) (4,5) (6,7)
+                    bh.x = __builtin_amdgcn_perm(ent[1], ent[0], 0x05040100u);
+                    bh.y = __builtin_amdgcn_perm(ent[3], ent[2], 0x05040100u);
+                    bh.z = __builtin_amdgcn_perm(ent[5], ent[4], 0x05040100u);
+                    bh.w = __builtin_amdgcn_perm(ent[7], ent[6], 0x05040100u);
+                    bl.x = __builtin_amdgcn_perm(ent[1], ent[0], 0x07060302u);
+                    bl.y = __builtin_amdgcn_perm(ent[3], ent[2], 0x07060302u);
+                    bl.z = __builtin_amdgcn_perm(ent[5], ent[4], 0x07060302u);
+                    bl.w = __builtin_amdgcn_perm(ent[7], ent[6], 0x07060302u);
+                    const bf16x8 B_hi = __builtin_bit_cast(bf16x8, bh);
+                    const bf16x8 B_lo = __builtin_bit_cast(bf16x8, bl);
+                    if (NG == 8) {
+                        // G = 16: octets 0-1 of the block are group 2j, octets 2-3 group 2j+1
+                        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+                        const bf16x8 A_e = __builtin_bit_cast(bf16x8, hl < 2 ? qa : z);
+                        const bf16x8 A_o = __builtin_bit_cast(bf16x8, hl < 2 ? z : qa);
+                        v4f ce = {0.0f, 0.0f, 0.0f, 0.0f}, co = ce;
+                        ce = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_e, B_hi, ce, 0, 0, 0);
+                        ce = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_e, B_lo, ce, 0, 0, 0);
+                        co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_o, B_hi, co, 0, 0, 0);
+                        co = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A_o, B_lo, co, 0, 0, 0);
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            acc[rr] = __builtin_fmaf(sv8[2 * j], ce[rr], acc[rr]);
+                            acc[rr] = __builtin_fmaf(sv8[2 * j + 1], co[rr], acc[rr]);
+                        }
+                    } else {
+                        const bf16x8 A = __builtin_bit_cast(bf16x8, qa);
+                        cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B_hi, cg, 0, 0, 0);
+                        cg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B_lo, cg, 0, 0, 0);
+                        if ((j + 1) % (GS ? GS : 1) == 0) {
+#pragma unroll
+                            for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(sv[j / (GS ? GS : 1)], cg[rr], acc[rr]);
+                            cg = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+                        }
+                    }
+                }
+            } else if (DOT4) {
+                const uint4 q01 = qp[0], q23 = qp[1];
+                const uint32_t qw[8] = {q01.x, q01.y, q01.z, q01.w, q23.x, q23.y, q23.z, q23.w};
+                int part[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = __builtin_amdgcn_sdot4((int)hi[j], (int)qw[2 * j + 1], 0, false);
+                    part[j] = __builtin_amdgcn_sdot4((int)lo[j], (int)qw[2 * j], c, false);
+                }
+                int pg[NG];
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    pg[gi] = 0;
+#pragma unroll
+                    for (int jj = 0; jj < GS; ++jj) pg[gi] += part[gi * GS + jj];
+                    acc[0] = __builtin_fmaf(sv[gi], (float)pg[gi], acc[0]);
+                }
+                if (DBG && a.p_out) {        // debug export: this lane's share of each group partial
+                    if (row_ok) {
+#pragma unroll
+                        for (int gi = 0; gi < NG; ++gi)
+                            atomicAdd(&a.p_out[((int64_t)t * TILE_ROWS + nl) * a.kg + kb * NG + gi],
+                                      pg[gi] >> WSH);
+                    }
+                }
+            } else {
+                uint4 q01 = make_uint4(0u, 0u, 0u, 0u), q23 = q01;
+                if (ml < M) {
+                    q01 = qp[0];
+                    q23 = qp[1];
+                }
+                const long av[4] = {(long)((uint64_t)q01.x | ((uint64_t)q01.y << 32)),
+                                    (long)((uint64_t)q01.z | ((uint64_t)q01.w << 32)),
+                                    (long)((uint64_t)q23.x | ((uint64_t)q23.y << 32)),
+                                    (long)((uint64_t)q23.z | ((uint64_t)q23.w << 32))};
+                long bv[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) bv[j] = (long)((uint64_t)lo[j] | ((uint64_t)hi[j] << 32));
+#pragma unroll
+                for (int gi = 0; gi < NG; ++gi) {
+                    v4i c = {0, 0, 0, 0};
+#pragma unroll
+                    for (int jj = 0; jj < GS; ++jj)
+                        c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[gi * GS + jj],
+                                                                 bv[gi * GS + jj], c, 0, 0, 0);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(sv[gi], (float)c[rr], acc[rr]);
+                    if (DBG && a.p_out) {    // debug export of the group partials
+#pragma unroll
+                        for (int rr = 0; rr < 4; ++rr) {
+                            const int mm = 4 * hl + rr;
+                            if (mm < M && row_ok)
+                                a.p_out[((int64_t)mm * a.n + (int64_t)t * TILE_ROWS + nl) * a.kg +
+                                        kb * NG + gi] = c[rr] >> WSH;
+                        }
+                    }
+                }
+            }
+        }
+        if (pu == a.spw - 1 && pi < jall) {
+            // last super-block of its tile step: park the sums for the epilogue
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                sav[d][rr] = acc[rr];
+                acc[rr] = 0.0f;
+            }
+            ended |= 1u << d;
+        }
+        ++pi;
+        ++kbr;
+        if (++pu == a.spw) {
+            pu = 0;
+            ++pj;
+            kbr -= a.spw;
+        }
+    };
+
+    // 4. tile epilogue of tile step j with this lane's sums v4: fixed-order sum
+    //    of the waves' partials.  The partials buffer alternates between two
+    //    halves, so one barrier per tile is enough (a wave cannot reuse a half
+    //    before every thread passed the next barrier).
+    auto tile_epilogue = [&](const float* v4, const int j) {
+        float* red = red_l + (j & 1) * (NW * 128);
+        if (DOT4) {
+            // the four k-quarters of a row sit 16 lanes apart
+            float v = v4[0];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (lane < 16) red[wv * 16 + nl] = v;
+        } else {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int mm = 4 * hl + rr;
+                if (mm < M) red[(wv * 8 + mm) * 16 + nl] = v4[rr];
+            }
+        }
+        __syncthreads();
+        const int nout = a.TW * M * 16;
+        if (tid < nout) {
+            const int ogrp = tid / (M * 16);
+            const int omm = (tid / 16) % M;
+            const int onn = tid & 15;
+            const int ot = t_begin + ogrp + j * a.TW;
+            if (ot < t_end) {
+                float osum = 0.0f;
+                const int w0 = ogrp * a.KW;
+                if (DOT4) {
+                    for (int w = w0; w < w0 + a.KW; ++w) osum += red[w * 16 + onn];
+                } else {
+                    for (int w = w0; w < w0 + a.KW; ++w) osum += red[(w * 8 + omm) * 16 + onn];
+                }
+                if (a.S == 1) {
+                    if (ot * TILE_ROWS + onn < a.n)
+                        a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (osum * KINV);
+                } else {
+                    const u64 v = ((u64)sm.tag << 32) | __float_as_uint(osum);
+                    __hip_atomic_store(&a.part[(((int64_t)ot * a.S + s) * M + omm) * 16 + onn], v,
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    };
+
+    for (int base = 0; base < iters; base += PIPE) {
+#pragma unroll
+        for (int d = 0; d < PIPE; ++d) {
+            process(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+            load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+        }
+        // epilogues of the tile steps that ended in this group, in order
+#pragma clang loop unroll(disable)
+        while (ended) {
+            const int d = __builtin_ctz(ended);
+            ended &= ended - 1;
+            float v[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                v[rr] = sav[0][rr];
+#pragma unroll
+                for (int dd = 1; dd < PIPE; ++dd) v[rr] = (d == dd) ? sav[dd][rr] : v[rr];
+            }
+            tile_epilogue(v, pje);
+            ++pje;
+        }
+    }
+
+    // 5. merge the slices' partials: the last workgroup of each tile adds them
+    if (a.S > 1) {
+        __syncthreads();
+        for (int c0 = 0; c0 < ntile; c0 += kMaxTilesPerGroup) {
+            const int nc = min(kMaxTilesPerGroup, ntile - c0);
+            if (tid < nc) {
+                const int tt = t_begin + c0 + tid;
+                const uint32_t old =
+                    __hip_atomic_fetch_add(&a.cnt[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const int lst = (old == (uint32_t)(a.S - 1));
+                if (lst) __hip_atomic_store(&a.cnt[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.last[tid] = lst;
+            }
+            __syncthreads();
+            for (int e = tid; e < nc * M * 16; e += NT) {
+                const int ci = e / (M * 16);
+                if (!sm.last[ci]) continue;
+                const int omm = (e / 16) % M;
+                const int onn = e & 15;
+                const int ot = t_begin + c0 + ci;
+                float tot = 0.0f;
+                for (int sl = 0; sl < a.S; ++sl) {
+                    // Every partial was stored before its workgroup counted the tile, so its
+                    // tag shows up shortly; the bound only guards against a hang (a missing
+                    // partial would turn y into NaN rather than stall the GPU).
+                    const u64* p = &a.part[(((int64_t)ot * a.S + sl) * M + omm) * 16 + onn];
+                    u64 v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int it = 0; (uint32_t)(v >> 32) != sm.tag && it < (1 << 24); ++it)
+                        v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    tot += ((uint32_t)(v >> 32) == sm.tag) ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
+                }
+                if (ot * TILE_ROWS + onn < a.n)
+                    a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (tot * KINV);
+            }
+            __syncthreads();
+        }
+        // generation bookkeeping for the exchange words and tags
+        if (tid == 0) {
+            const uint32_t old =
+                __hip_atomic_fetch_add(&a.ws->done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == (uint32_t)(a.P - 1)) {
+                __hip_atomic_store(&a.ws->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.ws->gen, sm.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// Kernel pointer for a format, prologue, activation dtype, groups per 32-k block
+// (gs; 0 = the codebook's G = 16) and M = 1 / M >= 2; nullptr if not built.
+template <int FMT, int PRO, int XT, int GS, bool DBG>
+KernelFn pick_dot(bool dot4) {
+    if constexpr (FMT == FMT_CB) {
+        return gemm_kernel<FMT, PRO, XT, GS, false, DBG>;   // the codebook runs on MFMA for every M
+    } else {
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG> : gemm_kernel<FMT, PRO, XT, GS, false, DBG>;
+    }
+}
+template <int FMT, int PRO, int XT, bool DBG>
+KernelFn pick_gs(int gs, bool dot4) {
+    switch (gs) {
+        case 0:
+            if constexpr (FMT == FMT_CB) return pick_dot<FMT, PRO, XT, 0, DBG>(dot4);
+            return nullptr;
+        case 1: return pick_dot<FMT, PRO, XT, 1, DBG>(dot4);
+        case 2: return pick_dot<FMT, PRO, XT, 2, DBG>(dot4);
+        default: return pick_dot<FMT, PRO, XT, 4, DBG>(dot4);
+    }
+}
+template <int FMT, int PRO, bool DBG>
+KernelFn pick_xt(int xt, int gs, bool dot4) {
+    return xt == 1 ? pick_gs<FMT, PRO, 1, DBG>(gs, dot4) : pick_gs<FMT, PRO, 0, DBG>(gs, dot4);
+}
+template <int FMT, bool DBG>
+KernelFn pick_format(int pro, int xt, int gs, bool dot4) {
+    switch (pro) {
+        case PRO_RMSNORM: return pick_xt<FMT, PRO_RMSNORM, DBG>(xt, gs, dot4);
+        case PRO_SWIGLU: return pick_xt<FMT, PRO_SWIGLU, DBG>(xt, gs, dot4);
+        default: return pick_xt<FMT, PRO_NONE, DBG>(xt, gs, dot4);
+    }
+}
+
+}  // namespace
+
+}  // namespace sk
+
+#endif  // SK_GEMM_KERNEL_H

@@ -1,0 +1,10 @@
+// sk_gemm_w4.hip -- GEMM kernels for 4-bit weights, production instances (no debug exports).
+#include "sk_gemm_kernel.h"
+
+namespace sk {
+
+KernelFn pick_kernel_w4(int pro, int xt, int gs, bool dot4) {
+    return pick_format<FMT_W4, false>(pro, xt, gs, dot4);
+}
+
+}  // namespace sk

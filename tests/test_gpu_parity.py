@@ -125,17 +125,20 @@ def test_gemm_matches_oracle(fmt, n, k, g, ms, xt):
         check_call(w, buf, fmt, n, k, g, h_dev, h_ref, m)
 
 
-def test_public_entry_points_equal_debug_run():
-    for fmt, g in ((0, 32), (2, 64)):
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_public_entry_points_equal_debug_run(xt):
+    """The public entry points run kernel instances built without the debug
+    exports; their y must equal the test hook's bit for bit."""
+    for fmt, g in ((0, 32), (2, 64), (1, 16), (0, 128)):
         n, k = 640, 2048
         w, buf = gpu_weight(fmt, n, k, g, 11)
         sk.sk_repack_w4a8(w)
-        for m in (1, 8):
-            x = torch.from_numpy(S.activations(12, m, k)).cuda()
+        for m in (1, 3, 8):
+            x, _ = to_dev(S.activations(12 + m, m, k), xt)
             y_dbg = sk.sk_debug_gemm(w, sk.PRO_NONE, x, want_partials=False)[0]
-            y = (sk.sk_gemm_w4a8 if fmt == 0 else sk.sk_gemm_w6a8)(w, x)
+            y = (sk.sk_gemm_w6a8 if fmt == 2 else sk.sk_gemm_w4a8)(w, x)
             torch.cuda.synchronize()
-            assert torch.equal(y, y_dbg)
+            assert torch.equal(y, y_dbg), (fmt, g, m, xt)
 
 
 def test_zero_and_constant_rows():
