@@ -575,16 +575,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
     float* red_l = reinterpret_cast<float*>(q_l + (size_t)M * a.ks);
 
-    // Slots: the wave's weight stream is a sequence of super-blocks, spw per tile
-    // step; tile step j is tile t_begin + tg + j * TW.  Slots [0, nvalid) hold
-    // work; every wave walks jall slots (the tile barriers); the rest of the
-    // load stream reads stand-in bytes at the start of the weight.
+    // Slots: the wave's weight stream is a sequence of super-blocks, spw per
+    // tile step, walked in groups of PIPE slots (a tile step's last group is
+    // padded when PIPE does not divide spw); tile step j is tile
+    // t_begin + tg + j * TW.  Tile steps [0, jw) hold work; every wave walks jn
+    // of them (the tile barriers).  Padding slots and the steps past jw load
+    // in-bounds stand-in bytes and skip the arithmetic.
     const int ntile = t_end - t_begin;
     // tiles tg, tg + TW, ... below ntile: jn = ceil(ntile / TW) of them, one
     // fewer for the groups past the last step's share
     const int jw = active ? jn - (tg >= ntile - (jn - 1) * a.TW ? 1 : 0) : 0;
-    const int nvalid = jw * a.spw;
-    const int jall = jn * a.spw;
+    const int ngrp = (a.spw + PIPE - 1) / PIPE;      // slot groups per tile step
 
     // Per-lane byte offsets inside a super-block: a full tile (16 rows) and the
     // weight's ragged last tile (nr_last rows; its lanes nl >= nr_last read
@@ -597,33 +598,46 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int lh_full = 16 * 64 + lane * 8, lh_rag = lane_rag_ok ? nr_rag * 64 + (hl * nr_rag + nl) * 8 : 0;
     const int ls_full = nl * NG * 4, ls_rag = lane_rag_ok ? nl * NG * 4 : 0;
 
-    // Load-side cursor: the next slot's index, super-block within the tile
-    // step, tile step, byte offsets of its weights and scales, their per-slot
-    // strides and the lane offsets of its tile kind.
-    int li = 0, lu = 0, lj = 0;
-    int64_t lwo = 0, lso = 0;
-    int lwst = 0, lsst = 0;
-    bool lrag = false;
-    auto tile_setup = [&]() {          // for tile step lj, super-block 0
+    // Load-side cursor: group lg of tile step lj.  Its slots' weights and
+    // scales start at byte offsets gw / gs and step by gws / gss; grg marks the
+    // ragged tile; gnv counts the slots that hold work.  A stand-in group has
+    // zero offsets and strides.  All of it is wave-uniform and set once per
+    // group, so a slot's load is a few scalar operations.
+    int lj = 0, lg = 0;
+    int64_t gw = 0, gs = 0;
+    int gws = 0, gss = 0, gnv = 0;
+    bool grg = false;
+    auto group_setup = [&]() {
         const int t = t_begin + tg + lj * a.TW;
-        lrag = t == a.t_rag;
-        const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kbw * a.sbf;
-        lwo = lrag ? a.rag_w + (int64_t)kbw * a.rag_sbw : wo;
-        lso = lrag ? a.rag_s + (int64_t)kbw * a.rag_sbs : wo + a.swo;
-        lwst = lrag ? a.rag_sbw : a.sbf;
-        lsst = lrag ? a.rag_sbs : a.sbf;
+        const bool valid = lj < jw;
+        const int kb = kbw + lg * PIPE;
+        grg = valid && t == a.t_rag;
+        const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kb * a.sbf;
+        gw = !valid ? 0 : grg ? a.rag_w + (int64_t)kb * a.rag_sbw : wo;
+        gs = !valid ? 0 : grg ? a.rag_s + (int64_t)kb * a.rag_sbs : wo + a.swo;
+        gws = !valid ? 0 : grg ? a.rag_sbw : a.sbf;
+        gss = !valid ? 0 : grg ? a.rag_sbs : a.sbf;
+        gnv = valid ? min(PIPE, a.spw - lg * PIPE) : 0;
     };
-    tile_setup();
-    // The next slot into registers, then advance.  Every wave issues the same
-    // load instructions, so the compiler's wait counts are exact.
-    auto load_next = [&](uint4& w4, uint2& h2, float4& sv, float4& sv2) {
-        const bool valid = li < nvalid;
-        const uint8_t* wb = a.data + (valid ? lwo : 0);
-        const uint8_t* sb = a.data + (valid ? lso : 0);
-        const int lw = lrag ? lw_rag : lw_full;
-        const int ls = lrag ? ls_rag : ls_full;
+    auto group_next = [&]() {
+        if (++lg == ngrp) {
+            lg = 0;
+            ++lj;
+        }
+        group_setup();
+    };
+    group_setup();
+    // Slot d of the load group into registers (padding slots re-read slot 0).
+    // Every wave issues the same load instructions, so the compiler's wait
+    // counts are exact.
+    auto load_slot = [&](const int d, uint4& w4, uint2& h2, float4& sv, float4& sv2) {
+        const int dd = d < gnv ? d : 0;
+        const uint8_t* wb = a.data + gw + dd * gws;
+        const uint8_t* sb = a.data + gs + dd * gss;
+        const int lw = grg ? lw_rag : lw_full;
+        const int ls = grg ? ls_rag : ls_full;
         w4 = *reinterpret_cast<const uint4*>(wb + lw);
-        if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (lrag ? lh_rag : lh_full));
+        if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (grg ? lh_rag : lh_full));
         if (NG == 8) {
             sv = *reinterpret_cast<const float4*>(sb + ls);
             sv2 = *reinterpret_cast<const float4*>(sb + ls + 16);
@@ -635,21 +649,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         } else {
             sv = make_float4(*reinterpret_cast<const float*>(sb + ls), 0.0f, 0.0f, 0.0f);
         }
-        ++li;
-        lwo += lwst;
-        lso += lsst;
-        if (++lu == a.spw) {
-            lu = 0;
-            ++lj;
-            if (li < nvalid) tile_setup();
-        }
     };
 
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
     float4 sbuf[PIPE], sbuf2[PIPE];
 #pragma unroll
-    for (int d = 0; d < PRIME; ++d) load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+    for (int d = 0; d < PRIME; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
 
     // 2. activation prologue: per-row statistics of h, then q into LDS
     if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
@@ -780,30 +786,22 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __syncthreads();
 
 #pragma unroll
-    for (int d = PRIME; d < PIPE; ++d) load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+    for (int d = PRIME; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+    group_next();
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     const int ml = nl;   // A-operand row (activation row m) of this lane
-    const int iters = (jall + PIPE - 1) / PIPE * PIPE;
-    // Consume-side cursor: slot index, super-block within the tile step, tile
-    // step, and the slot's super-block within the slice.
-    int pi = 0, pu = 0, pj = 0, kbr = kw * a.spw;
-    // Sums of the tile steps that end inside a group of PIPE slots; their
-    // epilogues run after the group, from a single copy of the code (it runs
-    // once per tile step, so unrolled copies would only be more cold fetches).
-    float sav[PIPE][4];
-    uint32_t ended = 0;     // bit d: slot d of the group ended a tile step
-    int pje = 0;            // tile step of the next epilogue
-    // consume the next slot (group position d, weights w_in/h_in, scales s_in)
-    auto process = [&](const int d, const uint4 w_in, const uint2 h_in, const float4 s_in, const float4 s_in2) {
+    // consume slot (weights w_in/h_in, scales s_in) of tile t whose super-block
+    // is kbr within the slice; `work` is false for padding and stand-in slots
+    auto process = [&](const bool work, const int t, const int kbr, const uint4 w_in, const uint2 h_in,
+                       const float4 s_in, const float4 s_in2) {
         // Every slot's registers count as read here, valid or not, so the
         // compiler waits for exactly this slot's loads (a skipped read would
         // leave them pending when the next load reuses the registers).
         if (FMT == FMT_W6) __asm__ volatile("" ::"v"(w_in.x), "v"(h_in.x), "v"(s_in.x));
         else __asm__ volatile("" ::"v"(w_in.x), "v"(s_in.x));
-        if (pi < nvalid) {
-            const int t = t_begin + tg + pj * a.TW;
+        if (work) {
             const int kb = kb_lo + kbr;
             // Lanes of rows past the weight's end (ragged last tile) hold
             // stand-in bytes; they only ever feed their own row's sums, which are
@@ -944,22 +942,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 }
             }
         }
-        if (pu == a.spw - 1 && pi < jall) {
-            // last super-block of its tile step: park the sums for the epilogue
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                sav[d][rr] = acc[rr];
-                acc[rr] = 0.0f;
-            }
-            ended |= 1u << d;
-        }
-        ++pi;
-        ++kbr;
-        if (++pu == a.spw) {
-            pu = 0;
-            ++pj;
-            kbr -= a.spw;
-        }
     };
 
     // 4. tile epilogue of tile step j with this lane's sums v4: fixed-order sum
@@ -1008,27 +990,22 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
     };
 
-    for (int base = 0; base < iters; base += PIPE) {
+    for (int pj = 0; pj < jn; ++pj) {
+        const bool pvalid = pj < jw;
+        const int t = t_begin + tg + pj * a.TW;
+        for (int pg = 0; pg < ngrp; ++pg) {
+            const int pnv = pvalid ? min(PIPE, a.spw - pg * PIPE) : 0;
+            const int kb0 = kw * a.spw + pg * PIPE;
 #pragma unroll
-        for (int d = 0; d < PIPE; ++d) {
-            process(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
-            load_next(wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
-        }
-        // epilogues of the tile steps that ended in this group, in order
-#pragma clang loop unroll(disable)
-        while (ended) {
-            const int d = __builtin_ctz(ended);
-            ended &= ended - 1;
-            float v[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                v[rr] = sav[0][rr];
-#pragma unroll
-                for (int dd = 1; dd < PIPE; ++dd) v[rr] = (d == dd) ? sav[dd][rr] : v[rr];
+            for (int d = 0; d < PIPE; ++d) {
+                process(d < pnv, t, kb0 + d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+                load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
             }
-            tile_epilogue(v, pje);
-            ++pje;
+            group_next();
         }
+        tile_epilogue(acc, pj);
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
     }
 
     // 5. merge the slices' partials: the last workgroup of each tile adds them
