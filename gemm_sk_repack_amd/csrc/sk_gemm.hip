@@ -45,8 +45,9 @@ namespace {
 
 // Waves of a workgroup: TW tile groups x KW waves along k (KW divides the
 // slice's KBs super-blocks).  Each wave walks ceil(tiles / TW) tile steps of
-// KBs / KW super-blocks; the split with the fewest slots per wave wins, then
-// the one with the fewest tile steps (each ends with a workgroup barrier).
+// KBs / KW super-blocks, in groups of PIPE slots (a step's last group padded);
+// the split with the fewest slots per wave, padding included, wins, then the
+// one with the fewest tile steps (each ends with a workgroup barrier).
 // Returns the slots per wave.
 int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int& KW, int& TW) {
     KW = 1;
@@ -58,7 +59,8 @@ int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int& KW, int& TW)
         while (tw > 1 && tw * m * 16 > NT) --tw;      // the epilogue uses one thread per output
         if (tw > tiles_per_wg) tw = tiles_per_wg;
         const int64_t steps = (tiles_per_wg + tw - 1) / tw;
-        const int64_t slots = steps * (KBs / kw);
+        const int spw = KBs / kw;
+        const int64_t slots = steps * ((spw + PIPE - 1) / PIPE * PIPE);   // padded to whole groups
         if (best_slots < 0 || slots < best_slots || (slots == best_slots && steps < best_steps)) {
             best_slots = slots;
             best_steps = steps;
