@@ -791,7 +791,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int ml = nl;   // A-operand row (activation row m) of this lane
+    // A-operand row (activation row) of this lane.  Rows past M repeat row
+    // M - 1: their products land in output rows >= M, which are never stored,
+    // so the LDS reads need no mask.
+    const int ml = nl < M ? nl : M - 1;
     // consume slot (weights w_in/h_in, scales s_in) of tile t whose super-block
     // is kbr within the slice; `work` is false for padding and stand-in slots
     auto process = [&](const bool work, const int t, const int kbr, const uint4 w_in, const uint2 h_in,
@@ -839,7 +842,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 v4f cg = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const uint4 qa = (ml < M) ? qbp[j] : make_uint4(0u, 0u, 0u, 0u);
+                    const uint4 qa = qbp[j];
                     uint32_t ent[8];
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
@@ -909,11 +912,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     }
                 }
             } else {
-                uint4 q01 = make_uint4(0u, 0u, 0u, 0u), q23 = q01;
-                if (ml < M) {
-                    q01 = qp[0];
-                    q23 = qp[1];
-                }
+                const uint4 q01 = qp[0], q23 = qp[1];
                 const long av[4] = {(long)((uint64_t)q01.x | ((uint64_t)q01.y << 32)),
                                     (long)((uint64_t)q01.z | ((uint64_t)q01.w << 32)),
                                     (long)((uint64_t)q23.x | ((uint64_t)q23.y << 32)),
@@ -921,22 +920,28 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 long bv[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) bv[j] = (long)((uint64_t)lo[j] | ((uint64_t)hi[j] << 32));
+                // every group's MFMAs first (independent, so they issue back to
+                // back), then the scaling
+                v4i c[NG];
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                    v4i c = {0, 0, 0, 0};
+                    c[gi] = v4i{0, 0, 0, 0};
 #pragma unroll
                     for (int jj = 0; jj < GS; ++jj)
-                        c = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[gi * GS + jj],
-                                                                 bv[gi * GS + jj], c, 0, 0, 0);
+                        c[gi] = __builtin_amdgcn_mfma_i32_16x16x32_i8(av[gi * GS + jj],
+                                                                     bv[gi * GS + jj], c[gi], 0, 0, 0);
+                }
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(sv[gi], (float)c[rr], acc[rr]);
+                for (int gi = 0; gi < NG; ++gi) {
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) acc[rr] = __builtin_fmaf(sv[gi], (float)c[gi][rr], acc[rr]);
                     if (DBG && a.p_out) {    // debug export of the group partials
 #pragma unroll
                         for (int rr = 0; rr < 4; ++rr) {
                             const int mm = 4 * hl + rr;
                             if (mm < M && row_ok)
                                 a.p_out[((int64_t)mm * a.n + (int64_t)t * TILE_ROWS + nl) * a.kg +
-                                        kb * NG + gi] = c[rr] >> WSH;
+                                        kb * NG + gi] = c[gi][rr] >> WSH;
                         }
                     }
                 }
