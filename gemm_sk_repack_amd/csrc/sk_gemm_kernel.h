@@ -651,6 +651,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
     };
 
+    // M >= 2 (more activation loads, and with S > 1 every slice's statistics
+    // gate the exchange): the weight stream starts once the activations are in,
+    // so their loads do not queue behind a burst of cold weight requests.
+    if (!DOT4) {
+        __builtin_amdgcn_s_waitcnt(0xF70);    // vmcnt(0)
+        __syncthreads();
+    }
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
     float4 sbuf[PIPE], sbuf2[PIPE];
