@@ -30,7 +30,9 @@ BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
 
 # Every symbol include/sk_repack.h and include/sk_repack_test.h declare.
 EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4a8",
-           "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu", "sk_debug_gemm",
+           "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu",
+           "sk_quantize_rows", "sk_gemm_w4a8_canonical", "sk_gemm_w4a8_canonical_q",
+           "sk_debug_gemm",
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
            "sk_test_set_spin_limit"]
 
@@ -63,6 +65,9 @@ def _load() -> ctypes.CDLL:
         "sk_gemm_w6a8": ([W, P, I, I, P, P], I),
         "sk_gemm_fused_rmsnorm": ([W, P, I, P, F, I, P, P], I),
         "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P], I),
+        "sk_quantize_rows": ([P, I, I, I, P, P, P], I),
+        "sk_gemm_w4a8_canonical": ([W, P, I, I, P, P], I),
+        "sk_gemm_w4a8_canonical_q": ([W, P, P, I, P, P], I),
         "sk_debug_gemm": ([W, I, P, P, I64, I, P, F, I, P, P, P, P, P], I),
         "sk_test_repack_on_host": ([W, P, I], I),
         "sk_test_gemm_plan": ([I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_int64)], I),
@@ -164,6 +169,37 @@ def sk_gemm_w6a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.
     y = _out(w, m, y)
     _check(LIB.sk_gemm_w6a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
            "sk_gemm_w6a8")
+    return y
+
+
+def sk_quantize_rows(x: torch.Tensor, q=None, sx=None, stream=None):
+    """Per-row int8 quantisation as its own launch (the split path); returns (q, sx)."""
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    if sx is None:
+        sx = torch.empty((m,), dtype=torch.float32, device="cuda")
+    _check(LIB.sk_quantize_rows(_ptr(x), _xt(x), m, k, _ptr(q), _ptr(sx), _stream(stream)),
+           "sk_quantize_rows")
+    return q, sx
+
+
+def sk_gemm_w4a8_canonical(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+    """W4A8 GEMM on a weight left in the canonical layout (no repack)."""
+    m = x.shape[0]
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_w4a8_canonical(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y),
+                                      _stream(stream)), "sk_gemm_w4a8_canonical")
+    return y
+
+
+def sk_gemm_w4a8_canonical_q(w: QuantWeight, q: torch.Tensor, sx: torch.Tensor, y=None,
+                             stream=None) -> torch.Tensor:
+    """The same GEMM on activations already quantised by sk_quantize_rows."""
+    m = q.shape[0]
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_w4a8_canonical_q(ctypes.byref(w.desc), _ptr(q), _ptr(sx), m, _ptr(y),
+                                        _stream(stream)), "sk_gemm_w4a8_canonical_q")
     return y
 
 

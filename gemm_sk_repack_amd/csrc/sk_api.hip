@@ -60,9 +60,12 @@ int g_spin_limit = 0;   // test hook: exchange polls before the local fallback (
 // Checks for the GEMM entry points, then the launch.
 sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* x, const void* x2,
                    int64_t ld, int xt, const float* gamma, float eps, int m, float* y,
-                   int8_t* q_out, float* sx_out, int32_t* p_out, void* stream, bool any_format) {
+                   int8_t* q_out, float* sx_out, int32_t* p_out, void* stream, bool any_format,
+                   bool canon = false) {
     sk_status s = check_weight(w);
     if (s != SK_OK) return s;
+    if (canon && w->format != SK_W4_SYM) return SK_ERR_FORMAT;
+    if (prologue == sk::PRO_QIN && !x2) return SK_ERR_NULL;
     if (!x || !y || (prologue == sk::PRO_SWIGLU && !x2) || (prologue == sk::PRO_RMSNORM && !gamma))
         return SK_ERR_NULL;
     if (xt != SK_F32 && xt != SK_BF16) return SK_ERR_FORMAT;
@@ -79,10 +82,11 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     } else {
         ld = w->k;
     }
-    if (!aligned16(x) || !aligned16(y) || (x2 && !aligned16(x2)) || (gamma && !aligned16(gamma)) ||
+    if (!aligned16(x) || !aligned16(y) || (x2 && prologue != sk::PRO_QIN && !aligned16(x2)) ||
+        (gamma && !aligned16(gamma)) ||
         (q_out && !aligned16(q_out)) || (p_out && !aligned16(p_out)))
         return SK_ERR_ALIGN;
-    if (w->layout != SK_LAYOUT_STREAM) return SK_ERR_LAYOUT;
+    if (w->layout != (canon ? SK_LAYOUT_CANONICAL : SK_LAYOUT_STREAM)) return SK_ERR_LAYOUT;
     const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
     if (!sk::gemm_plan_ok(G, m, prologue)) return SK_ERR_UNSUPPORTED;
 
@@ -107,6 +111,7 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     c.sx_out = sx_out;
     c.p_out = p_out;
     c.spin_limit = g_spin_limit;
+    c.canon = canon;
     return from_hip(sk::launch_gemm(G, c, st));
 }
 
@@ -180,6 +185,29 @@ SK_EXPORT sk_status sk_debug_gemm(const sk_weight* w, int prologue, const void* 
     if (prologue < sk::PRO_NONE || prologue > sk::PRO_SWIGLU) return SK_ERR_FORMAT;
     return run_gemm(w, false, prologue, x, x2, ld, xt, gamma, eps, m, y, q_out, sx_out, p_out,
                     stream, true);
+}
+
+SK_EXPORT sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t* q, float* sx,
+                                     void* stream) {
+    if (!x || !q || !sx) return SK_ERR_NULL;
+    if (xt != SK_F32 && xt != SK_BF16) return SK_ERR_FORMAT;
+    if (m < 1 || m > 8 || k < 16 || k % 16 != 0) return SK_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(q) || (reinterpret_cast<uintptr_t>(sx) & 3u) != 0)
+        return SK_ERR_ALIGN;
+    return from_hip(sk::launch_quantize(x, xt, m, k, q, sx, static_cast<hipStream_t>(stream)));
+}
+
+SK_EXPORT sk_status sk_gemm_w4a8_canonical(const sk_weight* w, const void* x, int xt, int m,
+                                           float* y, void* stream) {
+    return run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
+                    nullptr, nullptr, stream, false, true);
+}
+
+SK_EXPORT sk_status sk_gemm_w4a8_canonical_q(const sk_weight* w, const int8_t* q, const float* sx,
+                                             int m, float* y, void* stream) {
+    if (sx && (reinterpret_cast<uintptr_t>(sx) & 3u) != 0) return SK_ERR_ALIGN;
+    return run_gemm(w, false, sk::PRO_QIN, q, sx, 0, SK_F32, nullptr, 0.0f, m, y, nullptr,
+                    nullptr, nullptr, stream, false, true);
 }
 
 SK_EXPORT sk_status sk_test_repack_on_host(const sk_weight* w, void* host_bytes, int inverse) {

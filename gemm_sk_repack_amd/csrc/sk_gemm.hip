@@ -89,7 +89,8 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     const int tpr = p.WPR * 64;
     // each thread quantises at most 16 activations of its row, 32 for M >= 2
     // without a prologue (the kernel's register budget)
-    const int ept = (dot4 || pro != PRO_NONE || cb) ? 16 : 32;
+    // (the split path's PRO_QIN keeps PRO_NONE's plan, so the two compare like for like)
+    const int ept = (dot4 || (pro != PRO_NONE && pro != PRO_QIN) || cb) ? 16 : 32;
     p.ept = ept;
     auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
     auto lds_of = [&](int s) {
@@ -192,7 +193,8 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     const bool dot4 = (c.m == 1) && G.fmt != FMT_CB;
     const int gs = (int)(G.g / 32);                // 0 for the codebook's G = 16
     const bool dbg = c.q_out || c.sx_out || c.p_out;
-    KernelFn fn = pick(G.fmt, c.prologue, c.xt, gs, dot4, dbg);
+    KernelFn fn = c.canon ? pick_kernel_split(c.prologue, c.xt, gs, dot4)
+                          : pick(G.fmt, c.prologue, c.xt, gs, dot4, dbg);
     if (!fn) return hipErrorInvalidValue;
 
     KArgs a;

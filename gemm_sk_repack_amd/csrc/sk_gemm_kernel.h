@@ -117,6 +117,7 @@ KernelFn pick_kernel_cb(int pro, int xt, int gs, bool dot4);
 KernelFn pick_kernel_w4_dbg(int pro, int xt, int gs, bool dot4);
 KernelFn pick_kernel_w6_dbg(int pro, int xt, int gs, bool dot4);
 KernelFn pick_kernel_cb_dbg(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4);
 
 namespace {
 
@@ -516,7 +517,7 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
 // the kernel
 // --------------------------------------------------------------------------
 
-template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG>
+template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG, bool CANON>
 __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ Smem sm;
@@ -549,8 +550,28 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
     uint4 xr[NCH], ur[NCH];
     float gv[NCH * E];
-    load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
-    if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
+    // Split path (PRO_QIN): the slice's q arrives ready, M rows of KS / 8
+    // octets; thread tid takes octets tid + i * NT, QMAX per pass.
+    constexpr int QMAX = 4;
+    const int q_oct = a.KS / 8;
+    const int q_total = M * q_oct;
+    uint2 qr[QMAX];
+    auto q_load = [&](const int pass) {
+#pragma unroll
+        for (int i = 0; i < QMAX; ++i) {
+            const int o = (pass * QMAX + i) * NT + tid;
+            const int mq = o / q_oct, ko = o - mq * q_oct;
+            qr[i] = (o < q_total) ? *reinterpret_cast<const uint2*>(
+                        static_cast<const int8_t*>(a.x) + (int64_t)mq * a.k + k_lo + ko * 8)
+                                  : make_uint2(0u, 0u);
+        }
+    };
+    if constexpr (PRO == PRO_QIN) {
+        q_load(0);
+    } else {
+        load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
+        if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
+    }
     const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
@@ -607,17 +628,32 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     int64_t gw = 0, gs = 0;
     int gws = 0, gss = 0, gnv = 0;
     bool grg = false;
+    // canonical layout (CANON, W4 only): per-lane offsets of the group's tile
+    // (rows past N read row N - 1; those lanes' sums are never stored)
+    int glw = 0, gls = 0;
+    const int rb = a.k / 2;                          // bytes per canonical weight row
     auto group_setup = [&]() {
         const int t = t_begin + tg + lj * a.TW;
         const bool valid = lj < jw;
         const int kb = kbw + lg * PIPE;
-        grg = valid && t == a.t_rag;
-        const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kb * a.sbf;
-        gw = !valid ? 0 : grg ? a.rag_w + (int64_t)kb * a.rag_sbw : wo;
-        gs = !valid ? 0 : grg ? a.rag_s + (int64_t)kb * a.rag_sbs : wo + a.swo;
-        gws = !valid ? 0 : grg ? a.rag_sbw : a.sbf;
-        gss = !valid ? 0 : grg ? a.rag_sbs : a.sbf;
         gnv = valid ? min(PIPE, a.spw - lg * PIPE) : 0;
+        if constexpr (CANON) {
+            const int tt = valid ? t : 0;
+            const int nlc = min(tt * TILE_ROWS + nl, a.n - 1) - tt * TILE_ROWS;
+            glw = nlc * rb + 4 * hl;
+            gls = nlc * a.kg * 4;
+            gw = !valid ? 0 : (int64_t)tt * TILE_ROWS * rb + (int64_t)kb * 64;
+            gs = (int64_t)a.n * rb + (!valid ? 0 : ((int64_t)tt * TILE_ROWS * a.kg + (int64_t)kb * NG) * 4);
+            gws = !valid ? 0 : 64;
+            gss = !valid ? 0 : NG * 4;
+        } else {
+            grg = valid && t == a.t_rag;
+            const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kb * a.sbf;
+            gw = !valid ? 0 : grg ? a.rag_w + (int64_t)kb * a.rag_sbw : wo;
+            gs = !valid ? 0 : grg ? a.rag_s + (int64_t)kb * a.rag_sbs : wo + a.swo;
+            gws = !valid ? 0 : grg ? a.rag_sbw : a.sbf;
+            gss = !valid ? 0 : grg ? a.rag_sbs : a.sbf;
+        }
     };
     auto group_next = [&]() {
         if (++lg == ngrp) {
@@ -634,9 +670,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         const int dd = d < gnv ? d : 0;
         const uint8_t* wb = a.data + gw + dd * gws;
         const uint8_t* sb = a.data + gs + dd * gss;
-        const int lw = grg ? lw_rag : lw_full;
-        const int ls = grg ? ls_rag : ls_full;
-        w4 = *reinterpret_cast<const uint4*>(wb + lw);
+        const int lw = CANON ? glw : grg ? lw_rag : lw_full;
+        const int ls = CANON ? gls : grg ? ls_rag : ls_full;
+        if (CANON) {
+            // octet hl of each 32-k block j: 4 bytes, 16 bytes apart in the row
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(wb + lw);
+            w4 = make_uint4(p[0], p[4], p[8], p[12]);
+        } else {
+            w4 = *reinterpret_cast<const uint4*>(wb + lw);
+        }
         if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (grg ? lh_rag : lh_full));
         if (NG == 8) {
             sv = *reinterpret_cast<const float4*>(sb + ls);
@@ -673,119 +715,137 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         const uint32_t lo = bf16_rne(v - __uint_as_float(hi << 16));
         lut_l[tid] = hi | (lo << 16);
     }
-    float h[NCH * E];
-    finish_act<PRO, XT, EPT>(am, xr, ur, h);
-    const int mrow = am.m < M ? am.m : 0;
-    const bool row_lead = lane == 0 && am.m < M && am.it == 0;   // one thread per row
-
-    if (PRO == PRO_RMSNORM) {
-        const double ss = wave_sum(sum_sq<XT, EPT>(h));
-        if (lane == 0) sm.wd[wv] = ss;
-        __syncthreads();
-        double tot;
-        if (a.S == 1) {
-            tot = combine_d(a, sm, mrow);
-        } else {
-            if (poller) exchange_poll(a, sm, lane, s, true);
-            __syncthreads();
-            for (int sl = 0; sl < a.S; ++sl)
-                if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, true);
-            tot = slices_sum(a, sm, mrow);
-        }
-        const float ms = (float)(tot / (double)a.k);
-        const float d = ms + a.eps;
-        const float sd = (float)__builtin_sqrt((double)d);   // correctly rounded fp32 sqrt
-        const float rr = (float)(1.0 / (double)sd);          // correctly rounded fp32 1/x
-        if (row_lead) sm.rr[am.m] = rr;
+    if constexpr (PRO == PRO_QIN) {
+        // the ready-made q octets into LDS (same order as the quantiser's), then sx
+        for (int pass = 0; pass * QMAX * NT < q_total; ++pass) {
+            if (pass > 0) q_load(pass);
 #pragma unroll
-        for (int j = 0; j < NCH * E; ++j) h[j] = rms_apply(h[j], rr, gv[j]);
-    }
-    float amx;
-    {
-        const float mx = wave_max(abs_max<XT, EPT>(h));
-        if (lane == 0) sm.wf[wv] = mx;
-        __syncthreads();
-        if (a.S == 1) {
-            amx = row_max(a, sm, mrow, lane);
-        } else {
-            if (poller) exchange_poll(a, sm, lane, s, false);
-            __syncthreads();
-            for (int sl = 0; sl < a.S; ++sl)
-                if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, false);
-            amx = slices_max(a, sm, mrow);
-        }
-    }
-    const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
-    const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
-    if (row_lead) {
-        sm.sx[am.m] = sx;
-        if (DBG && a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
-    }
-
-    // quantise this slice into LDS (straight-line code: it runs once per
-    // launch, so every instruction of it is a cold instruction-cache fetch)
-    if (am.nw > 0) {
-        // codes of all elements first; the exact division, rarely needed, is one
-        // out-of-line block for the whole thread
-        uint32_t b[NCH * E];
-        float dev = 1.0f;           // min over elements of |fract(t) - 0.5|
-#pragma unroll
-        for (int j = 0; j < NCH * E; ++j) {
-            const float t = h[j] * inv;
-            b[j] = __float_as_uint(t + kRoundMagic);
-            dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
-        }
-        // 2^-125: 1/sx may not be normal
-        if (__builtin_expect((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f, 0)) {
-#pragma unroll
-            for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
-        }
-        uint32_t pk[NCH * E / 4];
-#pragma unroll
-        for (int w = 0; w < NCH * E / 4; ++w) pk[w] = pack_low_bytes(b[4 * w], b[4 * w + 1], b[4 * w + 2], b[4 * w + 3]);
-        // LDS order: in each 128-k super-block, octet 4j + h is stored at position
-        // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
-        // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
-        // is chunk 0's plus i whole super-blocks.
-        const int c0 = am.it;
-        const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
-        const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
-        const int pstep = am.tpr * E;
-#pragma unroll
-        for (int i = 0; i < NCH; ++i) {
-            const uint32_t* pc = pk + i * (E / 4);
-            const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
-            const int pos = pos0 + i * pstep;
-            if (CB) {
-                // bf16 copies of q (exact: |q| <= 127), two per dword
-                uint32_t hb[E / 2];
-#pragma unroll
-                for (int e2 = 0; e2 < E / 2; ++e2) {
-                    const int q0 = (int)(int8_t)(pc[(2 * e2) / 4] >> (8 * ((2 * e2) % 4)));
-                    const int q1 = (int)(int8_t)(pc[(2 * e2 + 1) / 4] >> (8 * ((2 * e2 + 1) % 4)));
-                    hb[e2] = (__float_as_uint((float)q0) >> 16) | (__float_as_uint((float)q1) & 0xFFFF0000u);
-                }
-                uint8_t* dst = reinterpret_cast<uint8_t*>(q_l) + am.m * a.ks + pos * 2;
-                if (ok) {
-                    if (E == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0], hb[1]);
-                    else *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[E / 2 - 1]);
-                }
-            } else {
-                int8_t* dst = q_l + am.m * a.ks + pos;
-                if (ok) {
-                    if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pc[0];
-                    else *reinterpret_cast<uint2*>(dst) = make_uint2(pc[0], pc[E / 4 - 1]);
+            for (int i = 0; i < QMAX; ++i) {
+                const int o = (pass * QMAX + i) * NT + tid;
+                if (o < q_total) {
+                    const int mq = o / q_oct, ko = o - mq * q_oct;
+                    const int ow = ko & 15;
+                    const int pos = (ko >> 4) * 128 + ((ow & 3) * 4 + (ow >> 2)) * 8;
+                    *reinterpret_cast<uint2*>(q_l + mq * a.ks + pos) = qr[i];
                 }
             }
         }
-        if (DBG && a.q_out && r == 0) {          // debug export of q
+        if (tid < M) sm.sx[tid] = static_cast<const float*>(a.x2)[tid];
+    } else {
+        float h[NCH * E];
+        finish_act<PRO, XT, EPT>(am, xr, ur, h);
+        const int mrow = am.m < M ? am.m : 0;
+        const bool row_lead = lane == 0 && am.m < M && am.it == 0;   // one thread per row
+
+        if (PRO == PRO_RMSNORM) {
+            const double ss = wave_sum(sum_sq<XT, EPT>(h));
+            if (lane == 0) sm.wd[wv] = ss;
+            __syncthreads();
+            double tot;
+            if (a.S == 1) {
+                tot = combine_d(a, sm, mrow);
+            } else {
+                if (poller) exchange_poll(a, sm, lane, s, true);
+                __syncthreads();
+                for (int sl = 0; sl < a.S; ++sl)
+                    if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, true);
+                tot = slices_sum(a, sm, mrow);
+            }
+            const float ms = (float)(tot / (double)a.k);
+            const float d = ms + a.eps;
+            const float sd = (float)__builtin_sqrt((double)d);   // correctly rounded fp32 sqrt
+            const float rr = (float)(1.0 / (double)sd);          // correctly rounded fp32 1/x
+            if (row_lead) sm.rr[am.m] = rr;
+#pragma unroll
+            for (int j = 0; j < NCH * E; ++j) h[j] = rms_apply(h[j], rr, gv[j]);
+        }
+        float amx;
+        {
+            const float mx = wave_max(abs_max<XT, EPT>(h));
+            if (lane == 0) sm.wf[wv] = mx;
+            __syncthreads();
+            if (a.S == 1) {
+                amx = row_max(a, sm, mrow, lane);
+            } else {
+                if (poller) exchange_poll(a, sm, lane, s, false);
+                __syncthreads();
+                for (int sl = 0; sl < a.S; ++sl)
+                    if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, false);
+                amx = slices_max(a, sm, mrow);
+            }
+        }
+        const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
+        const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+        if (row_lead) {
+            sm.sx[am.m] = sx;
+            if (DBG && a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
+        }
+
+        // quantise this slice into LDS (straight-line code: it runs once per
+        // launch, so every instruction of it is a cold instruction-cache fetch)
+        if (am.nw > 0) {
+            // codes of all elements first; the exact division, rarely needed, is one
+            // out-of-line block for the whole thread
+            uint32_t b[NCH * E];
+            float dev = 1.0f;           // min over elements of |fract(t) - 0.5|
+#pragma unroll
+            for (int j = 0; j < NCH * E; ++j) {
+                const float t = h[j] * inv;
+                b[j] = __float_as_uint(t + kRoundMagic);
+                dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
+            }
+            // 2^-125: 1/sx may not be normal
+            if (__builtin_expect((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f, 0)) {
+#pragma unroll
+                for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+            }
+            uint32_t pk[NCH * E / 4];
+#pragma unroll
+            for (int w = 0; w < NCH * E / 4; ++w) pk[w] = pack_low_bytes(b[4 * w], b[4 * w + 1], b[4 * w + 2], b[4 * w + 3]);
+            // LDS order: in each 128-k super-block, octet 4j + h is stored at position
+            // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
+            // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
+            // is chunk 0's plus i whole super-blocks.
+            const int c0 = am.it;
+            const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
+            const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
+            const int pstep = am.tpr * E;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
-                const int c = chunk_of(am, i);
-                if (i < am.nw && c < am.cpr) {
-                    int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
-                    if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[i];
-                    else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[2 * i], pk[2 * i + 1]);
+                const uint32_t* pc = pk + i * (E / 4);
+                const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
+                const int pos = pos0 + i * pstep;
+                if (CB) {
+                    // bf16 copies of q (exact: |q| <= 127), two per dword
+                    uint32_t hb[E / 2];
+#pragma unroll
+                    for (int e2 = 0; e2 < E / 2; ++e2) {
+                        const int q0 = (int)(int8_t)(pc[(2 * e2) / 4] >> (8 * ((2 * e2) % 4)));
+                        const int q1 = (int)(int8_t)(pc[(2 * e2 + 1) / 4] >> (8 * ((2 * e2 + 1) % 4)));
+                        hb[e2] = (__float_as_uint((float)q0) >> 16) | (__float_as_uint((float)q1) & 0xFFFF0000u);
+                    }
+                    uint8_t* dst = reinterpret_cast<uint8_t*>(q_l) + am.m * a.ks + pos * 2;
+                    if (ok) {
+                        if (E == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(hb[0], hb[1]);
+                        else *reinterpret_cast<uint4*>(dst) = make_uint4(hb[0], hb[1], hb[2], hb[E / 2 - 1]);
+                    }
+                } else {
+                    int8_t* dst = q_l + am.m * a.ks + pos;
+                    if (ok) {
+                        if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pc[0];
+                        else *reinterpret_cast<uint2*>(dst) = make_uint2(pc[0], pc[E / 4 - 1]);
+                    }
+                }
+            }
+            if (DBG && a.q_out && r == 0) {          // debug export of q
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    const int c = chunk_of(am, i);
+                    if (i < am.nw && c < am.cpr) {
+                        int8_t* gq = a.q_out + (int64_t)am.m * a.k + k_lo + c * E;
+                        if (E == 4) *reinterpret_cast<uint32_t*>(gq) = pk[i];
+                        else *reinterpret_cast<uint2*>(gq) = make_uint2(pk[2 * i], pk[2 * i + 1]);
+                    }
                 }
             }
         }
@@ -810,6 +870,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         // compiler waits for exactly this slot's loads (a skipped read would
         // leave them pending when the next load reuses the registers).
         if (FMT == FMT_W6) __asm__ volatile("" ::"v"(w_in.x), "v"(h_in.x), "v"(s_in.x));
+        else if (CANON) __asm__ volatile("" ::"v"(w_in.x), "v"(w_in.y), "v"(w_in.z), "v"(w_in.w), "v"(s_in.x));
         else __asm__ volatile("" ::"v"(w_in.x), "v"(s_in.x));
         if (work) {
             const int kb = kb_lo + kbr;
@@ -830,6 +891,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     const uint32_t hhi = (j & 1) ? hd : (hd << 4);          // bits 4-5 of code c + 4
                     lo[j] = ((wd[j] << 2) & 0x3C3C3C3Cu) | (hlo & 0xC0C0C0C0u);
                     hi[j] = ((wd[j] >> 2) & 0x3C3C3C3Cu) | (hhi & 0xC0C0C0C0u);
+                } else if (CANON) {
+                    // canonical bytes hold codes (2i, 2i + 1) in (low, high) nibbles
+                    const uint32_t ev = (wd[j] << 4) & 0xF0F0F0F0u;   // codes 0, 2, 4, 6
+                    const uint32_t od = wd[j] & 0xF0F0F0F0u;          // codes 1, 3, 5, 7
+                    lo[j] = __builtin_amdgcn_perm(od, ev, 0x05010400u);
+                    hi[j] = __builtin_amdgcn_perm(od, ev, 0x07030602u);
                 } else {
                     lo[j] = (wd[j] << 4) & 0xF0F0F0F0u;
                     hi[j] = wd[j] & 0xF0F0F0F0u;
@@ -1073,9 +1140,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 template <int FMT, int PRO, int XT, int GS, bool DBG>
 KernelFn pick_dot(bool dot4) {
     if constexpr (FMT == FMT_CB) {
-        return gemm_kernel<FMT, PRO, XT, GS, false, DBG>;   // the codebook runs on MFMA for every M
+        return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false>;   // the codebook runs on MFMA for every M
     } else {
-        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG> : gemm_kernel<FMT, PRO, XT, GS, false, DBG>;
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false>
+                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false>;
     }
 }
 template <int FMT, int PRO, int XT, bool DBG>
@@ -1093,6 +1161,23 @@ template <int FMT, int PRO, bool DBG>
 KernelFn pick_xt(int xt, int gs, bool dot4) {
     return xt == 1 ? pick_gs<FMT, PRO, 1, DBG>(gs, dot4) : pick_gs<FMT, PRO, 0, DBG>(gs, dot4);
 }
+// The split path's kernels: 4-bit weights in the canonical layout, either
+// quantising x in the launch (PRO_NONE) or reading q from memory (PRO_QIN).
+template <int PRO, int XT, int GS>
+KernelFn pick_canon_dot(bool dot4) {
+    return dot4 ? gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true>
+                : gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true>;
+}
+template <int PRO, int XT>
+KernelFn pick_canon_gs(int gs, bool dot4) {
+    switch (gs) {
+        case 1: return pick_canon_dot<PRO, XT, 1>(dot4);
+        case 2: return pick_canon_dot<PRO, XT, 2>(dot4);
+        case 4: return pick_canon_dot<PRO, XT, 4>(dot4);
+        default: return nullptr;
+    }
+}
+
 template <int FMT, bool DBG>
 KernelFn pick_format(int pro, int xt, int gs, bool dot4) {
     switch (pro) {

@@ -1,0 +1,90 @@
+// sk_gemm_split.hip -- the split path kept for comparison: GEMM kernels that
+// read 4-bit weights straight from the canonical [codes | scales] layout, with
+// the activations quantised in the launch or by a separate kernel, and that
+// separate quantisation kernel.
+#include "sk_gemm_kernel.h"
+
+namespace sk {
+
+KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4) {
+    if (pro == PRO_QIN) return pick_canon_gs<PRO_QIN, 0>(gs, dot4);
+    return xt == 1 ? pick_canon_gs<PRO_NONE, 1>(gs, dot4) : pick_canon_gs<PRO_NONE, 0>(gs, dot4);
+}
+
+}  // namespace sk
+
+namespace sk {
+namespace {
+
+// One workgroup per activation row: the row's absmax, then sx = absmax/127 and
+// q = rint(h/sx) with the same arithmetic as the GEMM's in-launch quantiser
+// (multiply by 1/sx, exact division where the product may sit within rounding
+// error of a half-integer), written to memory.
+constexpr int QT = 256;
+template <int XT>
+__global__ __launch_bounds__(QT) void quantize_kernel(const void* x, int k, int8_t* q, float* sx_out) {
+    constexpr int E = XT == 0 ? 4 : 8;              // elements per 16-byte chunk
+    __shared__ float wmax[QT / 64];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x;
+    const uint8_t* row = static_cast<const uint8_t*>(x) + (int64_t)m * k * (XT == 0 ? 4 : 2);
+    const int nch = k / E;
+    auto chunk = [&](const int c, float v[E]) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(row + (int64_t)c * 16);
+        const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            v[e] = XT == 0 ? __uint_as_float(w[e])
+                           : __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+    };
+    float mx = 0.0f;
+    for (int c = tid; c < nch; c += QT) {
+        float v[E];
+        chunk(c, v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    }
+    mx = wave_max(mx);
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    float amx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < QT / 64; ++w) amx = fmaxf(amx, wmax[w]);
+    const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
+    const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+    if (tid == 0) sx_out[m] = sx;
+    for (int c = tid; c < nch; c += QT) {
+        float v[E];
+        chunk(c, v);
+        uint32_t b[E];
+        float dev = 1.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float t = v[e] * inv;
+            b[e] = __float_as_uint(t + kRoundMagic);
+            dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
+        }
+        if ((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) b[e] = __float_as_uint(v[e] / sx + kRoundMagic);
+        }
+        int8_t* dst = q + (int64_t)m * k + (int64_t)c * E;
+        if constexpr (E == 4) {
+            *reinterpret_cast<uint32_t*>(dst) = pack_low_bytes(b[0], b[1], b[2], b[3]);
+        } else {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low_bytes(b[0], b[1], b[2], b[3]),
+                                                        pack_low_bytes(b[4], b[5], b[6], b[7]));
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int xt, int m, int64_t k, int8_t* q, float* sx,
+                           hipStream_t st) {
+    if (xt == 1) hipLaunchKernelGGL(quantize_kernel<1>, dim3(m), dim3(QT), 0, st, x, (int)k, q, sx);
+    else hipLaunchKernelGGL(quantize_kernel<0>, dim3(m), dim3(QT), 0, st, x, (int)k, q, sx);
+    return hipGetLastError();
+}
+
+}  // namespace sk

@@ -15,7 +15,10 @@ hipError_t repack_device(uint8_t* data, const Geom& G, bool inverse, hipStream_t
 bool repack_host(uint8_t* data, const Geom& G, bool inverse);
 
 // GEMM (sk_gemm.hip)
-enum Prologue : int { PRO_NONE = 0, PRO_RMSNORM = 1, PRO_SWIGLU = 2 };
+// PRO_QIN: no prologue and no quantisation in the GEMM; x holds the int8 q
+// [M][K] and x2 the float sx [M] that a separate quantisation kernel wrote
+// (the split, unfused path kept for comparison).
+enum Prologue : int { PRO_NONE = 0, PRO_RMSNORM = 1, PRO_SWIGLU = 2, PRO_QIN = 3 };
 
 struct GemmCall {
     const uint8_t* data;   // repacked weight
@@ -33,6 +36,7 @@ struct GemmCall {
     float* sx_out;
     int32_t* p_out;
     int spin_limit;        // polls of an exchange slot before computing it locally (0 = default)
+    bool canon;            // weight in the canonical [codes | scales] layout (no repack)
 };
 
 // Largest K a GEMM call accepts.
@@ -70,5 +74,9 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override);
 bool gemm_plan_ok(const Geom& G, int m, int pro);
 void set_split_override(int s);
 hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st);
+// Per-row int8 quantisation of x [M][K] into q [M][K] and sx [M] as its own
+// launch (the split path); the same arithmetic as inside the GEMM.
+hipError_t launch_quantize(const void* x, int xt, int m, int64_t k, int8_t* q, float* sx,
+                           hipStream_t st);
 
 }  // namespace sk

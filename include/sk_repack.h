@@ -192,6 +192,47 @@ sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void*
                                int64_t ld, int xt, int m, float* y, void* stream);
 
 /*
+ * The split path, kept to measure what the stream layout and the fused
+ * quantisation buy [LIN]: the pages' earlier design read the weights and
+ * their scales from two separate tensors and quantised the activations in a
+ * launch of its own, with q going through memory.  Here the weight stays in
+ * the canonical layout (codes region, then scales region), and the
+ * quantisation can run as its own launch.  Results equal those of the fused
+ * entry points bit for bit (same q, same partial sums in the same order).
+ */
+
+/*
+ * Per-row int8 quantisation as its own launch: q[m][k] and sx[m] exactly as
+ * sk_gemm_w4a8 computes them inside its launch [FMT activations].
+ *   x  : device [M][K] row-major, dtype xt, 16-byte aligned
+ *   q  : device [M][K] int8, 16-byte aligned (fully overwritten)
+ *   sx : device [M] float32, 4-byte aligned (fully overwritten)
+ *   m 1..8, K a positive multiple of 16.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT (dtype), HIP.
+ */
+sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t* q, float* sx,
+                           void* stream);
+
+/*
+ * sk_gemm_w4a8 on a weight left in the canonical layout
+ * (w->layout == SK_LAYOUT_CANONICAL, no repack): the workgroups read each
+ * tile's codes and its scales from the two regions.  SK_W4_SYM only; the
+ * backend restrictions of sk_gemm_w4a8 apply.
+ * Errors: as sk_gemm_w4a8 (LAYOUT if the weight is repacked, FORMAT if it is
+ * not SK_W4_SYM).
+ */
+sk_status sk_gemm_w4a8_canonical(const sk_weight* w, const void* x, int xt, int m,
+                                 float* y, void* stream);
+
+/*
+ * The same GEMM with the activations already quantised (by sk_quantize_rows):
+ *   q  : device [M][K] int8, 16-byte aligned;  sx : device [M] float32, 4-byte aligned.
+ * Errors: as sk_gemm_w4a8_canonical.
+ */
+sk_status sk_gemm_w4a8_canonical_q(const sk_weight* w, const int8_t* q, const float* sx, int m,
+                                   float* y, void* stream);
+
+/*
  * Test hook: the GEMM kernels instantiated with an export flag.  Runs the same
  * computation as the entry point selected by `prologue` (0 = none,
  * 1 = RMSNorm, 2 = SwiGLU; `x2`, `ld`, `gamma`, `eps` as there; for prologue 0

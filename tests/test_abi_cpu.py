@@ -116,6 +116,26 @@ def test_backend_restrictions():
             assert sk.gemm_plan(12288, 4096, g, sk.SK_W4_CODEBOOK, m)["status"] == sk.SK_OK
 
 
+def test_split_path_validation():
+    q = sk.LIB.sk_quantize_rows
+    assert q(None, 0, 1, 256, FAKE, FAKE, None) == sk.SK_ERR_NULL
+    assert q(FAKE, 0, 1, 256, FAKE, None, None) == sk.SK_ERR_NULL
+    assert q(FAKE, 5, 1, 256, FAKE, FAKE, None) == sk.SK_ERR_FORMAT
+    assert q(FAKE, 0, 0, 256, FAKE, FAKE, None) == sk.SK_ERR_SHAPE
+    assert q(FAKE, 0, 9, 256, FAKE, FAKE, None) == sk.SK_ERR_SHAPE
+    assert q(FAKE, 0, 1, 24, FAKE, FAKE, None) == sk.SK_ERR_SHAPE
+    assert q(FAKE + 4, 0, 1, 256, FAKE, FAKE, None) == sk.SK_ERR_ALIGN
+    assert q(FAKE, 0, 1, 256, FAKE, FAKE + 2, None) == sk.SK_ERR_ALIGN
+    can = sk.LIB.sk_gemm_w4a8_canonical
+    assert can(ctypes.byref(W(layout=1)), FAKE, 0, 1, FAKE, None) == sk.SK_ERR_LAYOUT
+    assert can(ctypes.byref(W(fmt=2, g=64, layout=0)), FAKE, 0, 1, FAKE, None) == sk.SK_ERR_FORMAT
+    assert can(ctypes.byref(W(layout=0)), None, 0, 1, FAKE, None) == sk.SK_ERR_NULL
+    cq = sk.LIB.sk_gemm_w4a8_canonical_q
+    assert cq(ctypes.byref(W(layout=0)), FAKE, None, 1, FAKE, None) == sk.SK_ERR_NULL
+    assert cq(ctypes.byref(W(layout=0)), FAKE, FAKE + 2, 1, FAKE, None) == sk.SK_ERR_ALIGN
+    assert cq(ctypes.byref(W(layout=1)), FAKE, FAKE, 1, FAKE, None) == sk.SK_ERR_LAYOUT
+
+
 def test_failed_call_leaves_descriptor_unchanged():
     w = W(layout=0, data=FAKE + 8)
     assert sk.LIB.sk_repack_w4a8(ctypes.byref(w), None) == sk.SK_ERR_ALIGN
