@@ -95,6 +95,51 @@ def time_graph(torch, stream, fn, calls):
     return float(np.median(t))
 
 
+def time_ablation(torch, sk, stream, host, xs, R, per):
+    """The same step on the split path: (a) the weight left in the canonical
+    layout (codes and scales read from their two regions), quantising in the
+    launch; (b) also quantising in a launch of its own, q and sx through
+    memory.  µs per call from graphs over R rotated canonical copies."""
+    dev = torch.device("cuda:0")
+    rows = []
+    tot = {"fused": 0.0, "canonical": 0.0, "split": 0.0}
+    for name, n, k in SHAPES:
+        base = torch.from_numpy(host[name]).to(dev)
+        cps = [sk.QuantWeight(base if i == 0 else base.clone(), n, k, GROUP, sk.SK_W4_SYM)
+               for i in range(R)]
+        for m in (1, 8):
+            x = xs[(m, k)]
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            q = torch.empty((m, k), dtype=torch.int8, device=dev)
+            sx = torch.empty((m,), dtype=torch.float32, device=dev)
+            us_can = time_graph(torch, stream, lambda i: sk.sk_gemm_w4a8_canonical(cps[i % R], x, y=y),
+                                4 * R)
+
+            def split(i):
+                sk.sk_quantize_rows(x, q=q, sx=sx)
+                sk.sk_gemm_w4a8_canonical_q(cps[i % R], q, sx, y=y)
+            us_split = time_graph(torch, stream, split, 4 * R)
+            us_fused = next(p["us_per_call"] for p in per if p["linear"] == name and p["m"] == m)
+            b = alg_bytes(n, k, m)
+            rows.append({"linear": name, "m": m, "fused_us": round(us_fused, 3),
+                         "canonical_us": round(us_can, 3), "split_us": round(us_split, 3),
+                         "fused_GBps": round(b / (us_fused * 1e-6) / 1e9, 1),
+                         "split_GBps": round(b / (us_split * 1e-6) / 1e9, 1)})
+            tot["fused"] += us_fused
+            tot["canonical"] += us_can
+            tot["split"] += us_split
+            log(f"split path {name:8s} M={m}: fused {us_fused:7.3f}  canonical {us_can:7.3f}  "
+                f"canonical + separate quantisation {us_split:7.3f} us/call")
+        del cps, base
+    return {"what": ("the step's 8 calls on (a) the weight in the canonical layout, quantising "
+                     "in the launch, and (b) that plus quantisation as its own launch (q, sx "
+                     "through memory), against the fused stream-layout path"),
+            "step_us": {kk: round(v, 3) for kk, v in tot.items()},
+            "speedup_of_fused": {"over_canonical": round(tot["canonical"] / tot["fused"], 4),
+                                 "over_split": round(tot["split"] / tot["fused"], 4)},
+            "per_call": rows}
+
+
 def time_variants(torch, sk, S, dev, stream):
     """The other workloads: fused prologues at hidden 4096, the W6 / codebook /
     lm_head formats at K = 4096, and one 27B-class layer (bf16 activations) whose
@@ -194,6 +239,8 @@ def main() -> int:
     ap.add_argument("--variants", action="store_true",
                     help="also time the other workloads (fused prologues, W6 / codebook / "
                          "lm_head formats, the 27B-class layer) and add them as `variants`")
+    ap.add_argument("--no-ablation", action="store_true",
+                    help="skip the split-path comparison (canonical layout, separate quantisation)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy a 256 MiB device buffer 5 times and exit: the known-size "
                          "kernel that calibrates the HBM byte counters")
@@ -343,6 +390,11 @@ def main() -> int:
         "us_per_launch": round(dom_us / len(SHAPES), 3),
     }
 
+    # ---------------- split path: what the stream layout and fusion buy ----------------
+    ablation = None
+    if not args.no_ablation:
+        ablation = time_ablation(torch, sk, stream, host, xs, R, per)
+
     # ---------------- CPU baseline: the oracle on one step ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -394,6 +446,8 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if ablation is not None:
+        out["ablation"] = ablation
     if variants is not None:
         out["variants"] = variants
     print(json.dumps(out), flush=True)
