@@ -31,7 +31,8 @@ BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
 # Every symbol include/sk_repack.h and include/sk_repack_test.h declare.
 EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4a8",
            "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu",
-           "sk_quantize_rows", "sk_gemm_w4a8_canonical", "sk_gemm_w4a8_canonical_q",
+           "sk_gemm_experts", "sk_quantize_rows", "sk_gemm_w4a8_canonical",
+           "sk_gemm_w4a8_canonical_q",
            "sk_debug_gemm",
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
            "sk_test_set_spin_limit"]
@@ -65,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "sk_gemm_w6a8": ([W, P, I, I, P, P], I),
         "sk_gemm_fused_rmsnorm": ([W, P, I, P, F, I, P, P], I),
         "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P], I),
+        "sk_gemm_experts": ([W, I, ctypes.POINTER(ctypes.c_int32), I, P, I, I, P, P], I),
         "sk_quantize_rows": ([P, I, I, I, P, P, P], I),
         "sk_gemm_w4a8_canonical": ([W, P, I, I, P, P], I),
         "sk_gemm_w4a8_canonical_q": ([W, P, P, I, P, P], I),
@@ -169,6 +171,19 @@ def sk_gemm_w6a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.
     y = _out(w, m, y)
     _check(LIB.sk_gemm_w6a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
            "sk_gemm_w6a8")
+    return y
+
+
+def sk_gemm_experts(bank: QuantWeight, rows_per_expert: int, experts, x: torch.Tensor, y=None,
+                    stream=None) -> torch.Tensor:
+    """Listed experts of a repacked expert bank (E * rows_per_expert rows) times x, in one
+    launch; returns y [M, len(experts) * rows_per_expert]."""
+    ids = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, len(experts) * rows_per_expert), dtype=torch.float32, device="cuda")
+    _check(LIB.sk_gemm_experts(ctypes.byref(bank.desc), rows_per_expert, ids, len(experts),
+                               _ptr(x), _xt(x), m, _ptr(y), _stream(stream)), "sk_gemm_experts")
     return y
 
 

@@ -61,7 +61,8 @@ int g_spin_limit = 0;   // test hook: exchange polls before the local fallback (
 sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* x, const void* x2,
                    int64_t ld, int xt, const float* gamma, float eps, int m, float* y,
                    int8_t* q_out, float* sx_out, int32_t* p_out, void* stream, bool any_format,
-                   bool canon = false) {
+                   bool canon = false, int rows_per_expert = 0, const int32_t* experts = nullptr,
+                   int n_list = 0) {
     sk_status s = check_weight(w);
     if (s != SK_OK) return s;
     if (canon && w->format != SK_W4_SYM) return SK_ERR_FORMAT;
@@ -87,7 +88,10 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
         (q_out && !aligned16(q_out)) || (p_out && !aligned16(p_out)))
         return SK_ERR_ALIGN;
     if (w->layout != (canon ? SK_LAYOUT_CANONICAL : SK_LAYOUT_STREAM)) return SK_ERR_LAYOUT;
-    const Geom G = sk::make_geom(w->n, w->k, w->group, w->format);
+    // expert bank: the call's output rows are n_list experts of rows_per_expert rows
+    int64_t n_call = w->n;
+    if (rows_per_expert) n_call = (int64_t)n_list * rows_per_expert;
+    const Geom G = sk::make_geom(n_call, w->k, w->group, w->format);
     if (!sk::gemm_plan_ok(G, m, prologue)) return SK_ERR_UNSUPPORTED;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -112,6 +116,9 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     c.p_out = p_out;
     c.spin_limit = g_spin_limit;
     c.canon = canon;
+    c.rows_per_expert = rows_per_expert;
+    c.n_list = n_list;
+    c.experts = experts;
     return from_hip(sk::launch_gemm(G, c, st));
 }
 
@@ -176,6 +183,23 @@ SK_EXPORT sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, c
                                          int64_t ld, int xt, int m, float* y, void* stream) {
     return run_gemm(w, false, sk::PRO_SWIGLU, gate, up, ld, xt, nullptr, 0.0f, m, y, nullptr,
                     nullptr, nullptr, stream, true);
+}
+
+SK_EXPORT sk_status sk_gemm_experts(const sk_weight* bank, int rows_per_expert,
+                                    const int32_t* experts, int n_list, const void* x, int xt,
+                                    int m, float* y, void* stream) {
+    sk_status s = check_weight(bank);
+    if (s != SK_OK) return s;
+    if (!experts) return SK_ERR_NULL;
+    if (rows_per_expert < 16 || rows_per_expert % 16 != 0 || bank->n % rows_per_expert != 0)
+        return SK_ERR_SHAPE;
+    const int n_experts = bank->n / rows_per_expert;
+    if (n_list < 1 || n_list > 64) return SK_ERR_SHAPE;
+    for (int i = 0; i < n_list; ++i)
+        if (experts[i] < 0 || experts[i] >= n_experts) return SK_ERR_SHAPE;
+    return run_gemm(bank, bank->format == SK_W6_SYM, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f,
+                    m, y, nullptr, nullptr, nullptr, stream, true, false, rows_per_expert,
+                    experts, n_list);
 }
 
 SK_EXPORT sk_status sk_debug_gemm(const sk_weight* w, int prologue, const void* x, const void* x2,

@@ -242,6 +242,9 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.WPR = p.WPR;
     a.ks = p.ks;
     a.spin_limit = c.spin_limit > 0 ? c.spin_limit : (1 << 20);
+    a.tpe = c.rows_per_expert / TILE_ROWS;
+    for (int i = 0; i < kMaxExperts; ++i)
+        a.emap[i] = (uint16_t)((c.rows_per_expert && i < c.n_list) ? c.experts[i] : 0);
     a.tq = (int)(G.T / p.R);
     a.trem = (int)(G.T % p.R);
     a.jn0 = (a.tq + p.TW - 1) / p.TW;

@@ -54,6 +54,7 @@ constexpr int PIPE = 4;        // super-blocks in flight per wave
 constexpr int PRIME = 2;       // of which issued before the activation prologue
 constexpr int SMAX = 32;       // largest number of K-slices
 constexpr int kMaxTilesPerGroup = 64;
+constexpr int kMaxExperts = 64;          // experts per expert-bank call
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -93,6 +94,10 @@ struct KArgs {
     // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
     // wave index within the row (14-18) and activation chunk steps (19-22)
     uint32_t wtab[NW];
+    // expert banks: logical tile t is tile t % tpe of expert emap[t / tpe] in
+    // the bank (tpe = tiles per expert; 0 for a plain weight)
+    int tpe;
+    uint16_t emap[kMaxExperts];
 };
 
 struct Smem {
@@ -648,7 +653,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             gss = !valid ? 0 : NG * 4;
         } else {
             grg = valid && t == a.t_rag;
-            const int64_t wo = (int64_t)t * a.tile_full + (int64_t)kb * a.sbf;
+            // the bank's tile behind logical tile t (expert banks), else t; a
+            // stand-in group maps tile 0 so the map is never read past the list
+            const int tv = valid ? t : 0;
+            const int tb = a.tpe ? a.emap[tv / a.tpe] * a.tpe + tv % a.tpe : t;
+            const int64_t wo = (int64_t)tb * a.tile_full + (int64_t)kb * a.sbf;
             gw = !valid ? 0 : grg ? a.rag_w + (int64_t)kb * a.rag_sbw : wo;
             gs = !valid ? 0 : grg ? a.rag_s + (int64_t)kb * a.rag_sbs : wo + a.swo;
             gws = !valid ? 0 : grg ? a.rag_sbw : a.sbf;

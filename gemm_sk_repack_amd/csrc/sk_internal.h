@@ -37,6 +37,11 @@ struct GemmCall {
     int32_t* p_out;
     int spin_limit;        // polls of an exchange slot before computing it locally (0 = default)
     bool canon;            // weight in the canonical [codes | scales] layout (no repack)
+    // expert bank: the call's N is n_list experts x rows_per_expert rows, drawn
+    // from the bank by `experts` (host ids); rows_per_expert == 0 otherwise
+    int rows_per_expert;
+    int n_list;
+    const int32_t* experts;
 };
 
 // Largest K a GEMM call accepts.

@@ -192,6 +192,26 @@ sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void*
                                int64_t ld, int xt, int m, float* y, void* stream);
 
 /*
+ * Expert bank [FMT, embeddings and MoE: grouped W4A8/W6A8 banks store their
+ * experts' output rows flattened to E * N]: `bank` is one repacked weight of
+ * E * rows_per_expert rows (any format), expert e owning rows
+ * [e * rows_per_expert, (e + 1) * rows_per_expert).  One launch computes, for
+ * each of the n_list listed experts, its rows times x (quantised once):
+ *   y[m][i * rows_per_expert + j] = (expert experts[i], row j) . x[m]
+ *   experts : HOST array of n_list expert ids in [0, E) (repeats allowed),
+ *             read at the call (a captured graph keeps the list it saw)
+ *   y       : device [M][n_list * rows_per_expert] float32, 16-byte aligned
+ *   rows_per_expert a multiple of 16 dividing bank->n; 1 <= n_list <= 64.
+ * Each listed expert's output is what sk_gemm_w4a8 / sk_gemm_w6a8 gives on
+ * that expert's rows alone: the same q and the same int32 partials; only the
+ * grouping of the fp32 sums across waves may differ with the launch plan.
+ * Errors: NULL, SHAPE (rows_per_expert, n_list or an id out of range), ALIGN,
+ * FORMAT, LAYOUT, UNSUPPORTED, HIP.
+ */
+sk_status sk_gemm_experts(const sk_weight* bank, int rows_per_expert, const int32_t* experts,
+                          int n_list, const void* x, int xt, int m, float* y, void* stream);
+
+/*
  * The split path, kept to measure what the stream layout and the fused
  * quantisation buy [LIN]: the pages' earlier design read the weights and
  * their scales from two separate tensors and quantised the activations in a

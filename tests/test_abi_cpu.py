@@ -116,6 +116,22 @@ def test_backend_restrictions():
             assert sk.gemm_plan(12288, 4096, g, sk.SK_W4_CODEBOOK, m)["status"] == sk.SK_OK
 
 
+def test_expert_bank_validation():
+    ex = sk.LIB.sk_gemm_experts
+    ids = (ctypes.c_int32 * 2)(0, 1)
+    bad = (ctypes.c_int32 * 1)(4)
+    bank = W(n=512, layout=1)                       # 4 experts of 128 rows
+    assert ex(ctypes.byref(bank), 128, None, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_NULL
+    assert ex(ctypes.byref(bank), 100, ids, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
+    assert ex(ctypes.byref(bank), 96, ids, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
+    assert ex(ctypes.byref(bank), 128, ids, 0, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
+    assert ex(ctypes.byref(bank), 128, ids, 65, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
+    assert ex(ctypes.byref(bank), 128, bad, 1, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
+    assert ex(ctypes.byref(bank), 128, ids, 2, FAKE, 0, 9, FAKE, None) == sk.SK_ERR_SHAPE
+    assert ex(ctypes.byref(W(n=512, layout=0)), 128, ids, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_LAYOUT
+    assert ex(ctypes.byref(bank), 128, ids, 2, FAKE + 4, 0, 1, FAKE, None) == sk.SK_ERR_ALIGN
+
+
 def test_split_path_validation():
     q = sk.LIB.sk_quantize_rows
     assert q(None, 0, 1, 256, FAKE, FAKE, None) == sk.SK_ERR_NULL
