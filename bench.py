@@ -95,6 +95,55 @@ def time_graph(torch, stream, fn, calls):
     return float(np.median(t))
 
 
+def time_experts(torch, sk, S, stream):
+    """Expert-bank workload (synthetic): a W4A8 G=32 bank of 32 experts x 2048
+    rows at K = 4096 (168 MB), 7 rotated copies (1.2 GB); M = 1 with 2 listed
+    experts and M = 8 with 8, a fresh list per call.  One sk_gemm_experts
+    launch against one sk_gemm_w4a8 launch per listed expert."""
+    dev = torch.device("cuda:0")
+    E, rows, k, g, R = 32, 2048, 4096, 32, 7
+    _, _, buf = S.make_weight(0, E * rows, k, g, S.seed_of(5, 0, S.TENSOR_W), S.seed_of(5, 0, S.TENSOR_S))
+    base = sk.QuantWeight(torch.from_numpy(buf).to(dev), E * rows, k, g, sk.SK_W4_SYM)
+    sk.sk_repack_w4a8(base)
+    banks = [base]
+    for _ in range(R - 1):
+        c = sk.QuantWeight(base.data.clone(), E * rows, k, g, sk.SK_W4_SYM)
+        c.desc.layout = sk.SK_LAYOUT_STREAM
+        banks.append(c)
+    eb = sk.weight_bytes(sk.SK_W4_SYM, rows, k, g)       # one expert's bytes, contiguous in the bank
+
+    def view(b, e):
+        v = sk.QuantWeight(banks[b].data[e * eb:(e + 1) * eb], rows, k, g, sk.SK_W4_SYM)
+        v.desc.layout = sk.SK_LAYOUT_STREAM
+        return v
+    views = [[view(b, e) for e in range(E)] for b in range(R)]
+    rng = np.random.default_rng(S.seed_of(5, 0, 9))
+    out = []
+    for m, nl in ((1, 2), (8, 8)):
+        lists = [sorted(rng.choice(E, nl, replace=False).tolist()) for _ in range(16)]
+        x = torch.from_numpy(S.activations(S.seed_of(5, m, S.TENSOR_X), m, k)).to(dev)
+        y = torch.empty((m, nl * rows), dtype=torch.float32, device=dev)
+        ys = [torch.empty((m, rows), dtype=torch.float32, device=dev) for _ in range(nl)]
+        us_bank = time_graph(torch, stream,
+                             lambda i: sk.sk_gemm_experts(banks[i % R], rows, lists[i % 16], x, y=y), 4 * R)
+
+        def separate(i):
+            for j, e in enumerate(lists[i % 16]):
+                sk.sk_gemm_w4a8(views[i % R][e], x, y=ys[j])
+        us_sep = time_graph(torch, stream, separate, 4 * R)
+        b = alg_bytes(nl * rows, k, m)
+        out.append({"m": m, "experts_per_call": nl, "us_per_call": round(us_bank, 3),
+                    "GBps": round(b / (us_bank * 1e-6) / 1e9, 1),
+                    "separate_launches_us": round(us_sep, 3),
+                    "separate_GBps": round(b / (us_sep * 1e-6) / 1e9, 1)})
+        log(f"experts M={m} x{nl}: one launch {us_bank:7.3f} us ({out[-1]['GBps']} GB/s), "
+            f"{nl} launches {us_sep:7.3f} us")
+    del views, banks, base
+    return {"workload": ("synthetic W4A8 G=32 expert bank, 32 experts x 2048 rows, K = 4096, "
+                         "7 rotated copies; a fresh expert list per call"),
+            "per_call": out}
+
+
 def time_ablation(torch, sk, stream, host, xs, R, per):
     """The same step on the split path: (a) the weight left in the canonical
     layout (codes and scales read from their two regions), quantising in the
@@ -239,6 +288,8 @@ def main() -> int:
     ap.add_argument("--variants", action="store_true",
                     help="also time the other workloads (fused prologues, W6 / codebook / "
                          "lm_head formats, the 27B-class layer) and add them as `variants`")
+    ap.add_argument("--no-experts", action="store_true",
+                    help="skip the expert-bank workload")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the split-path comparison (canonical layout, separate quantisation)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -395,6 +446,10 @@ def main() -> int:
     if not args.no_ablation:
         ablation = time_ablation(torch, sk, stream, host, xs, R, per)
 
+    experts = None
+    if not args.no_experts:
+        experts = time_experts(torch, sk, S, stream)
+
     # ---------------- CPU baseline: the oracle on one step ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -448,6 +503,8 @@ def main() -> int:
     }
     if ablation is not None:
         out["ablation"] = ablation
+    if experts is not None:
+        out["experts"] = experts
     if variants is not None:
         out["variants"] = variants
     print(json.dumps(out), flush=True)
