@@ -165,3 +165,25 @@ def make_weight(fmt: int, n: int, k: int, g: int, seed_w: int, seed_s: int):
 def weight_bytes(fmt: int, n: int, k: int, g: int) -> int:
     """Size of the canonical buffer: N*K*bits/8 + N*(K/G)*4."""
     return n * k * BITS[fmt] // 8 + n * (k // g) * 4
+
+
+# ----------------------------------------------------------------------------
+# decode attention inputs
+# ----------------------------------------------------------------------------
+
+TENSOR_Q, TENSOR_K, TENSOR_V = 7, 8, 9
+
+
+def attention_inputs(seed: int, m: int, hq: int, hkv: int, length: int, d: int = 128,
+                     q_scale: float = 1.0):
+    """Query rows and a KV cache for grouped-query decode attention, as bf16 bits.
+
+    Returns ``(q, k, v)``: q ``[M, Hq, D]``, k and v ``[Hkv, L, D]`` (logical
+    order, one contiguous ``[L, D]`` matrix per KV head), each uint16 bfloat16
+    bits of N(0, 1) draws (q multiplied by ``q_scale`` first) rounded to
+    nearest-even.  Seeds: ``seed + 7`` (q), ``seed + 8`` (k), ``seed + 9`` (v).
+    """
+    q = _rng(seed + TENSOR_Q).standard_normal(size=(m, hq, d)).astype(np.float32) * np.float32(q_scale)
+    k = _rng(seed + TENSOR_K).standard_normal(size=(hkv, length, d)).astype(np.float32)
+    v = _rng(seed + TENSOR_V).standard_normal(size=(hkv, length, d)).astype(np.float32)
+    return to_bf16_bits(q), to_bf16_bits(k), to_bf16_bits(v)
