@@ -7,7 +7,9 @@ this module fails: there is no CPU path.
 
 Function names follow the C ABI: ``sk_repack_w4a8``, ``sk_unrepack_w4a8``,
 ``sk_gemm_w4a8``, ``sk_gemm_w6a8``, ``sk_gemm_fused_rmsnorm``,
-``sk_gemm_fused_swiglu``, ``sk_debug_gemm``.
+``sk_gemm_fused_swiglu``, ``sk_debug_gemm`` (include/sk_repack.h) and
+``sk_kv_append``, ``sk_decode_attention``, ``sk_kv_pack_host``
+(include/sk_attention.h).
 """
 
 from __future__ import annotations
@@ -35,7 +37,9 @@ EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4
            "sk_gemm_w4a8_canonical_q",
            "sk_debug_gemm",
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
-           "sk_test_set_spin_limit"]
+           "sk_test_set_spin_limit",
+           "sk_kv_append", "sk_decode_attention", "sk_kv_pack_host",
+           "sk_test_attention_plan", "sk_test_set_attention_split"]
 
 
 class SkWeightStruct(ctypes.Structure):
@@ -75,6 +79,11 @@ def _load() -> ctypes.CDLL:
         "sk_test_gemm_plan": ([I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_int64)], I),
         "sk_test_set_split": ([I], I),
         "sk_test_set_spin_limit": ([I], I),
+        "sk_kv_append": ([P, I, I, I, I, P, P, P], I),
+        "sk_decode_attention": ([P, I, I, I, P, I, I, F, P, P], I),
+        "sk_kv_pack_host": ([P, P, I, I, I, P], I),
+        "sk_test_attention_plan": ([I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)], I),
+        "sk_test_set_attention_split": ([I], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -278,3 +287,78 @@ def set_split(s: int) -> None:
 def set_spin_limit(polls: int) -> None:
     """Test hook: exchange polls before the local fallback (0 = default)."""
     _check(LIB.sk_test_set_spin_limit(polls), "sk_test_set_spin_limit")
+
+
+# ----------------------------------------------------------------------------
+# grouped-query decode attention over the tiled KV cache (include/sk_attention.h)
+# ----------------------------------------------------------------------------
+
+HEAD_DIM = 128
+KV_BLOCK = 32                 # cache entries per block
+KV_BLOCK_BYTES = 16384        # K tile + V tile of one block
+
+
+def kv_cache_bytes(hkv: int, cap: int) -> int:
+    """Size of a cache buffer for ``hkv`` KV heads and ``cap`` entries (cap % 32 == 0)."""
+    return hkv * (cap // KV_BLOCK) * KV_BLOCK_BYTES
+
+
+def _bf16_bits(t: torch.Tensor) -> torch.Tensor:
+    if t.dtype == torch.bfloat16:
+        return t
+    if t.dtype in (torch.uint16, torch.int16):
+        return t
+    raise ValueError(f"bfloat16 tensors (or their uint16 bits) expected, got {t.dtype}")
+
+
+def sk_kv_append(kv: torch.Tensor, hkv: int, cap: int, pos: int, k_new: torch.Tensor,
+                 v_new: torch.Tensor, stream=None) -> None:
+    """Write entries pos .. pos+T-1 of every KV head; k_new, v_new are [T, Hkv, 128] bf16."""
+    k_new, v_new = _bf16_bits(k_new), _bf16_bits(v_new)
+    if not (k_new.is_contiguous() and v_new.is_contiguous()) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must be contiguous [T, Hkv, 128] tensors of one shape")
+    t = k_new.shape[0] if k_new.dim() == 3 else -1
+    _check(LIB.sk_kv_append(_ptr(kv), hkv, cap, pos, t, _ptr(k_new), _ptr(v_new), _stream(stream)),
+           "sk_kv_append")
+
+
+def sk_decode_attention(q: torch.Tensor, hkv: int, kv: torch.Tensor, cap: int, length: int,
+                        scale: float | None = None, out=None, stream=None) -> torch.Tensor:
+    """O [M, Hq, 128] float32 for query rows q [M, Hq, 128] bf16 over the first ``length`` entries."""
+    q = _bf16_bits(q)
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [M, Hq, 128] tensor")
+    m, hq = q.shape[0], q.shape[1]
+    if q.shape[2] != HEAD_DIM:
+        raise ValueError("head dimension must be 128")
+    if scale is None:
+        scale = HEAD_DIM ** -0.5
+    if out is None:
+        out = torch.empty((m, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(LIB.sk_decode_attention(_ptr(q), m, hq, hkv, _ptr(kv), cap, length, ctypes.c_float(scale),
+                                   _ptr(out), _stream(stream)), "sk_decode_attention")
+    return out
+
+
+def sk_kv_pack_host(k, v, hkv: int, length: int, cap: int):
+    """Host packing of k, v ([Hkv, L, 128] uint16 bf16 bits, numpy) into the cache layout (numpy uint8)."""
+    import numpy as np
+    k = np.ascontiguousarray(k, dtype=np.uint16)
+    v = np.ascontiguousarray(v, dtype=np.uint16)
+    out = np.empty(kv_cache_bytes(hkv, cap), dtype=np.uint8)
+    _check(LIB.sk_kv_pack_host(k.ctypes.data, v.ctypes.data, hkv, length, cap, out.ctypes.data),
+           "sk_kv_pack_host")
+    return out
+
+
+def attention_plan(m: int, hq: int, hkv: int, length: int, cus: int = 256):
+    """(splits, blocks_per_split) the next sk_decode_attention with these sizes uses."""
+    sp, bps = ctypes.c_int(), ctypes.c_int()
+    _check(LIB.sk_test_attention_plan(m, hq, hkv, length, cus, ctypes.byref(sp), ctypes.byref(bps)),
+           "sk_test_attention_plan")
+    return sp.value, bps.value
+
+
+def set_attention_split(blocks_per_split: int) -> None:
+    """Test hook: force the blocks per prefix range (0 = planner)."""
+    _check(LIB.sk_test_set_attention_split(blocks_per_split), "sk_test_set_attention_split")
