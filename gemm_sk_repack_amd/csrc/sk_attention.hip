@@ -26,11 +26,14 @@
 // The score accumulator's lane layout (lane l holds query row l%16 and entries
 // 4*(l/16)+v) is exactly the B-operand layout of the second product, so P
 // never moves between lanes; the cache layout puts V's entries in that order.
-// The four waves' states are combined through LDS in wave order; with one
-// range the workgroup writes O, otherwise it writes its partial state, and
-// the last of the KV head's workgroups to arrive (one arrival counter per
-// head, release/acquire fences around it) combines the ranges in range order
-// and writes O.  Results do not depend on timing.
+// The four waves' states are combined through LDS in wave order.  With one
+// range the workgroup writes O.  Otherwise every workgroup counts itself on
+// its head's arrival counter when it starts, stores its partial state
+// write-through and publishes it by a release store of the launch's tag
+// (a generation number kept in the workspace) into its flag; the head's
+// last workgroup to start waits for all flags (acquire), combines the ranges
+// in range order and writes O, inside the same launch.  Results do not
+// depend on timing.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -49,44 +52,82 @@ constexpr int BLOCK_BYTES = 2 * BK * HD * 2;  // K tile + V tile, bf16
 constexpr int AW = 4;                         // waves per workgroup
 constexpr int AT = AW * 64;
 constexpr int kMaxRows = 64;                  // M * G
-constexpr int kMaxSplits = 128;
+constexpr int kMaxSplits = 64;
+constexpr int kSpin = 1 << 20;                // polls of one word before giving up (NaN)
 constexpr int PSTRIDE = HD + 2;               // floats per partial query row: O[128], max, sum
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr int kSC1 = 16;                      // cache policy: system-coherent (write-through) access
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
     const uint16_t* q;   // [M][Hq][128]
     const uint8_t* kv;   // cache, layout in sk_attention.h
     float* out;          // [M][Hq][128]
-    float* part;         // [Hkv][nsplit]{ O [RP][128], (max, sum) [RP][2] }
-    uint32_t* cnt;       // [Hkv]
-    int m, hq, g, r, len, nbc, nblk, bps, nsplit;
+    float* part;         // partial states: [Hkv][nsplit]{ O [RP][128], (max, sum) [RP][2] }
+    uint32_t* flag;      // [Hkv][nsplit] partial state published (the launch's tag)
+    uint32_t* hdr;       // [0] generation of the last multi-range launch, [1] workgroups done
+    uint32_t* cnt;       // [Hkv] arrivals
+    int m, hq, g, r, len, nbc, nblk, bps, nsplit, nwg, part_bytes;
     float sl2;           // scale * log2(e)
 };
 
-__device__ inline uint32_t bf16_rne(float f) {
-    // f is finite and >= 0 here (a softmax weight or its remainder)
-    const uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline uint32_t peek_gen(const uint32_t* hdr) {
+    return __hip_atomic_load(hdr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ inline bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+// Publishes a partial state.  Its data was stored write-through (sc1) and the
+// barrier before the call ordered every thread's stores before this one; the
+// release store then makes them visible at device scope before the flag
+// shows the launch's tag.
+__device__ inline void publish(uint32_t* flag, uint32_t tag) {
+    __hip_atomic_store(flag, tag, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polls a flag until it shows `tag`; the caller issues one acquire fence after
+// all its flags are seen.  The bound only guards against a hang (false then;
+// the caller writes NaN).
+__device__ inline bool await_flag(const uint32_t* flag, uint32_t tag) {
+    for (int it = 0; it < kSpin; ++it)
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag) return true;
+    return false;
+}
+
+// Write-through 16-byte store into the workspace (offset in bytes from its base).
+__device__ inline void wt_store(const __amdgpu_buffer_rsrc_t& ws, int off, float4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, v), ws, off, 0, kSC1);
+}
 
 template <int NQT>
 __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
     constexpr int RP = NQT * 16;              // query rows padded to whole tiles
-    // wave-state exchange: [t][dt*4+v][lane] output values, [t][lane] max and sum;
-    // reused by the final merge for the ranges' weights
-    __shared__ float xo[NQT * 32 * 64];
-    __shared__ float xm[NQT * 64], xl[NQT * 64];
-    __shared__ float den[RP];
+    constexpr int NSLOT = NQT == 1 ? 4 : (NQT == 2 ? 3 : 2);   // blocks held in registers
+    // dynamic LDS (smem below): the waves' states, [AW][NQT][34][64] floats,
+    // later reused by the merges
+    static_assert(AW * NQT * 34 * 64 >= 2 * kMaxSplits * RP, "merge scratch");
+    __shared__ float den[RP], dmx[RP];        // staging of a range's (max, sum) per row
     __shared__ int last;
 
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int g4 = lane >> 4, l16 = lane & 15;
     const int s = blockIdx.x, hk = blockIdx.y;
     const int M = a.m, G = a.g, R = a.r, L = a.len;
+    // this launch's tag: one more than the previous multi-range launch's
+    const uint32_t tag = a.nsplit > 1 ? peek_gen(a.hdr) + 1u : 0u;
+    // With several ranges, count this workgroup on its head's counter right
+    // away: the last to start merges, after its own loop, waiting for the
+    // others' published partial states.  Counting early keeps the atomics'
+    // round trip off the end of the launch.
+    uint32_t arrived = 0, done = 0;
+    if (a.nsplit > 1 && tid == 0) {
+        arrived = __hip_atomic_fetch_add(&a.cnt[hk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = __hip_atomic_fetch_add(&a.hdr[1], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 
     // 1. this lane's query rows (B operand: row t*16 + l16, dims 32c + 8*g4 + e)
     uint4 qv[NQT][4];
@@ -107,17 +148,20 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         }
     }
 
-    // 2. this wave's blocks: b0 + wv, b0 + wv + 4, ... below b1.  Loads go
-    //    through a buffer resource covering exactly this range, so the
-    //    pipeline's look-ahead loads past the range return zeros without
-    //    touching memory and every wave issues the same, static load pattern.
+    // 2. this wave's blocks: b0 + wv, b0 + wv + 4, ... below b1.  The main
+    //    loop takes the range's whole blocks (below nfull = L / 32) through a
+    //    buffer resource covering exactly them, so the pipeline's look-ahead
+    //    loads past them return zeros without touching memory and every wave
+    //    issues the same, static load pattern; a final partial block is done
+    //    after the loop by the wave that owns it.
     const int wu = __builtin_amdgcn_readfirstlane(wv);
     const int b0 = s * a.bps;
     const int b1 = min(b0 + a.bps, a.nblk);
-    const int nw = (b1 - b0 > wu) ? (b1 - b0 - wu + AW - 1) / AW : 0;
-    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(a.kv + ((size_t)hk * a.nbc + b0) * BLOCK_BYTES), (short)0,
-        (b1 - b0) * BLOCK_BYTES, 0x00020000);
+    const int bfull = min(b1, L / BK);
+    const int nw = (bfull - b0 > wu) ? (bfull - b0 - wu + AW - 1) / AW : 0;
+    uint8_t* const rbase = const_cast<uint8_t*>(a.kv + ((size_t)hk * a.nbc + b0) * BLOCK_BYTES);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(rbase, (short)0, max(bfull - b0, 0) * BLOCK_BYTES, 0x00020000);
 
     float mrun[NQT], lrun[NQT];
     v4f o[NQT][8];
@@ -129,42 +173,28 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         for (int dt = 0; dt < 8; ++dt) o[t][dt] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    auto load = [&](uint4 (&kb)[8], uint4 (&vb)[8], int i) {
+    auto load = [&](uint4 (&kb)[8], uint4 (&vb)[8], const __amdgpu_buffer_rsrc_t& rs, int i) {
         const int off = (wu + AW * i) * BLOCK_BYTES + lane * 16;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            kb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + j * 1024, 0, 0));
+            kb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + j * 1024, 0, 0));
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            vb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, off + 8192 + j * 1024, 0, 0));
+            vb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 8192 + j * 1024, 0, 0));
     };
 
-    auto compute = [&](const uint4 (&kb)[8], const uint4 (&vin)[8], int i) {
-        const int blk = b0 + wu + AW * i;
-        const int key0 = blk * BK + 4 * g4;
-        uint4 vb[8];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) vb[dt] = vin[dt];
-        if (blk * BK + BK > L) {
-            // the prefix ends inside this block: entries at or past L may hold
-            // anything (0 * Inf would be NaN), so their V values become zero
-            const int nv = L - blk * BK;      // valid entries, 1..31
-            uint32_t km[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int e0 = 2 * j, e1 = 2 * j + 1;
-                const int k0 = e0 < 4 ? 4 * g4 + e0 : 16 + 4 * g4 + e0 - 4;
-                const int k1 = e1 < 4 ? 4 * g4 + e1 : 16 + 4 * g4 + e1 - 4;
-                km[j] = (k0 < nv ? 0x0000FFFFu : 0u) | (k1 < nv ? 0xFFFF0000u : 0u);
-            }
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                vb[dt].x &= km[0];
-                vb[dt].y &= km[1];
-                vb[dt].z &= km[2];
-                vb[dt].w &= km[3];
-            }
-        }
+    // Max over the four lanes of a query row (lanes l, l^16, l^32, l^48).
+    auto rowmax = [](float v) {
+        const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = fmaxf(__uint_as_float(a16[0]), __uint_as_float(a16[1]));
+        const auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        return fmaxf(__uint_as_float(a32[0]), __uint_as_float(a32[1]));
+    };
+
+    // One block: i-th of this wave; `ok` false makes every score -inf (a
+    // look-ahead slot past the range, whose K and V read as zeros).
+    auto compute = [&](const uint4 (&kb)[8], const uint4 (&vb)[8], int i, bool ok) {
+        const int key0 = (b0 + wu + AW * i) * BK + 4 * g4;
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
             v4f s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = s0;
@@ -176,31 +206,34 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
             float x[8];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                x[v] = (key0 + v <= lim[t]) ? s0[v] * a.sl2 : -INFINITY;
-                x[4 + v] = (key0 + 16 + v <= lim[t]) ? s1[v] * a.sl2 : -INFINITY;
+                x[v] = (ok && key0 + v <= lim[t]) ? s0[v] * a.sl2 : -INFINITY;
+                x[4 + v] = (ok && key0 + 16 + v <= lim[t]) ? s1[v] * a.sl2 : -INFINITY;
             }
-            float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mx = rowmax(fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))));
             const float mnew = fmaxf(mrun[t], mx);
             const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
             const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mu);
             mrun[t] = mnew;
-            uint32_t hb[8], lb[8];
+            // P = hi + lo, both bf16 (round to nearest even): hi = bf16(p),
+            // lo = bf16(p - hi), where p - hi is exact in fp32
+            uint32_t ph2[4], pl2[4];
             float ps = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float p = __builtin_amdgcn_exp2f(x[j] - mu);
-                ps += p;
-                hb[j] = bf16_rne(p);
-                lb[j] = bf16_rne(p - __uint_as_float(hb[j] << 16));
+            for (int j = 0; j < 4; ++j) {
+                const float p0 = __builtin_amdgcn_exp2f(x[2 * j] - mu);
+                const float p1 = __builtin_amdgcn_exp2f(x[2 * j + 1] - mu);
+                ps += p0;
+                ps += p1;
+                const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+                const float r0 = p0 - __uint_as_float(h << 16);
+                const float r1 = p1 - __uint_as_float(h & 0xFFFF0000u);
+                ph2[j] = h;
+                pl2[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
             }
             lrun[t] = lrun[t] * alpha + ps;
-            const uint4 ph = make_uint4(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16),
-                                        hb[4] | (hb[5] << 16), hb[6] | (hb[7] << 16));
-            const uint4 pl = make_uint4(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16),
-                                        lb[4] | (lb[5] << 16), lb[6] | (lb[7] << 16));
+            const uint4 ph = make_uint4(ph2[0], ph2[1], ph2[2], ph2[3]);
+            const uint4 pl = make_uint4(pl2[0], pl2[1], pl2[2], pl2[3]);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 o[t][dt] *= alpha;
@@ -210,147 +243,255 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         }
     };
 
-    // 3. the wave's blocks, two register slots: the next block's loads are in
-    //    flight while a block is computed
+    // 3. the wave's blocks through NSLOT register slots: while a block is
+    //    computed, the next NSLOT-1 blocks' loads are in flight.  The body is
+    //    branch-free so that consecutive blocks' instructions interleave.
     if (nw > 0) {
-        uint4 k0[8], v0[8], k1[8], v1[8];
-        load(k0, v0, 0);
-        load(k1, v1, 1);
-        for (int i = 0; i < nw; i += 2) {
-            compute(k0, v0, i);
-            load(k0, v0, i + 2);
-            if (i + 1 < nw) compute(k1, v1, i + 1);
-            load(k1, v1, i + 3);
+        uint4 kb[NSLOT][8], vb[NSLOT][8];
+#pragma unroll
+        for (int u = 0; u < NSLOT; ++u) load(kb[u], vb[u], rsrc, u);
+        for (int i = 0; i < nw; i += NSLOT) {
+#pragma unroll
+            for (int u = 0; u < NSLOT; ++u) {
+                compute(kb[u], vb[u], i + u, i + u < nw);
+                load(kb[u], vb[u], rsrc, i + u + NSLOT);
+            }
         }
+    }
+    // the prefix's final partial block, if this range holds it: entries at or
+    // past L may hold anything (0 * Inf would be NaN), so their V values are
+    // zeroed before the product
+    if (bfull < b1 && ((bfull - b0) & (AW - 1)) == wu) {
+        const int it = (bfull - b0) / AW;          // this wave's index of the block
+        const __amdgpu_buffer_rsrc_t rt =
+            __builtin_amdgcn_make_buffer_rsrc(rbase, (short)0, (b1 - b0) * BLOCK_BYTES, 0x00020000);
+        uint4 kb[8], vb[8];
+        load(kb, vb, rt, it);
+        const int nv = L - bfull * BK;             // valid entries, 1..31
+        uint32_t km[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e0 = 2 * j, e1 = 2 * j + 1;
+            const int k0 = e0 < 4 ? 4 * g4 + e0 : 16 + 4 * g4 + e0 - 4;
+            const int k1 = e1 < 4 ? 4 * g4 + e1 : 16 + 4 * g4 + e1 - 4;
+            km[j] = (k0 < nv ? 0x0000FFFFu : 0u) | (k1 < nv ? 0xFFFF0000u : 0u);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            vb[dt].x &= km[0];
+            vb[dt].y &= km[1];
+            vb[dt].z &= km[2];
+            vb[dt].w &= km[3];
+        }
+        compute(kb, vb, it, true);
     }
 #pragma unroll
     for (int t = 0; t < NQT; ++t) {
-        lrun[t] += __shfl_xor(lrun[t], 16);
-        lrun[t] += __shfl_xor(lrun[t], 32);
+        const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrun[t]), __float_as_uint(lrun[t]), false, false);
+        const float l2 = __uint_as_float(a16[0]) + __uint_as_float(a16[1]);
+        const auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(l2), __float_as_uint(l2), false, false);
+        lrun[t] = __uint_as_float(a32[0]) + __uint_as_float(a32[1]);
     }
 
-    // 4. combine the waves' states in wave order (wave 0 accumulates)
-    for (int src = 1; src < AW; ++src) {
-        if (wv == src) {
+    // 4. combine the four waves' states: every wave parks its state in LDS,
+    //    then each thread combines 8 of its lane's 32 output values over the
+    //    waves (wave w takes values 8w .. 8w+7: dims 16*(2w + k/4) + 4*g4 + k%4,
+    //    k = 0..7), always in wave order
+    extern __shared__ float smem[];
+    constexpr int SW = 34 * 64;               // floats per (wave, query tile) state
 #pragma unroll
-            for (int t = 0; t < NQT; ++t) {
-                xm[t * 64 + lane] = mrun[t];
-                xl[t * 64 + lane] = lrun[t];
+    for (int t = 0; t < NQT; ++t) {
+        float* st = smem + (wv * NQT + t) * SW + lane;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
+        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) xo[(t * 32 + dt * 4 + v) * 64 + lane] = o[t][dt][v];
-            }
+            for (int v = 0; v < 4; ++v) st[(dt * 4 + v) * 64] = o[t][dt][v];
+        st[32 * 64] = mrun[t];
+        st[33 * 64] = lrun[t];
+    }
+    if (a.nsplit > 1 && tid == 0) {
+        const int lst = arrived == (uint32_t)(a.nsplit - 1);
+        if (lst) __hip_atomic_store(&a.cnt[hk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = lst;
+        // generation bookkeeping: after every workgroup of the launch has read
+        // the generation (each did so before counting itself), the last one
+        // publishes this launch's tag for the next launch
+        if (done == (uint32_t)(a.nwg - 1)) {
+            __hip_atomic_store(&a.hdr[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.hdr[0], tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        __syncthreads();
-        if (wv == 0) {
+    }
+    __syncthreads();
+    float cm[NQT], cl[NQT], cv[NQT][8];
 #pragma unroll
-            for (int t = 0; t < NQT; ++t) {
-                const float mb = xm[t * 64 + lane], lb = xl[t * 64 + lane];
-                const float mn = fmaxf(mrun[t], mb);
-                const float mu = (mn == -INFINITY) ? 0.0f : mn;
-                const float wa = __builtin_amdgcn_exp2f(mrun[t] - mu);
-                const float wb = __builtin_amdgcn_exp2f(mb - mu);
-                mrun[t] = mn;
-                lrun[t] = __builtin_fmaf(lb, wb, lrun[t] * wa);
+    for (int t = 0; t < NQT; ++t) {
+        float mw[AW], ww[AW];
+        float mx = -INFINITY;
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        o[t][dt][v] = __builtin_fmaf(xo[(t * 32 + dt * 4 + v) * 64 + lane], wb, o[t][dt][v] * wa);
-            }
+        for (int w = 0; w < AW; ++w) {
+            mw[w] = smem[(w * NQT + t) * SW + 32 * 64 + lane];
+            mx = fmaxf(mx, mw[w]);
         }
-        __syncthreads();
+        const float mu = (mx == -INFINITY) ? 0.0f : mx;
+        float l = 0.0f;
+#pragma unroll
+        for (int w = 0; w < AW; ++w) {
+            ww[w] = __builtin_amdgcn_exp2f(mw[w] - mu);
+            l = __builtin_fmaf(smem[(w * NQT + t) * SW + 33 * 64 + lane], ww[w], l);
+        }
+        cm[t] = mx;
+        cl[t] = l;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < AW; ++w) acc = __builtin_fmaf(smem[(w * NQT + t) * SW + (8 * wv + k) * 64 + lane], ww[w], acc);
+            cv[t][k] = acc;
+        }
     }
 
-    // 5. one range: write O.  Otherwise store the partial state; the last
-    //    workgroup of this head to arrive merges.
+    // 5. one range: write O.
     if (a.nsplit == 1) {
-        if (wv == 0) {
 #pragma unroll
-            for (int t = 0; t < NQT; ++t) {
-                const int r = t * 16 + l16;
-                if (r < R) {
-                    const int mm = r / G, hg = r - mm * G;
-                    const float inv = 1.0f / lrun[t];
-                    float* op = a.out + (size_t)(mm * a.hq + hk * G + hg) * HD + 4 * g4;
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
-                        *reinterpret_cast<float4*>(op + dt * 16) =
-                            make_float4(o[t][dt][0] * inv, o[t][dt][1] * inv, o[t][dt][2] * inv, o[t][dt][3] * inv);
-                }
+        for (int t = 0; t < NQT; ++t) {
+            const int r = t * 16 + l16;
+            if (r < R) {
+                const int mm = r / G, hg = r - mm * G;
+                const float inv = 1.0f / cl[t];
+                float* op = a.out + (size_t)(mm * a.hq + hk * G + hg) * HD + 4 * g4 + 32 * wv;
+                *reinterpret_cast<float4*>(op) =
+                    make_float4(cv[t][0] * inv, cv[t][1] * inv, cv[t][2] * inv, cv[t][3] * inv);
+                *reinterpret_cast<float4*>(op + 16) =
+                    make_float4(cv[t][4] * inv, cv[t][5] * inv, cv[t][6] * inv, cv[t][7] * inv);
             }
         }
         return;
     }
 
-    // this head's partials: per range, O [RP][128] then (max, sum) [RP][2]
+    //    Otherwise store the partial state, O [RP][128] then (max, sum)
+    //    [RP][2] per range, and publish it with the launch's tag.  Workgroups
+    //    other than the head's merger are then done.
     constexpr int CH = RP * PSTRIDE;
-    float* const hpart = a.part + (size_t)hk * a.nsplit * CH;
-    if (wv == 0) {
+    float* const p0 = a.part + ((size_t)hk * a.nsplit) * CH;        // [nsplit][CH]
+    const __amdgpu_buffer_rsrc_t wsr = __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+    {
+        const int mine = (int)((p0 - a.part) + (size_t)s * CH);         // float offset
 #pragma unroll
         for (int t = 0; t < NQT; ++t) {
             const int r = t * 16 + l16;
             if (r < R) {
-                float* pp = hpart + (size_t)s * CH + r * HD + 4 * g4;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-                    *reinterpret_cast<float4*>(pp + dt * 16) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
-                if (g4 == 0)
-                    *reinterpret_cast<float2*>(hpart + (size_t)s * CH + RP * HD + 2 * r) = make_float2(mrun[t], lrun[t]);
+                const int pp = mine + r * HD + 4 * g4 + 32 * wv;
+                wt_store(wsr, 4 * pp, make_float4(cv[t][0], cv[t][1], cv[t][2], cv[t][3]));
+                wt_store(wsr, 4 * (pp + 16), make_float4(cv[t][4], cv[t][5], cv[t][6], cv[t][7]));
             }
         }
-        __threadfence();                      // release: the partial before the arrival
-        if (lane == 0) {
-            const uint32_t old = __hip_atomic_fetch_add(&a.cnt[hk], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const int lst = old == (uint32_t)(a.nsplit - 1);
-            if (lst) __hip_atomic_store(&a.cnt[hk], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            last = lst;
+        // (max, sum) of rows 2j and 2j+1 as one 16-byte store: row r's pair
+        // sits in lane l16 = r of wave 0 (g4 = 0); gather it via LDS
+        if (wv == 0 && g4 == 0) {
+#pragma unroll
+            for (int t = 0; t < NQT; ++t) {
+                dmx[t * 16 + l16] = cm[t];
+                den[t * 16 + l16] = cl[t];
+            }
         }
     }
     __syncthreads();
+    if (tid < (R + 1) / 2) {
+        const int r = 2 * tid;
+        const int mine = (int)((p0 - a.part) + (size_t)s * CH);
+        wt_store(wsr, 4 * (mine + RP * HD + 2 * r), make_float4(dmx[r], den[r], dmx[r + 1], den[r + 1]));
+    }
+    __syncthreads();
+    if (tid == 0) publish(&a.flag[(size_t)hk * a.nsplit + s], tag);
     if (!last) return;
-    __threadfence();                          // acquire: every range's partial is visible
 
-    // 6. merge the ranges in range order: weights exp2(max_s - max) per (range, row)
-    float* const wts = xo;                    // [nsplit][RP]
-    if (tid < R) {
-        float mx = -INFINITY;
-        for (int q = 0; q < a.nsplit; ++q) mx = fmaxf(mx, hpart[(size_t)q * CH + RP * HD + 2 * tid]);
-        float d = 0.0f;
-        for (int q = 0; q < a.nsplit; ++q) {
-            const float2 ml = *reinterpret_cast<const float2*>(hpart + (size_t)q * CH + RP * HD + 2 * tid);
-            const float w = __builtin_amdgcn_exp2f(ml.x - mx);
-            wts[q * RP + tid] = w;
-            d = __builtin_fmaf(ml.y, w, d);
+    // 6. merge (the head's last workgroup to start): wait until every range's
+    //    state is published, then per row the max over the ranges, weights
+    //    exp2(max_q - max), and every (row, dim) as the weighted sum in range
+    //    order, divided by the weighted sum of the ranges' sums.
+    float* const wq = smem;                   // [n][RP] maxima (LDS reused)
+    float* const lq = smem + kMaxSplits * RP; // [n][RP] sums
+    __shared__ int okf;
+    auto merge = [&](const float* src, const uint32_t* flags, int n) {
+        if (tid == 0) okf = 1;
+        __syncthreads();
+        if (tid < n) {
+            if (!await_flag(&flags[tid], tag)) okf = 0;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-        den[tid] = 1.0f / d;
-    }
-    __syncthreads();
-    for (int it = tid; it < R * (HD / 4); it += AT) {
-        const int r = it / (HD / 4), d4 = it - r * (HD / 4);
-        const float* pp = hpart + (size_t)r * HD + 4 * d4;
-        float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        auto add = [&](const float4 v, const float w) {
-            acc.x = __builtin_fmaf(v.x, w, acc.x);
-            acc.y = __builtin_fmaf(v.y, w, acc.y);
-            acc.z = __builtin_fmaf(v.z, w, acc.z);
-            acc.w = __builtin_fmaf(v.w, w, acc.w);
+        __syncthreads();
+        const float bad = okf ? 0.0f : __builtin_nanf("");
+        // Each thread owns E4 float4 items (row, 4 dims).  The first batch of
+        // partial outputs is loaded before the (max, sum) pass so that both
+        // round trips overlap; every thread then derives its rows' weights
+        // from the (max, sum) values in LDS.
+        constexpr int E4 = RP * HD / 4 / AT;
+        constexpr int QB = 64 / E4;           // partials per batch: 64 float4 in flight
+        float4 acc[E4], v[QB][E4];
+        float mu[E4], den_e[E4];
+#pragma unroll
+        for (int e = 0; e < E4; ++e) {
+            acc[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            den_e[e] = 0.0f;
+        }
+        auto fetch = [&](int q0) {
+#pragma unroll
+            for (int u = 0; u < QB; ++u)
+#pragma unroll
+                for (int e = 0; e < E4; ++e) {
+                    const int i4 = tid + e * AT;
+                    v[u][e] = (q0 + u < n && i4 * 4 < R * HD)
+                                  ? *reinterpret_cast<const float4*>(src + (size_t)(q0 + u) * CH + 4 * i4)
+                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                }
         };
-        int q = 0;
-        for (; q + 4 <= a.nsplit; q += 4) {
-            float4 v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4*>(pp + (size_t)(q + u) * CH);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) add(v[u], wts[(q + u) * RP + r]);
+        fetch(0);
+        for (int idx = tid; idx < n * R; idx += AT) {
+            const int q = idx / R, r = idx - q * R;
+            const float2 ml = *reinterpret_cast<const float2*>(src + (size_t)q * CH + RP * HD + 2 * r);
+            wq[q * RP + r] = ml.x;
+            lq[q * RP + r] = ml.y;
         }
-        for (; q < a.nsplit; ++q) add(*reinterpret_cast<const float4*>(pp + (size_t)q * CH), wts[q * RP + r]);
-        const int mm = r / G, hg = r - mm * G;
-        const float dn = den[r];
-        *reinterpret_cast<float4*>(a.out + (size_t)(mm * a.hq + hk * G + hg) * HD + 4 * d4) =
-            make_float4(acc.x * dn, acc.y * dn, acc.z * dn, acc.w * dn);
-    }
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E4; ++e) {
+            const int r = min((tid + e * AT) * 4 / HD, RP - 1);
+            float mx = -INFINITY;
+            for (int q = 0; q < n; ++q) mx = fmaxf(mx, wq[q * RP + r]);
+            mu[e] = mx;
+        }
+        for (int q0 = 0; q0 < n; q0 += QB) {
+            if (q0 > 0) fetch(q0);
+#pragma unroll
+            for (int u = 0; u < QB; ++u)
+#pragma unroll
+                for (int e = 0; e < E4; ++e) {
+                    if (q0 + u < n) {
+                        const int r = min((tid + e * AT) * 4 / HD, RP - 1);
+                        const float m0 = (mu[e] == -INFINITY) ? 0.0f : mu[e];
+                        const float w = __builtin_amdgcn_exp2f(wq[(q0 + u) * RP + r] - m0);
+                        den_e[e] = __builtin_fmaf(lq[(q0 + u) * RP + r], w, den_e[e]);
+                        acc[e].x = __builtin_fmaf(v[u][e].x, w, acc[e].x);
+                        acc[e].y = __builtin_fmaf(v[u][e].y, w, acc[e].y);
+                        acc[e].z = __builtin_fmaf(v[u][e].z, w, acc[e].z);
+                        acc[e].w = __builtin_fmaf(v[u][e].w, w, acc[e].w);
+                    }
+                }
+        }
+#pragma unroll
+        for (int e = 0; e < E4; ++e) {
+            const int i4 = tid + e * AT;
+            if (i4 * 4 < R * HD) {
+                const int r = (4 * i4) / HD, d = 4 * i4 - r * HD;
+                const int mm = r / G, hg = r - mm * G;
+                const float inv = 1.0f / (den_e[e] + bad);
+                *reinterpret_cast<float4*>(a.out + (size_t)(mm * a.hq + hk * G + hg) * HD + d) =
+                    make_float4(acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv);
+            }
+        }
+    };
+
+    merge(p0, a.flag + (size_t)hk * a.nsplit, a.nsplit);
 }
 
 // Append t entries: one thread per (entry, head, 8 dimensions).
@@ -398,10 +539,11 @@ Plan make_plan(int m, int hq, int hkv, int len, int cus) {
     if (g_bps_override > 0) {
         bps = g_bps_override;
     } else {
-        // about two workgroups per compute unit over all heads, at least one
+        // about one workgroup per two compute units over all heads: a
+        // workgroup streams at most ~60 GB/s, so half the units already reach
+        // the HBM rate, and fewer ranges keep the merge short; at least one
         // block per wave
-        const int target = 2 * (cus > 0 ? cus : 256);
-        const int per_head = (target + hkv - 1) / hkv;
+        const int per_head = ((cus > 0 ? cus : 256) / 2 + hkv - 1) / hkv;
         bps = (p.nblk + per_head - 1) / per_head;
         if (bps < AW) bps = AW;
     }
@@ -414,12 +556,19 @@ Plan make_plan(int m, int hq, int hkv, int len, int cus) {
 
 struct DevState {
     int cus = 0;
-    void* ws = nullptr;        // [cnt: cap_h uint32, padded to 256 B][part: cap_part floats]
+    // [hdr: 256 B][cnt: cap_h][flag: cap_h*kMaxSplits] (u32, padded to 256 B)
+    // [part: cap_part floats]
+    void* ws = nullptr;
     int cap_h = 0;
     size_t cap_part = 0;
+    bool lds_set[5] = {false, false, false, false, false};
 };
 std::mutex g_mu;
 DevState g_dev[64];
+
+size_t counters_bytes(int cap_h) {
+    return ((size_t)cap_h * (1 + kMaxSplits) * 4 + 255) / 256 * 256;
+}
 
 hipError_t device_cus(int dev, int& cus) {
     DevState& ds = g_dev[dev];
@@ -443,21 +592,21 @@ hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const voi
     e = device_cus(dev, cus);
     if (e != hipSuccess) return e;
     const Plan p = make_plan(m, hq, hkv, len, cus);
-    const size_t part_floats = p.nsplit > 1 ? (size_t)hkv * p.nsplit * p.nqt * 16 * PSTRIDE : 0;
+    constexpr int kChunk = PSTRIDE * 16;      // floats of one partial state per query tile
+    const size_t part_words = p.nsplit > 1 ? (size_t)hkv * p.nsplit * p.nqt * kChunk : 0;
     DevState& ds = g_dev[dev];
     {
         std::lock_guard<std::mutex> lk(g_mu);
-        if (!ds.ws || ds.cap_h < hkv || ds.cap_part < part_floats) {
+        if (!ds.ws || ds.cap_h < hkv || ds.cap_part < part_words) {
             const int cap_h = ds.cap_h > hkv ? ds.cap_h : (hkv > 64 ? hkv : 64);
-            const size_t cap_part = ds.cap_part > part_floats ? ds.cap_part : part_floats;
+            const size_t cap_part = ds.cap_part > part_words ? ds.cap_part : part_words;
             if (ds.ws) {
                 e = hipDeviceSynchronize();
                 if (e != hipSuccess) return e;
                 (void)hipFree(ds.ws);
                 ds.ws = nullptr;
             }
-            const size_t cnt_bytes = ((size_t)cap_h * 4 + 255) / 256 * 256;
-            const size_t bytes = cnt_bytes + cap_part * 4;
+            const size_t bytes = 256 + counters_bytes(cap_h) + cap_part * 4;
             e = hipMalloc(&ds.ws, bytes);
             if (e != hipSuccess) return e;
             e = hipMemset(ds.ws, 0, bytes);
@@ -468,12 +617,15 @@ hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const voi
             ds.cap_part = cap_part;
         }
     }
+    uint8_t* const wsb = static_cast<uint8_t*>(ds.ws);
     AttnArgs a;
     a.q = q;
     a.kv = static_cast<const uint8_t*>(kv);
     a.out = out;
-    a.cnt = static_cast<uint32_t*>(ds.ws);
-    a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ds.ws) + ((size_t)ds.cap_h * 4 + 255) / 256 * 256);
+    a.hdr = reinterpret_cast<uint32_t*>(wsb);
+    a.cnt = reinterpret_cast<uint32_t*>(wsb + 256);
+    a.flag = a.cnt + ds.cap_h;
+    a.part = reinterpret_cast<float*>(wsb + 256 + counters_bytes(ds.cap_h));
     a.m = m;
     a.hq = hq;
     a.g = hq / hkv;
@@ -483,6 +635,8 @@ hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const voi
     a.nblk = p.nblk;
     a.bps = p.bps;
     a.nsplit = p.nsplit;
+    a.part_bytes = (int)(ds.cap_part * 4);
+    a.nwg = p.nsplit * hkv;
     a.sl2 = scale * 1.4426950408889634f;
     void (*fn)(AttnArgs) = nullptr;
     switch (p.nqt) {
@@ -492,7 +646,14 @@ hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const voi
         case 4: fn = attn_kernel<4>; break;
         default: return hipErrorInvalidValue;
     }
-    hipLaunchKernelGGL(fn, dim3((unsigned)p.nsplit, (unsigned)hkv), dim3(AT), 0, st, a);
+    const size_t lds = (size_t)AW * p.nqt * 34 * 64 * 4;
+    if (lds > 64 * 1024 && !ds.lds_set[p.nqt]) {
+        e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+        if (e != hipSuccess) return e;
+        ds.lds_set[p.nqt] = true;
+    }
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.nsplit, (unsigned)hkv), dim3(AT), lds, st, a);
     return hipGetLastError();
 }
 

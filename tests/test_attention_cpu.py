@@ -111,10 +111,10 @@ def test_pack_host_validation():
 def test_plan_covers_the_prefix(m, hq, hkv, length, cus):
     splits, bps = sk.attention_plan(m, hq, hkv, length, cus)
     nblk = -(-length // 32)
-    assert 1 <= splits <= 128
+    assert 1 <= splits <= 64
     assert 1 <= bps <= nblk
     assert splits * bps >= nblk and (splits - 1) * bps < nblk     # every range non-empty
-    assert bps >= min(4, nblk) or splits == 128                    # a block per wave at least
+    assert bps >= min(4, nblk) or splits == 64                     # a block per wave at least
 
 
 def test_split_override():

@@ -87,7 +87,8 @@ def test_parity_planner(m, hq, hkv, length):
 
 
 @pytest.mark.parametrize("bps", [1, 2, 3, 5, 8, 1000])
-@pytest.mark.parametrize("m,hq,hkv,length", [(1, 32, 8, 777), (8, 32, 8, 777), (6, 30, 6, 250)])
+@pytest.mark.parametrize("m,hq,hkv,length", [(1, 32, 8, 777), (8, 32, 8, 777), (6, 30, 6, 250),
+                                              (4, 16, 2, 2048), (8, 40, 8, 1100), (8, 64, 8, 1500)])
 def test_parity_forced_splits(m, hq, hkv, length, bps):
     cap = roundup(length, 32)
     qb, kb, vb = S.attention_inputs(2000 + m + length, m, hq, hkv, length)
@@ -95,10 +96,11 @@ def test_parity_forced_splits(m, hq, hkv, length, bps):
     assert_attn_close(run(qb, kv, hkv, cap, length, bps), qb, kb, vb)
 
 
-@pytest.mark.parametrize("q_scale", [4.0, 12.0])
+@pytest.mark.parametrize("q_scale", [4.0, 12.0, 30.0])
 def test_peaked_scores(q_scale):
-    """Scores with a spread of tens: the running maximum moves often and the
-    rescaling decides the result."""
+    """Scores with a spread of tens to hundreds (log2 units): the running
+    maximum moves often and the rescaling decides the result; a reference
+    that is not the true row maximum would overflow exp2 here."""
     m, hq, hkv, length = 8, 16, 4, 700
     cap = roundup(length, 32)
     qb, kb, vb = S.attention_inputs(3100, m, hq, hkv, length, q_scale=q_scale)
