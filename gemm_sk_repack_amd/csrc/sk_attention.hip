@@ -543,7 +543,7 @@ Plan make_plan(int m, int hq, int hkv, int len, int cus) {
         // workgroup streams at most ~60 GB/s, so half the units already reach
         // the HBM rate, and fewer ranges keep the merge short; at least one
         // block per wave
-        const int per_head = ((cus > 0 ? cus : 256) / 2 + hkv - 1) / hkv;
+        const int per_head = max(1, ((cus > 0 ? cus : 256) / 2 + hkv - 1) / hkv);
         bps = (p.nblk + per_head - 1) / per_head;
         if (bps < AW) bps = AW;
     }
