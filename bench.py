@@ -144,6 +144,41 @@ def time_experts(torch, sk, S, stream):
             "per_call": out}
 
 
+def time_attention(torch, sk, S, stream):
+    """Grouped-query decode attention of the 9B-class layer (synthetic): Hq 32,
+    Hkv 8, head dim 128, bf16 KV cache in the library's tiled layout, prefix L
+    in {4096, 16384, 32768}, M = 1 and M = 8 verification rows.  Rotated cache
+    copies (>= 1 GiB in total) so every call streams from HBM; µs per call
+    from graphs; GB/s over the algorithmic bytes (the prefix's K and V, q, O)."""
+    dev = torch.device("cuda:0")
+    hq, hkv, d = 32, 8, 128
+    out = []
+    for length in (4096, 16384, 32768):
+        _, kb, vb = S.attention_inputs(S.seed_of(6, 0, 0), 1, hq, hkv, length)
+        base = torch.from_numpy(sk.sk_kv_pack_host(kb, vb, hkv, length, length)).to(dev)
+        R = max(2, (1 << 30) // base.numel())
+        caches = [base] + [base.clone() for _ in range(R - 1)]
+        kv_bytes = 2 * hkv * length * d * 2
+        for m in (1, 8):
+            qb, _, _ = S.attention_inputs(S.seed_of(6, m, 0), m, hq, hkv, 1)
+            q = torch.from_numpy(qb.view(np.int16)).to(dev)
+            o = torch.empty((m, hq, d), dtype=torch.float32, device=dev)
+            us = time_graph(torch, stream,
+                            lambda i: sk.sk_decode_attention(q, hkv, caches[i % R], length, length, out=o),
+                            4 * R)
+            b = kv_bytes + m * hq * d * (2 + 4)
+            splits, bps = sk.attention_plan(m, hq, hkv, length)
+            out.append({"L": length, "m": m, "us_per_call": round(us, 3),
+                        "GBps": round(b / (us * 1e-6) / 1e9, 1), "ranges_per_head": splits,
+                        "blocks_per_range": bps})
+            log(f"attention L={length} M={m}: {us:7.3f} us ({out[-1]['GBps']} GB/s), "
+                f"{splits} ranges x {bps} blocks per head")
+        del caches, base
+    return {"workload": ("synthetic 9B-class GQA decode attention: Hq 32, Hkv 8, head dim 128, "
+                         "bf16 KV cache (tiled), causal verification rows; rotated cache copies"),
+            "per_call": out}
+
+
 def time_ablation(torch, sk, stream, host, xs, R, per):
     """The same step on the split path: (a) the weight left in the canonical
     layout (codes and scales read from their two regions), quantising in the
@@ -290,6 +325,8 @@ def main() -> int:
                          "lm_head formats, the 27B-class layer) and add them as `variants`")
     ap.add_argument("--no-experts", action="store_true",
                     help="skip the expert-bank workload")
+    ap.add_argument("--no-attention", action="store_true",
+                    help="skip the decode-attention workload")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the split-path comparison (canonical layout, separate quantisation)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -450,6 +487,10 @@ def main() -> int:
     if not args.no_experts:
         experts = time_experts(torch, sk, S, stream)
 
+    attention = None
+    if not args.no_attention:
+        attention = time_attention(torch, sk, S, stream)
+
     # ---------------- CPU baseline: the oracle on one step ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -505,6 +546,8 @@ def main() -> int:
         out["ablation"] = ablation
     if experts is not None:
         out["experts"] = experts
+    if attention is not None:
+        out["attention"] = attention
     if variants is not None:
         out["variants"] = variants
     print(json.dumps(out), flush=True)

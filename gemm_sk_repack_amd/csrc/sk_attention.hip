@@ -410,7 +410,7 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
     //    exp2(max_q - max), and every (row, dim) as the weighted sum in range
     //    order, divided by the weighted sum of the ranges' sums.
     float* const wq = smem;                   // [n][RP] maxima (LDS reused)
-    float* const lq = smem + kMaxSplits * RP; // [n][RP] sums
+    float* const lq = smem + kMaxSplits * RP; // [n][RP] sums, then weights
     __shared__ int okf;
     auto merge = [&](const float* src, const uint32_t* flags, int n) {
         if (tid == 0) okf = 1;
@@ -423,17 +423,14 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         const float bad = okf ? 0.0f : __builtin_nanf("");
         // Each thread owns E4 float4 items (row, 4 dims).  The first batch of
         // partial outputs is loaded before the (max, sum) pass so that both
-        // round trips overlap; every thread then derives its rows' weights
-        // from the (max, sum) values in LDS.
+        // round trips overlap.  Wave 0 turns the (max, sum) values into
+        // per-(range, row) weights in LDS, one row per lane (R <= 64; every
+        // lane computes, only lanes of real rows store).
         constexpr int E4 = RP * HD / 4 / AT;
         constexpr int QB = 64 / E4;           // partials per batch: 64 float4 in flight
         float4 acc[E4], v[QB][E4];
-        float mu[E4], den_e[E4];
 #pragma unroll
-        for (int e = 0; e < E4; ++e) {
-            acc[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            den_e[e] = 0.0f;
-        }
+        for (int e = 0; e < E4; ++e) acc[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         auto fetch = [&](int q0) {
 #pragma unroll
             for (int u = 0; u < QB; ++u)
@@ -453,29 +450,34 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
             lq[q * RP + r] = ml.y;
         }
         __syncthreads();
-#pragma unroll
-        for (int e = 0; e < E4; ++e) {
-            const int r = min((tid + e * AT) * 4 / HD, RP - 1);
+        if (wu == 0) {
+            const int r = min(lane, R - 1);
             float mx = -INFINITY;
             for (int q = 0; q < n; ++q) mx = fmaxf(mx, wq[q * RP + r]);
-            mu[e] = mx;
+            const float m0 = (mx == -INFINITY) ? 0.0f : mx;
+            float d = 0.0f;
+            for (int q = 0; q < n; ++q) {
+                const float w = __builtin_amdgcn_exp2f(wq[q * RP + r] - m0);
+                d = __builtin_fmaf(lq[q * RP + r], w, d);
+                lq[q * RP + r] = w;           // weights replace the sums (own row only)
+            }
+            if (lane < R) den[lane] = 1.0f / (d + bad);
         }
+        __syncthreads();
         for (int q0 = 0; q0 < n; q0 += QB) {
             if (q0 > 0) fetch(q0);
 #pragma unroll
             for (int u = 0; u < QB; ++u)
 #pragma unroll
                 for (int e = 0; e < E4; ++e) {
-                    if (q0 + u < n) {
-                        const int r = min((tid + e * AT) * 4 / HD, RP - 1);
-                        const float m0 = (mu[e] == -INFINITY) ? 0.0f : mu[e];
-                        const float w = __builtin_amdgcn_exp2f(wq[(q0 + u) * RP + r] - m0);
-                        den_e[e] = __builtin_fmaf(lq[(q0 + u) * RP + r], w, den_e[e]);
-                        acc[e].x = __builtin_fmaf(v[u][e].x, w, acc[e].x);
-                        acc[e].y = __builtin_fmaf(v[u][e].y, w, acc[e].y);
-                        acc[e].z = __builtin_fmaf(v[u][e].z, w, acc[e].z);
-                        acc[e].w = __builtin_fmaf(v[u][e].w, w, acc[e].w);
-                    }
+                    // past the n ranges v is zero and the weight is zero: no branch
+                    const float w = (q0 + u < n) ? lq[min(q0 + u, kMaxSplits - 1) * RP +
+                                                      min((tid + e * AT) * 4 / HD, RP - 1)]
+                                                 : 0.0f;
+                    acc[e].x = __builtin_fmaf(v[u][e].x, w, acc[e].x);
+                    acc[e].y = __builtin_fmaf(v[u][e].y, w, acc[e].y);
+                    acc[e].z = __builtin_fmaf(v[u][e].z, w, acc[e].z);
+                    acc[e].w = __builtin_fmaf(v[u][e].w, w, acc[e].w);
                 }
         }
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
             if (i4 * 4 < R * HD) {
                 const int r = (4 * i4) / HD, d = 4 * i4 - r * HD;
                 const int mm = r / G, hg = r - mm * G;
-                const float inv = 1.0f / (den_e[e] + bad);
+                const float inv = den[r];
                 *reinterpret_cast<float4*>(a.out + (size_t)(mm * a.hq + hk * G + hg) * HD + d) =
                     make_float4(acc[e].x * inv, acc[e].y * inv, acc[e].z * inv, acc[e].w * inv);
             }
