@@ -329,6 +329,9 @@ def main() -> int:
                     help="skip the decode-attention workload")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the split-path comparison (canonical layout, separate quantisation)")
+    ap.add_argument("--profile-attention", type=int, default=0,
+                    help="run this many eager decode-attention calls (L = 16384, M = 1 and 8, "
+                         "rotated caches) and exit: the workload for its rocprofv3 kernel trace")
     ap.add_argument("--copy-probe", action="store_true",
                     help="copy a 256 MiB device buffer 5 times and exit: the known-size "
                          "kernel that calibrates the HBM byte counters")
@@ -352,6 +355,19 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy probe: 5 copies of {COPY_PROBE_BYTES} bytes")
+        return 0
+    if args.profile_attention:
+        hq, hkv, length = 32, 8, 16384
+        _, kb, vb = S.attention_inputs(S.seed_of(6, 0, 0), 1, hq, hkv, length)
+        base = torch.from_numpy(sk.sk_kv_pack_host(kb, vb, hkv, length, length)).to(dev)
+        caches = [base] + [base.clone() for _ in range(15)]
+        for m in (1, 8):
+            qb, _, _ = S.attention_inputs(S.seed_of(6, m, 0), m, hq, hkv, 1)
+            q = torch.from_numpy(qb.view(np.int16)).to(dev)
+            for i in range(args.profile_attention):
+                sk.sk_decode_attention(q, hkv, caches[i % 16], length, length)
+        torch.cuda.synchronize()
+        log(f"profile run: {args.profile_attention} decode-attention calls at M = 1 and at M = 8")
         return 0
     R = args.copies
     if R % 2:
