@@ -7,9 +7,10 @@ this module fails: there is no CPU path.
 
 Function names follow the C ABI: ``sk_repack_w4a8``, ``sk_unrepack_w4a8``,
 ``sk_gemm_w4a8``, ``sk_gemm_w6a8``, ``sk_gemm_fused_rmsnorm``,
-``sk_gemm_fused_swiglu``, ``sk_debug_gemm`` (include/sk_repack.h) and
+``sk_gemm_fused_swiglu``, ``sk_debug_gemm`` (include/sk_repack.h),
 ``sk_kv_append``, ``sk_decode_attention``, ``sk_kv_pack_host``
-(include/sk_attention.h).
+(include/sk_attention.h) and the tree-MTP planner ``MtpPlanner`` over the
+``sk_mtp_*`` calls (include/sk_mtp.h, host code).
 """
 
 from __future__ import annotations
@@ -39,7 +40,9 @@ EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
            "sk_test_set_spin_limit",
            "sk_kv_append", "sk_decode_attention", "sk_kv_pack_host",
-           "sk_test_attention_plan", "sk_test_set_attention_split"]
+           "sk_test_attention_plan", "sk_test_set_attention_split",
+           "sk_mtp_create", "sk_mtp_destroy", "sk_mtp_observe", "sk_mtp_layout", "sk_mtp_layout_of",
+           "sk_mtp_accept", "sk_mtp_expected_tokens", "sk_mtp_state"]
 
 
 class SkWeightStruct(ctypes.Structure):
@@ -84,6 +87,14 @@ def _load() -> ctypes.CDLL:
         "sk_kv_pack_host": ([P, P, I, I, I, P], I),
         "sk_test_attention_plan": ([I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)], I),
         "sk_test_set_attention_split": ([I], I),
+        "sk_mtp_create": ([ctypes.c_double, I, ctypes.c_double, ctypes.POINTER(P)], I),
+        "sk_mtp_destroy": ([P], None),
+        "sk_mtp_observe": ([P, P, I, ctypes.c_double, ctypes.c_double, P, P], I),
+        "sk_mtp_layout": ([P, P, P, P], I),
+        "sk_mtp_layout_of": ([I, P, P], I),
+        "sk_mtp_accept": ([P, I, P, P, P], I),
+        "sk_mtp_expected_tokens": ([P, P, I, P], I),
+        "sk_mtp_state": ([P, P, P, P, P], I),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -362,3 +373,73 @@ def attention_plan(m: int, hq: int, hkv: int, length: int, cus: int = 256):
 def set_attention_split(blocks_per_split: int) -> None:
     """Test hook: force the blocks per prefix range (0 = planner)."""
     _check(LIB.sk_test_set_attention_split(blocks_per_split), "sk_test_set_attention_split")
+
+
+# ----------------------------------------------------------------------------
+# adaptive tree-MTP layout planner (include/sk_mtp.h; host code)
+# ----------------------------------------------------------------------------
+
+def _i32(values):
+    arr = (ctypes.c_int32 * max(1, len(values)))(*values)
+    return arr
+
+
+def mtp_layout_of(index: int) -> list:
+    w = (ctypes.c_int32 * 7)()
+    d = ctypes.c_int32()
+    _check(LIB.sk_mtp_layout_of(index, w, ctypes.byref(d)), "sk_mtp_layout_of")
+    return list(w[:d.value])
+
+
+def mtp_accept(widths, ranks):
+    """(accepted drafts, levels revealed) of one verified step."""
+    a, o = ctypes.c_int32(), ctypes.c_int32()
+    _check(LIB.sk_mtp_accept(_i32(widths), len(widths), _i32(ranks), ctypes.byref(a), ctypes.byref(o)),
+           "sk_mtp_accept")
+    return a.value, o.value
+
+
+def mtp_expected_tokens(p, widths) -> float:
+    """Expected tokens per step; p is [depth][8] rank probabilities (rank 0 = none)."""
+    flat = [float(x) for row in p[:len(widths)] for x in row]
+    arr = (ctypes.c_double * len(flat))(*flat)
+    out = ctypes.c_double()
+    _check(LIB.sk_mtp_expected_tokens(arr, _i32(widths), len(widths), ctypes.byref(out)),
+           "sk_mtp_expected_tokens")
+    return out.value
+
+
+class MtpPlanner:
+    """Owns one sk_mtp_planner."""
+
+    def __init__(self, decay: float = 0.95, interval: int = 32, gain: float = 1.03):
+        h = ctypes.c_void_p()
+        _check(LIB.sk_mtp_create(ctypes.c_double(decay), interval, ctypes.c_double(gain), ctypes.byref(h)),
+               "sk_mtp_create")
+        self._h = h
+        self._destroy = LIB.sk_mtp_destroy    # kept: the module global may be gone at exit
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            self._destroy(self._h)
+            self._h = None
+
+    def observe(self, ranks, verify_ms: float, draft_ms: float) -> list:
+        w = (ctypes.c_int32 * 7)()
+        d = ctypes.c_int32()
+        _check(LIB.sk_mtp_observe(self._h, _i32(ranks), len(ranks), ctypes.c_double(verify_ms),
+                                  ctypes.c_double(draft_ms), w, ctypes.byref(d)), "sk_mtp_observe")
+        return list(w[:d.value])
+
+    @property
+    def index(self) -> int:
+        i = ctypes.c_int32()
+        _check(LIB.sk_mtp_layout(self._h, ctypes.byref(i), None, None), "sk_mtp_layout")
+        return i.value
+
+    def state(self):
+        c = (ctypes.c_double * 56)()
+        v, dr = ctypes.c_double(), ctypes.c_double()
+        st = ctypes.c_int64()
+        _check(LIB.sk_mtp_state(self._h, c, ctypes.byref(v), ctypes.byref(dr), ctypes.byref(st)), "sk_mtp_state")
+        return [list(c[8 * i:8 * i + 8]) for i in range(7)], v.value, dr.value, st.value

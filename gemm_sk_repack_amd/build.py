@@ -23,7 +23,7 @@ LIB = os.path.join(HERE, "libsk_repack.so")
 SOURCES = ["sk_api.hip", "sk_repack.hip", "sk_gemm.hip",
            "sk_gemm_w4.hip", "sk_gemm_w6.hip", "sk_gemm_cb.hip",
            "sk_gemm_w4_dbg.hip", "sk_gemm_w6_dbg.hip", "sk_gemm_cb_dbg.hip",
-           "sk_gemm_split.hip", "sk_attention.hip"]
+           "sk_gemm_split.hip", "sk_attention.hip", "sk_mtp.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,7 +49,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     objs = []
     cmds = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         cmds.append([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), os.cpu_count() or 1)

@@ -17,7 +17,7 @@ FAKE = 0x7F0000000000          # 16-byte aligned, never dereferenced
 
 def declared_symbols():
     names = []
-    for h in ("sk_repack.h", "sk_repack_test.h", "sk_attention.h"):
+    for h in ("sk_repack.h", "sk_repack_test.h", "sk_attention.h", "sk_mtp.h"):
         src = open(os.path.join(ROOT, "include", h)).read()
         names += re.findall(r"^\s*(?:const\s+)?[\w\*\s]+?\b(sk_\w+)\s*\(", src, flags=re.M)
     return sorted(set(names))
