@@ -179,6 +179,45 @@ def time_attention(torch, sk, S, stream):
             "per_call": out}
 
 
+def plan_mtp(sk, t1_us: float, t8_us: float):
+    """The library's tree-MTP planner on synthetic acceptance statistics, with
+    this build's measured costs: verify = a 32-layer 9B-class forward at M = 8
+    (32 x the decoder-layer linears step at M = 8), draft = one MTP layer at
+    M = 1 (the linears step at M = 1).  Attention and the rest of the layer are
+    left out on both sides.  Reports the layout the planner settles on, the mean
+    tokens per step and the rate against plain decoding (32 layers at M = 1)."""
+    rng = np.random.default_rng(0)
+    regimes = {
+        "code-like": [0.04, 0.86, 0.06, 0.02, 0.01, 0.005, 0.003, 0.002],
+        "creative-like": [0.15, 0.35, 0.25, 0.13, 0.05, 0.03, 0.02, 0.02],
+    }
+    verify_ms, draft_ms = 32 * t8_us / 1e3, t1_us / 1e3
+    plain_ms = 32 * t1_us / 1e3
+    out = []
+    for name, probs in regimes.items():
+        pl = sk.MtpPlanner()
+        w = [1] * 7
+        toks = []
+        for step in range(640):
+            ranks_all = [int(rng.choice(8, p=probs)) for _ in range(7)]
+            acc, obs = sk.mtp_accept(w, ranks_all[:len(w)])
+            if step >= 320:
+                toks.append((1 + acc, len(w)))
+            w = pl.observe(ranks_all[:obs], verify_ms, draft_ms)
+        tok = float(np.mean([t for t, _ in toks]))
+        cost = float(np.mean([verify_ms + d * draft_ms for _, d in toks]))
+        chain_tok = sum(probs[1] ** i for i in range(8))
+        out.append({"regime": name, "layout": w, "tokens_per_step": round(tok, 3),
+                    "speedup_vs_plain_decode": round((tok / cost) / (1.0 / plain_ms), 3),
+                    "chain_of_7_expected_tokens": round(chain_tok, 3)})
+        log(f"mtp {name}: layout {w}, {tok:.2f} tokens/step, "
+            f"x{out[-1]['speedup_vs_plain_decode']} vs plain decoding")
+    return {"verify_ms": round(verify_ms, 4), "draft_ms": round(draft_ms, 4),
+            "note": ("synthetic rank statistics; costs from this run's decoder-layer linears "
+                     "(32 layers at M = 8 to verify, one layer at M = 1 to draft)"),
+            "regimes": out}
+
+
 def time_ablation(torch, sk, stream, host, xs, R, per):
     """The same step on the split path: (a) the weight left in the canonical
     layout (codes and scales read from their two regions), quantising in the
@@ -327,6 +366,8 @@ def main() -> int:
                     help="skip the expert-bank workload")
     ap.add_argument("--no-attention", action="store_true",
                     help="skip the decode-attention workload")
+    ap.add_argument("--no-mtp", action="store_true",
+                    help="skip the tree-MTP planning summary")
     ap.add_argument("--no-ablation", action="store_true",
                     help="skip the split-path comparison (canonical layout, separate quantisation)")
     ap.add_argument("--profile-attention", type=int, default=0,
@@ -507,6 +548,10 @@ def main() -> int:
     if not args.no_attention:
         attention = time_attention(torch, sk, S, stream)
 
+    mtp = None
+    if not args.no_mtp:
+        mtp = plan_mtp(sk, us1, us8)
+
     # ---------------- CPU baseline: the oracle on one step ----------------
     cpu = None
     if not args.no_cpu_baseline:
@@ -564,6 +609,8 @@ def main() -> int:
         out["experts"] = experts
     if attention is not None:
         out["attention"] = attention
+    if mtp is not None:
+        out["mtp"] = mtp
     if variants is not None:
         out["variants"] = variants
     print(json.dumps(out), flush=True)
