@@ -164,3 +164,16 @@ def test_full_size_sampled(m):
     rows = sorted({(int(rng.integers(m)), int(rng.integers(hq))) for _ in range(12)} | {(m - 1, hq - 1), (0, 0)})
     got = np.stack([out[mm, h] for mm, h in rows])
     assert_attn_close(got, qb, kb, vb, rows)
+
+
+def test_long_prefix_sampled():
+    """A 131072-entry prefix with two KV heads: the planner's largest split (64
+    ranges per head, 64 blocks each), checked on sampled (row, head) outputs."""
+    m, hq, hkv, length = 8, 8, 2, 131072
+    qb, kb, vb = S.attention_inputs(4100, m, hq, hkv, length)
+    assert sk.attention_plan(m, hq, hkv, length) == (64, 64)
+    kv = make_cache(kb, vb, length, length)
+    out = run(qb, kv, hkv, length, length)
+    rows = [(0, 0), (7, 7), (3, 4), (5, 1), (6, 6), (1, 3)]
+    got = np.stack([out[mm, h] for mm, h in rows])
+    assert_attn_close(got, qb, kb, vb, rows)
