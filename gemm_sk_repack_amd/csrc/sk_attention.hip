@@ -61,6 +61,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 constexpr int kSC1 = 16;                      // cache policy: system-coherent (write-through) access
+constexpr int kOutside = 0x7FFFFFF0;          // a buffer offset past any workspace: reads zero
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
@@ -427,19 +428,22 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         // per-(range, row) weights in LDS, one row per lane (R <= 64; every
         // lane computes, only lanes of real rows store).
         constexpr int E4 = RP * HD / 4 / AT;
-        constexpr int QB = 64 / E4;           // partials per batch: 64 float4 in flight
+        constexpr int QB = 32 / E4;           // partials per batch: 32 float4 in flight
         float4 acc[E4], v[QB][E4];
 #pragma unroll
         for (int e = 0; e < E4; ++e) acc[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        // Loads through the workspace's buffer resource: an item past the n
+        // ranges or the R rows gets an offset beyond the resource and reads
+        // zero without a memory access, so the loads need no branches.
+        const int sbase = (int)(src - a.part);
         auto fetch = [&](int q0) {
 #pragma unroll
             for (int u = 0; u < QB; ++u)
 #pragma unroll
                 for (int e = 0; e < E4; ++e) {
                     const int i4 = tid + e * AT;
-                    v[u][e] = (q0 + u < n && i4 * 4 < R * HD)
-                                  ? *reinterpret_cast<const float4*>(src + (size_t)(q0 + u) * CH + 4 * i4)
-                                  : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                    const int off = (q0 + u < n && i4 * 4 < R * HD) ? 4 * (sbase + (q0 + u) * CH + 4 * i4) : kOutside;
+                    v[u][e] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(wsr, off, 0, 0));
                 }
         };
         fetch(0);
@@ -451,15 +455,35 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         }
         __syncthreads();
         if (wu == 0) {
+            // 8 ranges per round, so that the LDS reads of a round are in flight
+            // together
             const int r = min(lane, R - 1);
             float mx = -INFINITY;
-            for (int q = 0; q < n; ++q) mx = fmaxf(mx, wq[q * RP + r]);
+            for (int q0 = 0; q0 < n; q0 += 8) {
+                float mv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) mv[u] = (q0 + u < n) ? wq[min(q0 + u, kMaxSplits - 1) * RP + r] : -INFINITY;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) mx = fmaxf(mx, mv[u]);
+            }
             const float m0 = (mx == -INFINITY) ? 0.0f : mx;
             float d = 0.0f;
-            for (int q = 0; q < n; ++q) {
-                const float w = __builtin_amdgcn_exp2f(wq[q * RP + r] - m0);
-                d = __builtin_fmaf(lq[q * RP + r], w, d);
-                lq[q * RP + r] = w;           // weights replace the sums (own row only)
+            for (int q0 = 0; q0 < n; q0 += 8) {
+                float mv[8], lv[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int qq = min(q0 + u, kMaxSplits - 1);
+                    mv[u] = wq[qq * RP + r];
+                    lv[u] = lq[qq * RP + r];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    if (q0 + u < n) {
+                        const float w = __builtin_amdgcn_exp2f(mv[u] - m0);
+                        d = __builtin_fmaf(lv[u], w, d);
+                        if (lane < R) lq[(q0 + u) * RP + r] = w;   // weights replace the sums
+                    }
+                }
             }
             if (lane < R) den[lane] = 1.0f / (d + bad);
         }
