@@ -53,16 +53,16 @@ constexpr int AW = 4;                         // waves per workgroup
 constexpr int AT = AW * 64;
 constexpr int kMaxRows = 64;                  // M * G
 constexpr int kMaxSplits = 64;
-constexpr int kSpin = 1 << 20;                // polls of one word before giving up (NaN)
+constexpr int kSpin = 1 << 20;                // polls of a flag before giving up (NaN)
 constexpr int PSTRIDE = HD + 2;               // floats per partial query row: O[128], max, sum
+constexpr int kSC1 = 16;                      // cache policy: system-coherent (write-through) access
+constexpr int kOutside = 0x7FFFFFF0;          // a buffer offset past any workspace: reads zero
 
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-constexpr int kSC1 = 16;                      // cache policy: system-coherent (write-through) access
-constexpr int kOutside = 0x7FFFFFF0;          // a buffer offset past any workspace: reads zero
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct AttnArgs {
     const uint16_t* q;   // [M][Hq][128]
@@ -118,7 +118,10 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
     const int g4 = lane >> 4, l16 = lane & 15;
     const int s = blockIdx.x, hk = blockIdx.y;
     const int M = a.m, G = a.g, R = a.r, L = a.len;
-    // this launch's tag: one more than the previous multi-range launch's
+    // this launch's tag: one more than the previous multi-range launch's.  The
+    // generation word and the done counter share a cache line and thread 0
+    // reads the one before it counts itself on the other, so every workgroup
+    // has read the generation before the last one to count replaces it.
     const uint32_t tag = a.nsplit > 1 ? peek_gen(a.hdr) + 1u : 0u;
     // With several ranges, count this workgroup on its head's counter right
     // away: the last to start merges, after its own loop, waiting for the

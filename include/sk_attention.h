@@ -41,11 +41,12 @@
  * Conventions: pointers are DEVICE pointers to caller-owned memory unless
  * stated; `stream` is a hipStream_t as void*; validation is synchronous and a
  * rejected call launches nothing.  sk_decode_attention uses a per-device
- * workspace (one arrival counter per KV head plus Hkv * splits * 16*ceil(M*G/16)
- * * 130 floats of partial results), allocated and zeroed by the first call that
- * needs it and grown with a device synchronisation (so such a call must not be
- * under stream capture); calls on one device must not overlap in time.  Each
- * launch leaves the counters at zero for the next one.
+ * workspace: a generation word, one arrival counter per KV head, one flag per
+ * (KV head, prefix range) and Hkv * ranges * 16*ceil(M*G/16) * 130 floats of
+ * partial results (at most 64 ranges per head).  It is allocated and zeroed
+ * by the first call that needs it and grown with a device synchronisation (so
+ * such a call must not be under stream capture); calls on one device must not
+ * overlap in time.  Each launch leaves the counters at zero for the next one.
  */
 #ifndef SK_ATTENTION_H
 #define SK_ATTENTION_H
@@ -76,10 +77,11 @@ sk_status sk_kv_append(void* kv, int hkv, int cap, int pos, int t,
  *   kv      cache (layout above) of capacity cap entries, L <= cap
  *   scale   softmax scale (1/sqrt(128) for the usual attention)
  *   out     [M][Hq][128] float32, 16-byte aligned
- * The prefix is split into ranges of 32-entry blocks over many workgroups;
- * the last workgroup of each KV head to finish combines the ranges'
- * partial results (log-sum-exp rescaling, fixed order) and writes out, in
- * the same launch.
+ * The prefix is split into ranges of 32-entry blocks over many workgroups
+ * (one per range and KV head); each publishes its partial result, and the
+ * last workgroup of each KV head to start combines the ranges' results
+ * (log-sum-exp rescaling, fixed range order) and writes out, in the same
+ * launch.
  * Errors: NULL, SHAPE (M not in 1..8, hq % hkv, L < M, L > cap, cap % 32,
  *         scale not finite and > 0), UNSUPPORTED (M * Hq / Hkv > 64), ALIGN, HIP.
  */
