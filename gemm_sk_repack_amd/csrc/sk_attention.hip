@@ -107,7 +107,7 @@ __device__ inline void wt_store(const __amdgpu_buffer_rsrc_t& ws, int off, float
 template <int NQT>
 __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
     constexpr int RP = NQT * 16;              // query rows padded to whole tiles
-    constexpr int NSLOT = NQT == 1 ? 4 : (NQT == 2 ? 3 : 2);   // blocks held in registers
+    constexpr int NSLOT = 2;                  // blocks held in registers (more measured slower)
     // dynamic LDS (smem below): the waves' states, [AW][NQT][34][64] floats,
     // later reused by the merges
     static_assert(AW * NQT * 34 * 64 >= 2 * kMaxSplits * RP, "merge scratch");
