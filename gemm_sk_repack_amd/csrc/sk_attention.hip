@@ -56,6 +56,7 @@ constexpr int kMaxSplits = 64;
 constexpr int kSpin = 1 << 20;                // polls of a flag before giving up (NaN)
 constexpr int PSTRIDE = HD + 2;               // floats per partial query row: O[128], max, sum
 constexpr int kSC1 = 16;                      // cache policy: system-coherent (write-through) access
+constexpr int kNT = 2;                        // cache policy: non-temporal (the cache is read once per call)
 constexpr int kOutside = 0x7FFFFFF0;          // a buffer offset past any workspace: reads zero
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -181,10 +182,10 @@ __global__ __launch_bounds__(AT) void attn_kernel(AttnArgs a) {
         const int off = (wu + AW * i) * BLOCK_BYTES + lane * 16;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            kb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + j * 1024, 0, 0));
+            kb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + j * 1024, 0, kNT));
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            vb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 8192 + j * 1024, 0, 0));
+            vb[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 8192 + j * 1024, 0, kNT));
     };
 
     // Max over the four lanes of a query row (lanes l, l^16, l^32, l^48).
