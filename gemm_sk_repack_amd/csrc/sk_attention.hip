@@ -53,6 +53,8 @@ constexpr int AW = 4;                         // waves per workgroup
 constexpr int AT = AW * 64;
 constexpr int kMaxRows = 64;                  // M * G
 constexpr int kMaxSplits = 64;
+constexpr int kMaxKvHeads = 512;              // keeps the partial states under 2 GiB
+constexpr int kMaxEntries = 1 << 22;          // keeps one range under 2 GiB
 constexpr int kSpin = 1 << 20;                // polls of a flag before giving up (NaN)
 constexpr int PSTRIDE = HD + 2;               // floats per partial query row: O[128], max, sum
 constexpr int kSC1 = 16;                      // cache policy: system-coherent (write-through) access
@@ -677,11 +679,14 @@ hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const voi
         default: return hipErrorInvalidValue;
     }
     const size_t lds = (size_t)AW * p.nqt * 34 * 64 * 4;
-    if (lds > 64 * 1024 && !ds.lds_set[p.nqt]) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)lds);
-        if (e != hipSuccess) return e;
-        ds.lds_set[p.nqt] = true;
+    if (lds > 64 * 1024) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        if (!ds.lds_set[p.nqt]) {
+            e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            ds.lds_set[p.nqt] = true;
+        }
     }
     hipLaunchKernelGGL(fn, dim3((unsigned)p.nsplit, (unsigned)hkv), dim3(AT), lds, st, a);
     return hipGetLastError();
@@ -731,7 +736,9 @@ SK_EXPORT sk_status sk_decode_attention(const uint16_t* q, int m, int hq, int hk
     if (m < 1 || m > 8 || hkv < 1 || hq < 1 || hq % hkv != 0 || cap < ska::BK || cap % ska::BK != 0 ||
         len < m || len > cap || !std::isfinite(scale) || !(scale > 0.0f))
         return SK_ERR_SHAPE;
-    if ((int64_t)m * (hq / hkv) > ska::kMaxRows || hkv > 65535) return SK_ERR_UNSUPPORTED;
+    // rows per KV head; 32-bit offsets into the workspace and into one range
+    if ((int64_t)m * (hq / hkv) > ska::kMaxRows || hkv > ska::kMaxKvHeads || cap > ska::kMaxEntries)
+        return SK_ERR_UNSUPPORTED;
     if (!ska::aligned16(q) || !ska::aligned16(kv) || !ska::aligned16(out)) return SK_ERR_ALIGN;
     const hipError_t e = ska::launch_attention(q, m, hq, hkv, kv, cap, len, scale, out,
                                                static_cast<hipStream_t>(stream));

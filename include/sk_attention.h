@@ -83,7 +83,8 @@ sk_status sk_kv_append(void* kv, int hkv, int cap, int pos, int t,
  * (log-sum-exp rescaling, fixed range order) and writes out, in the same
  * launch.
  * Errors: NULL, SHAPE (M not in 1..8, hq % hkv, L < M, L > cap, cap % 32,
- *         scale not finite and > 0), UNSUPPORTED (M * Hq / Hkv > 64), ALIGN, HIP.
+ *         scale not finite and > 0), UNSUPPORTED (M * Hq / Hkv > 64,
+ *         Hkv > 512, cap > 4194304), ALIGN, HIP.
  */
 sk_status sk_decode_attention(const uint16_t* q, int m, int hq, int hkv,
                               const void* kv, int cap, int len, float scale,

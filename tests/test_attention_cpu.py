@@ -76,6 +76,8 @@ def test_decode_attention_validation():
     assert attn(scale=float("inf")) == sk.SK_ERR_SHAPE
     assert attn(scale=float("nan")) == sk.SK_ERR_SHAPE
     assert attn(m=8, hq=72, hkv=8) == sk.SK_ERR_UNSUPPORTED     # 8 rows x 9 heads per group > 64
+    assert attn(hq=1024, hkv=1024) == sk.SK_ERR_UNSUPPORTED      # more KV heads than supported
+    assert attn(cap=1 << 23) == sk.SK_ERR_UNSUPPORTED            # a longer cache than supported
     assert attn(q=FAKE + 8) == sk.SK_ERR_ALIGN
     assert attn(kv=FAKE + 4) == sk.SK_ERR_ALIGN
     assert attn(out=FAKE + 4) == sk.SK_ERR_ALIGN
