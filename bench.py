@@ -168,9 +168,10 @@ def time_attention(torch, sk, S, stream):
                             4 * R)
             b = kv_bytes + m * hq * d * (2 + 4)
             splits, bps = sk.attention_plan(m, hq, hkv, length)
+            gbps = b / (us * 1e-6) / 1e9
             out.append({"L": length, "m": m, "us_per_call": round(us, 3),
-                        "GBps": round(b / (us * 1e-6) / 1e9, 1), "ranges_per_head": splits,
-                        "blocks_per_range": bps})
+                        "GBps": round(gbps, 1), "frac_peak": round(gbps / PEAK_GBPS, 4),
+                        "ranges_per_head": splits, "blocks_per_range": bps})
             log(f"attention L={length} M={m}: {us:7.3f} us ({out[-1]['GBps']} GB/s), "
                 f"{splits} ranges x {bps} blocks per head")
         del caches, base
