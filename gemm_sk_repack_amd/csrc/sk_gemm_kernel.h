@@ -171,15 +171,31 @@ __device__ inline float rms_apply(float x, float r, float g) {
 }
 
 // Activation codes q = clamp(rint(fp32(h / sx)), -127, 127), packed as int8
-// four to a dword.  For sx > 0, |h| <= 127 sx so the clamp never acts.  Adding 1.5 * 2^23 rounds a value of magnitude < 2^22 to
-// the nearest integer (ties to even) and leaves it in the low mantissa bits, so
-// the low byte of the sum's bit pattern is the int8 result.  t = h * inv with
-// inv = fp32(1/sx) is within |h/sx| * 2^-23 (< 1.6e-5 here) of h/sx, and
-// fp32(h/sx) within half an ulp (<= 2^-18) of it, so rint(t) equals
-// rint(fp32(h/sx)) unless t lies within 2e-5 of a half-integer; only then (or
-// for a tiny sx) is the quotient formed by IEEE division.
+// four to a dword.  For sx > 0, |h| <= 127 sx so the clamp never acts.
+// fma(h, c, 1.5 * 2^23) with |h c| < 2^22 rounds the exact product h c to the
+// nearest integer (ties to even) and leaves it in the low mantissa bits, so the
+// low byte of the result's bit pattern is the int8 code.  With inv = fp32(1/sx)
+// (correctly rounded), inv_lo = fp32(inv (1 - 2^-22)) and inv_hi =
+// fp32(inv (1 + 2^-22)) satisfy inv_lo <= (1 - 2^-24) / sx and inv_hi >=
+// (1 + 2^-24) / sx (three relative errors of at most 2^-24 each), and
+// fp32(h/sx) is within a factor 1 +- 2^-24 of h/sx, so fp32(h/sx) lies between
+// h inv_lo and h inv_hi.  Rounding to the nearest integer is monotone: where the
+// two products round to the same integer, fp32(h/sx) rounds to it too.  Only
+// where they differ (the quotient within about |h/sx| 2^-22 of a half-integer),
+// or for a tiny sx, is the quotient formed by IEEE division.
 constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
-constexpr float kTieBand = 2e-5f;
+constexpr float kInvLo = 0x1.fffff8p-1f;      // 1 - 2^-22
+constexpr float kInvHi = 0x1.000004p+0f;      // 1 + 2^-22
+constexpr float kTinySx = 2.3509887e-38f;     // 2^-125: below it 1/sx may not be normal
+// Code bits of h (its low byte is the int8 code) from the lower product; `split`
+// becomes nonzero when the two products round differently (each term is below
+// 2^23, so the sum of at most 32 terms cannot wrap).
+__device__ inline uint32_t code_bits(float h, float inv_lo, float inv_hi, uint32_t& split) {
+    const uint32_t lo = __float_as_uint(__builtin_fmaf(h, inv_lo, kRoundMagic));
+    const uint32_t hi = __float_as_uint(__builtin_fmaf(h, inv_hi, kRoundMagic));
+    split += lo ^ hi;
+    return lo;
+}
 // bytes 0..3 <- low bytes of b0..b3
 __device__ inline uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
     return __builtin_amdgcn_perm(b1, b0, 0x0C0C0400u) | __builtin_amdgcn_perm(b3, b2, 0x04000C0Cu);
@@ -796,15 +812,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             // codes of all elements first; the exact division, rarely needed, is one
             // out-of-line block for the whole thread
             uint32_t b[NCH * E];
-            float dev = 1.0f;           // min over elements of |fract(t) - 0.5|
+            uint32_t split = 0;
+            const float inv_lo = inv * kInvLo, inv_hi = inv * kInvHi;
 #pragma unroll
-            for (int j = 0; j < NCH * E; ++j) {
-                const float t = h[j] * inv;
-                b[j] = __float_as_uint(t + kRoundMagic);
-                dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
-            }
-            // 2^-125: 1/sx may not be normal
-            if (__builtin_expect((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f, 0)) {
+            for (int j = 0; j < NCH * E; ++j) b[j] = code_bits(h[j], inv_lo, inv_hi, split);
+            if (__builtin_expect((split != 0 || sx < kTinySx) && sx > 0.0f, 0)) {
 #pragma unroll
                 for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
             }

@@ -18,8 +18,8 @@ namespace {
 
 // One workgroup per activation row: the row's absmax, then sx = absmax/127 and
 // q = rint(h/sx) with the same arithmetic as the GEMM's in-launch quantiser
-// (multiply by 1/sx, exact division where the product may sit within rounding
-// error of a half-integer), written to memory.
+// (two products that bracket fp32(h/sx); exact division where they round to
+// different integers), written to memory.
 constexpr int QT = 256;
 template <int XT>
 __global__ __launch_bounds__(QT) void quantize_kernel(const void* x, int k, int8_t* q, float* sx_out) {
@@ -52,19 +52,16 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const void* x, int k, int8
     for (int w = 0; w < QT / 64; ++w) amx = fmaxf(amx, wmax[w]);
     const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
     const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+    const float inv_lo = inv * kInvLo, inv_hi = inv * kInvHi;
     if (tid == 0) sx_out[m] = sx;
     for (int c = tid; c < nch; c += QT) {
         float v[E];
         chunk(c, v);
         uint32_t b[E];
-        float dev = 1.0f;
+        uint32_t split = 0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float t = v[e] * inv;
-            b[e] = __float_as_uint(t + kRoundMagic);
-            dev = fminf(dev, fabsf(__builtin_amdgcn_fractf(t) - 0.5f));
-        }
-        if ((dev < kTieBand || sx < 2.3509887e-38f) && sx > 0.0f) {
+        for (int e = 0; e < E; ++e) b[e] = code_bits(v[e], inv_lo, inv_hi, split);
+        if ((split != 0 || sx < kTinySx) && sx > 0.0f) {
 #pragma unroll
             for (int e = 0; e < E; ++e) b[e] = __float_as_uint(v[e] / sx + kRoundMagic);
         }

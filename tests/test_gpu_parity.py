@@ -154,6 +154,37 @@ def test_zero_and_constant_rows():
     assert np.all(y.cpu().numpy()[1] == 0)
 
 
+def near_tie_rows(seed, m, k):
+    """Rows whose quotients h / sx sit at or a few float32 steps from half-integers."""
+    rng = np.random.default_rng(seed)
+    amx = rng.uniform(1e-2, 1e2, size=m).astype(F32)
+    sx = (amx / F32(127.0)).astype(np.float64)
+    n = rng.integers(-127, 127, size=(m, k)).astype(np.float64)
+    h = ((n + 0.5) * sx[:, None]).astype(F32)
+    steps = rng.integers(-3, 4, size=(m, k))
+    for _ in range(3):
+        h = np.where(steps > 0, np.nextafter(h, F32(np.inf)), h)
+        h = np.where(steps < 0, np.nextafter(h, F32(-np.inf)), h)
+        steps = steps - np.sign(steps)
+    h[:, 0] = amx
+    return h
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_near_tie_activations_bit_exact(m):
+    """Quotients next to half-integers take the kernels' exact-division branch."""
+    n, k, g = 256, 4096, 32
+    w, buf = gpu_weight(0, n, k, g, 25)
+    sk.sk_repack_w4a8(w)
+    h = near_tie_rows(26 + m, m, k)
+    check_call(w, buf, 0, n, k, g, torch.from_numpy(h).cuda(), h, m)
+    q, sx = sk.sk_quantize_rows(torch.from_numpy(h).cuda())
+    torch.cuda.synchronize()
+    q_ref, sx_ref = O.quantize_rows(h)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+
+
 def test_rows_do_not_interact_and_runs_repeat():
     n, k, g = 512, 2048, 32
     w, buf = gpu_weight(0, n, k, g, 31)
