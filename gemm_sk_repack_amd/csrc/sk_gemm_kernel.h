@@ -188,12 +188,14 @@ constexpr float kInvLo = 0x1.fffff8p-1f;      // 1 - 2^-22
 constexpr float kInvHi = 0x1.000004p+0f;      // 1 + 2^-22
 constexpr float kTinySx = 2.3509887e-38f;     // 2^-125: below it 1/sx may not be normal
 // Code bits of h (its low byte is the int8 code) from the lower product; `split`
-// becomes nonzero when the two products round differently (each term is below
-// 2^23, so the sum of at most 32 terms cannot wrap).
+// becomes nonzero when the two products round differently.  Both results are
+// 1.5 * 2^23 plus an integer of magnitude <= 128, so their low 16 bits differ
+// exactly when the integers do; the sum of absolute differences of those bits
+// adds less than 2^16 per element and cannot wrap.
 __device__ inline uint32_t code_bits(float h, float inv_lo, float inv_hi, uint32_t& split) {
     const uint32_t lo = __float_as_uint(__builtin_fmaf(h, inv_lo, kRoundMagic));
     const uint32_t hi = __float_as_uint(__builtin_fmaf(h, inv_hi, kRoundMagic));
-    split += lo ^ hi;
+    split = __builtin_amdgcn_sad_u16(lo, hi, split);
     return lo;
 }
 // bytes 0..3 <- low bytes of b0..b3
