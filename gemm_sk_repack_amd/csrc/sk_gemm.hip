@@ -106,15 +106,19 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
         S = split_override;
     } else if (!valid(1)) {
         // The slice must fit the thread layout and LDS.  Among the K-splits that
-        // do, the cheapest: weight slots per wave plus the cross-slice exchange
-        // and merge, priced at about 4 + S/4 slots (ties: fewer slices).
+        // do, the cheapest by a cost fitted to measured launch times: 4 per
+        // weight slot of a wave, 1/2048 per activation a workgroup quantises
+        // (M * KS) and 1/16 per (tile, slice, row) partial a workgroup's merges
+        // read (tiles per workgroup * S * M); ties: fewer slices.
         int64_t best = -1;
         for (int s = 2; s <= SMAX; ++s) {
             if (!valid(s)) continue;
             const int R = workgroups_per_slice(cus, s, T);
+            const int64_t tpw = (T + R - 1) / R;
             int kw, tw;
-            const int64_t slots = split_waves(KB / s, (T + R - 1) / R, m, NW - 1, kw, tw);
-            const int64_t cost = 4 * slots + 16 + s;
+            const int64_t slots = split_waves(KB / s, (int)tpw, m, NW - 1, kw, tw);
+            // in units of 1/2048
+            const int64_t cost = 8192 * slots + (int64_t)m * (G.k / s) + 128 * tpw * s * m;
             if (best < 0 || cost < best) {
                 best = cost;
                 S = s;
