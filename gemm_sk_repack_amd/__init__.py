@@ -277,7 +277,8 @@ def sk_debug_gemm(w: QuantWeight, prologue: int, x: torch.Tensor, x2=None, gamma
     return y, q, sx, p
 
 
-PLAN_FIELDS = ["S", "R", "P", "TW", "KW", "spw", "KBs", "KS", "WPR", "lds", "part_floats"]
+PLAN_FIELDS = ["S", "R", "P", "TW", "KW", "spw", "KBs", "KS", "WPR", "lds", "part_floats", "ept",
+               "wide"]
 
 
 def gemm_plan(n: int, k: int, group: int, fmt: int, m: int, cus: int = 256,

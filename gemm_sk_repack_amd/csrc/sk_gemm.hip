@@ -16,11 +16,11 @@ namespace {
 
 // Production kernels carry no debug-export code; the test hook's calls (any of
 // q_out / sx_out / p_out set) run the instances that have it.
-KernelFn pick(int fmt, int pro, int xt, int gs, bool dot4, bool dbg) {
+KernelFn pick(int fmt, int pro, int xt, int gs, bool dot4, bool dbg, bool wide) {
     switch (fmt) {
-        case FMT_W6: return dbg ? pick_kernel_w6_dbg(pro, xt, gs, dot4) : pick_kernel_w6(pro, xt, gs, dot4);
-        case FMT_CB: return dbg ? pick_kernel_cb_dbg(pro, xt, gs, dot4) : pick_kernel_cb(pro, xt, gs, dot4);
-        default: return dbg ? pick_kernel_w4_dbg(pro, xt, gs, dot4) : pick_kernel_w4(pro, xt, gs, dot4);
+        case FMT_W6: return dbg ? pick_kernel_w6_dbg(pro, xt, gs, dot4, wide) : pick_kernel_w6(pro, xt, gs, dot4, wide);
+        case FMT_CB: return dbg ? pick_kernel_cb_dbg(pro, xt, gs, dot4, wide) : pick_kernel_cb(pro, xt, gs, dot4, wide);
+        default: return dbg ? pick_kernel_w4_dbg(pro, xt, gs, dot4, wide) : pick_kernel_w4(pro, xt, gs, dot4, wide);
     }
 }
 
@@ -77,21 +77,17 @@ int workgroups_per_slice(int cus, int S, int T) {
     return R < 1 ? 1 : R;
 }
 
-}  // namespace
-
-Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
+// The plan for a given number of activations per thread (the kernel's register
+// budget for the prologue).
+Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
     Plan p;
     const int KB = (int)G.KB;
     const int T = (int)G.T;
     const bool cb = G.fmt == FMT_CB;
-    const bool dot4 = (m == 1) && !cb;
     p.WPR = NW / m;                               // waves per activation row
     const int tpr = p.WPR * 64;
-    // each thread quantises at most 16 activations of its row, 32 for M >= 2
-    // without a prologue (the kernel's register budget)
-    // (the split path's PRO_QIN keeps PRO_NONE's plan, so the two compare like for like)
-    const int ept = (dot4 || (pro != PRO_NONE && pro != PRO_QIN) || cb) ? 16 : 32;
     p.ept = ept;
+    p.wide = false;
     auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
@@ -147,6 +143,25 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     return p;
 }
 
+}  // namespace
+
+Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
+    const bool cb = G.fmt == FMT_CB;
+    const bool dot4 = (m == 1) && !cb;
+    // Each thread quantises at most 16 activations of its row, 32 for M >= 2
+    // without a prologue; the wide instances take 40 and are used only where
+    // that needs fewer K-slices.  (The split path's PRO_QIN keeps PRO_NONE's
+    // plan, so the two compare like for like.)
+    if (dot4 || cb || (pro != PRO_NONE && pro != PRO_QIN)) return plan_for(G, m, cus, split_override, 16);
+    const Plan p = plan_for(G, m, cus, split_override, 32);
+    Plan w = plan_for(G, m, cus, split_override, 40);
+    if (w.ok && (!p.ok || w.S < p.S)) {
+        w.wide = true;
+        return w;
+    }
+    return p;
+}
+
 void set_split_override(int s) { g_split_override = s; }
 
 bool gemm_plan_ok(const Geom& G, int m, int pro) {
@@ -197,8 +212,8 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     const bool dot4 = (c.m == 1) && G.fmt != FMT_CB;
     const int gs = (int)(G.g / 32);                // 0 for the codebook's G = 16
     const bool dbg = c.q_out || c.sx_out || c.p_out;
-    KernelFn fn = c.canon ? pick_kernel_split(c.prologue, c.xt, gs, dot4)
-                          : pick(G.fmt, c.prologue, c.xt, gs, dot4, dbg);
+    KernelFn fn = c.canon ? pick_kernel_split(c.prologue, c.xt, gs, dot4, p.wide)
+                          : pick(G.fmt, c.prologue, c.xt, gs, dot4, dbg, p.wide);
     if (!fn) return hipErrorInvalidValue;
 
     KArgs a;

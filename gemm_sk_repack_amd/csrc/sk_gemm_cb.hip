@@ -3,8 +3,8 @@
 
 namespace sk {
 
-KernelFn pick_kernel_cb(int pro, int xt, int gs, bool dot4) {
-    return pick_format<FMT_CB, false>(pro, xt, gs, dot4);
+KernelFn pick_kernel_cb(int pro, int xt, int gs, bool dot4, bool wide) {
+    return pick_format<FMT_CB, false>(pro, xt, gs, dot4, wide);
 }
 
 }  // namespace sk

@@ -116,13 +116,13 @@ struct Smem {
 typedef void (*KernelFn)(KArgs);
 
 // One picker per (format, debug exports) translation unit.
-KernelFn pick_kernel_w4(int pro, int xt, int gs, bool dot4);
-KernelFn pick_kernel_w6(int pro, int xt, int gs, bool dot4);
-KernelFn pick_kernel_cb(int pro, int xt, int gs, bool dot4);
-KernelFn pick_kernel_w4_dbg(int pro, int xt, int gs, bool dot4);
-KernelFn pick_kernel_w6_dbg(int pro, int xt, int gs, bool dot4);
-KernelFn pick_kernel_cb_dbg(int pro, int xt, int gs, bool dot4);
-KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4);
+KernelFn pick_kernel_w4(int pro, int xt, int gs, bool dot4, bool wide);
+KernelFn pick_kernel_w6(int pro, int xt, int gs, bool dot4, bool wide);
+KernelFn pick_kernel_cb(int pro, int xt, int gs, bool dot4, bool wide);
+KernelFn pick_kernel_w4_dbg(int pro, int xt, int gs, bool dot4, bool wide);
+KernelFn pick_kernel_w6_dbg(int pro, int xt, int gs, bool dot4, bool wide);
+KernelFn pick_kernel_cb_dbg(int pro, int xt, int gs, bool dot4, bool wide);
+KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4, bool wide);
 
 namespace {
 
@@ -540,7 +540,7 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
 // the kernel
 // --------------------------------------------------------------------------
 
-template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG, bool CANON>
+template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG, bool CANON, bool WIDE>
 __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ Smem sm;
@@ -551,8 +551,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // byte), so sign extension is free; the sums are scaled back at the store.
     constexpr int WSH = (FMT == FMT_W6) ? 2 : 4;
     constexpr float KINV = CB ? 1.0f : (FMT == FMT_W6) ? 0.25f : 0.0625f;
-    // activations per thread: 32 only where the registers allow it
-    constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : 32;
+    // activations per thread: 32 only where the registers allow it, 40 in the
+    // wide instances (used only where that saves K-slices: the larger code of
+    // their prologue costs the other calls time)
+    constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : WIDE ? 40 : 32;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
     const int tid = threadIdx.x;
@@ -1159,54 +1161,63 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 }
 
 // Kernel pointer for a format, prologue, activation dtype, groups per 32-k block
-// (gs; 0 = the codebook's G = 16) and M = 1 / M >= 2; nullptr if not built.
+// (gs; 0 = the codebook's G = 16), M = 1 / M >= 2 and the wide activation budget
+// (M >= 2 without a prologue only); nullptr if not built.
 template <int FMT, int PRO, int XT, int GS, bool DBG>
-KernelFn pick_dot(bool dot4) {
+KernelFn pick_dot(bool dot4, bool wide) {
     if constexpr (FMT == FMT_CB) {
-        return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false>;   // the codebook runs on MFMA for every M
+        return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;   // the codebook runs on MFMA for every M
+    } else if constexpr (PRO == PRO_NONE) {
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>
+               : wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true>
+                      : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
     } else {
-        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false>
-                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false>;
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>
+                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
     }
 }
 template <int FMT, int PRO, int XT, bool DBG>
-KernelFn pick_gs(int gs, bool dot4) {
+KernelFn pick_gs(int gs, bool dot4, bool wide) {
     switch (gs) {
         case 0:
-            if constexpr (FMT == FMT_CB) return pick_dot<FMT, PRO, XT, 0, DBG>(dot4);
+            if constexpr (FMT == FMT_CB) return pick_dot<FMT, PRO, XT, 0, DBG>(dot4, wide);
             return nullptr;
-        case 1: return pick_dot<FMT, PRO, XT, 1, DBG>(dot4);
-        case 2: return pick_dot<FMT, PRO, XT, 2, DBG>(dot4);
-        default: return pick_dot<FMT, PRO, XT, 4, DBG>(dot4);
+        case 1: return pick_dot<FMT, PRO, XT, 1, DBG>(dot4, wide);
+        case 2: return pick_dot<FMT, PRO, XT, 2, DBG>(dot4, wide);
+        default: return pick_dot<FMT, PRO, XT, 4, DBG>(dot4, wide);
     }
 }
 template <int FMT, int PRO, bool DBG>
-KernelFn pick_xt(int xt, int gs, bool dot4) {
-    return xt == 1 ? pick_gs<FMT, PRO, 1, DBG>(gs, dot4) : pick_gs<FMT, PRO, 0, DBG>(gs, dot4);
+KernelFn pick_xt(int xt, int gs, bool dot4, bool wide) {
+    return xt == 1 ? pick_gs<FMT, PRO, 1, DBG>(gs, dot4, wide) : pick_gs<FMT, PRO, 0, DBG>(gs, dot4, wide);
 }
 // The split path's kernels: 4-bit weights in the canonical layout, either
-// quantising x in the launch (PRO_NONE) or reading q from memory (PRO_QIN).
+// quantising x in the launch (PRO_NONE) or reading q from memory (PRO_QIN,
+// which has no activation budget).
 template <int PRO, int XT, int GS>
-KernelFn pick_canon_dot(bool dot4) {
-    return dot4 ? gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true>
-                : gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true>;
+KernelFn pick_canon_dot(bool dot4, bool wide) {
+    if constexpr (PRO == PRO_NONE) {
+        if (!dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, true>;
+    }
+    return dot4 ? gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, false>
+                : gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, false>;
 }
 template <int PRO, int XT>
-KernelFn pick_canon_gs(int gs, bool dot4) {
+KernelFn pick_canon_gs(int gs, bool dot4, bool wide) {
     switch (gs) {
-        case 1: return pick_canon_dot<PRO, XT, 1>(dot4);
-        case 2: return pick_canon_dot<PRO, XT, 2>(dot4);
-        case 4: return pick_canon_dot<PRO, XT, 4>(dot4);
+        case 1: return pick_canon_dot<PRO, XT, 1>(dot4, wide);
+        case 2: return pick_canon_dot<PRO, XT, 2>(dot4, wide);
+        case 4: return pick_canon_dot<PRO, XT, 4>(dot4, wide);
         default: return nullptr;
     }
 }
 
 template <int FMT, bool DBG>
-KernelFn pick_format(int pro, int xt, int gs, bool dot4) {
+KernelFn pick_format(int pro, int xt, int gs, bool dot4, bool wide) {
     switch (pro) {
-        case PRO_RMSNORM: return pick_xt<FMT, PRO_RMSNORM, DBG>(xt, gs, dot4);
-        case PRO_SWIGLU: return pick_xt<FMT, PRO_SWIGLU, DBG>(xt, gs, dot4);
-        default: return pick_xt<FMT, PRO_NONE, DBG>(xt, gs, dot4);
+        case PRO_RMSNORM: return pick_xt<FMT, PRO_RMSNORM, DBG>(xt, gs, dot4, false);
+        case PRO_SWIGLU: return pick_xt<FMT, PRO_SWIGLU, DBG>(xt, gs, dot4, false);
+        default: return pick_xt<FMT, PRO_NONE, DBG>(xt, gs, dot4, wide);
     }
 }
 

@@ -6,9 +6,9 @@
 
 namespace sk {
 
-KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4) {
-    if (pro == PRO_QIN) return pick_canon_gs<PRO_QIN, 0>(gs, dot4);
-    return xt == 1 ? pick_canon_gs<PRO_NONE, 1>(gs, dot4) : pick_canon_gs<PRO_NONE, 0>(gs, dot4);
+KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4, bool wide) {
+    if (pro == PRO_QIN) return pick_canon_gs<PRO_QIN, 0>(gs, dot4, false);
+    return xt == 1 ? pick_canon_gs<PRO_NONE, 1>(gs, dot4, wide) : pick_canon_gs<PRO_NONE, 0>(gs, dot4, wide);
 }
 
 }  // namespace sk

@@ -111,6 +111,10 @@ GEMM_CASES = [
     (1, 48, 256, 64, (1, 3)),
     (1, 33, 384, 128, (1, 8)),
     (1, 2048, 4096, 16, (1, 8)),
+    # the 40-activation instances (K-slices saved at M >= 6 for K = 5120, M = 3 for K = 12288)
+    (0, 528, 5120, 32, (6, 8)),
+    (2, 272, 5120, 64, (7, 8)),
+    (0, 300, 12288, 32, (3,)),
 ]
 
 

@@ -31,7 +31,12 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert 1 <= S <= 32 and KB % S == 0
     assert p["KBs"] == KB // S and p["KS"] == k // S
     assert p["P"] == S * p["R"] and p["P"] <= 256 and 1 <= p["R"] <= T
-    ept = 16 if (m == 1 or pro != sk.PRO_NONE or fmt == sk.SK_W4_CODEBOOK) else 32
+    narrow = m == 1 or pro != sk.PRO_NONE or fmt == sk.SK_W4_CODEBOOK
+    ept = p["ept"]
+    assert ept == (16 if narrow else 40 if p["wide"] else 32)
+    if p["wide"] and S == 1:
+        # the 40-activation instances run only where they save K-slices
+        assert k > 32 * 64 * (NW // m)
     # waves per activation row: as many as the slice needs, at most NW / M
     assert p["WPR"] == min(NW // m, -(-p["KS"] // (ept * 64)))
     assert p["KS"] // ept <= p["WPR"] * 64                 # the slice fits the registers
@@ -88,3 +93,17 @@ def test_forced_split_hook_validates():
     with pytest.raises(sk.SkError):
         sk.set_split(-1)
     sk.set_split(0)
+
+
+# Plans measured on the MI355X: the 40-activation instances where they remove or
+# halve the K-split (27B-class linears at M >= 6, K = 12288 at M = 3, K = 17408),
+# the 32-activation ones where the slice already fits.
+@pytest.mark.parametrize("n,k,m,S,wide", [
+    (6144, 4096, 8, 1, 0), (4096, 4096, 8, 1, 0), (24576, 4096, 8, 1, 0), (4096, 12288, 8, 4, 0),
+    (4096, 12288, 3, 1, 1), (4096, 12288, 2, 1, 0), (7168, 5120, 8, 1, 1), (5120, 5120, 6, 1, 1),
+    (34816, 5120, 8, 1, 1), (7168, 5120, 5, 1, 0), (5120, 17408, 8, 4, 1), (5120, 17408, 2, 1, 1),
+])
+def test_wide_budget_where_measured_faster(n, k, m, S, wide):
+    p = sk.gemm_plan(n, k, 32, 0, m)
+    assert (p["S"], p["wide"]) == (S, wide), p
+
