@@ -149,10 +149,22 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     const bool cb = G.fmt == FMT_CB;
     const bool dot4 = (m == 1) && !cb;
     // Each thread quantises at most 16 activations of its row, 32 for M >= 2
-    // without a prologue; the wide instances take 40 and are used only where
+    // without a prologue; the wide instances take 40 (no prologue) or 32
+    // (RMSNorm with 4-bit weights, one K-slice only) and are used only where
     // that needs fewer K-slices.  (The split path's PRO_QIN keeps PRO_NONE's
     // plan, so the two compare like for like.)
-    if (dot4 || cb || (pro != PRO_NONE && pro != PRO_QIN)) return plan_for(G, m, cus, split_override, 16);
+    if (dot4 || cb || pro == PRO_SWIGLU) return plan_for(G, m, cus, split_override, 16);
+    if (pro == PRO_RMSNORM) {
+        if (G.fmt != FMT_W4) return plan_for(G, m, cus, split_override, 16);
+        const Plan p = plan_for(G, m, cus, split_override, 16);
+        if (p.ok && p.S == 1) return p;
+        Plan w = plan_for(G, m, cus, split_override, 32);
+        if (w.ok && w.S == 1) {
+            w.wide = true;
+            return w;
+        }
+        return p;
+    }
     const Plan p = plan_for(G, m, cus, split_override, 32);
     Plan w = plan_for(G, m, cus, split_override, 40);
     if (w.ok && (!p.ok || w.S < p.S)) {

@@ -551,10 +551,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // byte), so sign extension is free; the sums are scaled back at the store.
     constexpr int WSH = (FMT == FMT_W6) ? 2 : 4;
     constexpr float KINV = CB ? 1.0f : (FMT == FMT_W6) ? 0.25f : 0.0625f;
-    // activations per thread: 32 only where the registers allow it, 40 in the
-    // wide instances (used only where that saves K-slices: the larger code of
-    // their prologue costs the other calls time)
-    constexpr int EPT = (DOT4 || PRO != PRO_NONE) ? 16 : WIDE ? 40 : 32;
+    // Activations per thread: 32 only where the registers allow it.  The wide
+    // instances (used only where they save K-slices: their larger prologue code
+    // costs the other calls time) take 40 without a prologue, and 32 with the
+    // RMSNorm prologue for a single K-slice and 4-bit weights: compiling out the
+    // cross-slice exchange (ONE) is what makes room for the latter (the 6-bit
+    // unpack needs a few registers more than are left).
+    constexpr bool ONE = WIDE && PRO == PRO_RMSNORM;
+    constexpr int EPT = DOT4 ? 16 : PRO == PRO_NONE ? (WIDE ? 40 : 32) : ONE ? 32 : 16;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
     const int tid = threadIdx.x;
@@ -612,7 +616,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int kbw = kb_lo + kw * a.spw;
     // With S > 1 the last wave only runs the cross-slice exchange: it never has
     // weight loads in flight, so its polls are not queued behind them.
-    const bool poller = (a.S > 1) && (wv == NW - 1);
+    const bool poller = !ONE && (a.S > 1) && (wv == NW - 1);
     const bool active = tg < a.TW && !poller;
 
     // LDS: [q: M x ks int8][sums of q][wave partials, two halves]
@@ -736,7 +740,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     for (int d = 0; d < PRIME; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
 
     // 2. activation prologue: per-row statistics of h, then q into LDS
-    if (a.S > 1 && tid == 0) sm.tag = gen + 1u;
+    if (!ONE && a.S > 1 && tid == 0) sm.tag = gen + 1u;
     if (CB && tid < 16) {
         // each level as a bf16 pair hi + lo (|level - hi - lo| <= 2^-17 |level|)
         const float v = a.codebook[tid];
@@ -771,7 +775,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             if (lane == 0) sm.wd[wv] = ss;
             __syncthreads();
             double tot;
-            if (a.S == 1) {
+            if (ONE || a.S == 1) {
                 tot = combine_d(a, sm, mrow);
             } else {
                 if (poller) exchange_poll(a, sm, lane, s, true);
@@ -793,7 +797,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const float mx = wave_max(abs_max<XT, EPT>(h));
             if (lane == 0) sm.wf[wv] = mx;
             __syncthreads();
-            if (a.S == 1) {
+            if (ONE || a.S == 1) {
                 amx = row_max(a, sm, mrow, lane);
             } else {
                 if (poller) exchange_poll(a, sm, lane, s, false);
@@ -1082,7 +1086,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 } else {
                     for (int w = w0; w < w0 + a.KW; ++w) osum += red[(w * 8 + omm) * 16 + onn];
                 }
-                if (a.S == 1) {
+                if (ONE || a.S == 1) {
                     if (ot * TILE_ROWS + onn < a.n)
                         a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (osum * KINV);
                 } else {
@@ -1113,7 +1117,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     }
 
     // 5. merge the slices' partials: the last workgroup of each tile adds them
-    if (a.S > 1) {
+    if (!ONE && a.S > 1) {
         __syncthreads();
         for (int c0 = 0; c0 < ntile; c0 += kMaxTilesPerGroup) {
             const int nc = min(kMaxTilesPerGroup, ntile - c0);
@@ -1162,12 +1166,12 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 
 // Kernel pointer for a format, prologue, activation dtype, groups per 32-k block
 // (gs; 0 = the codebook's G = 16), M = 1 / M >= 2 and the wide activation budget
-// (M >= 2 without a prologue only); nullptr if not built.
+// (M >= 2: no prologue with W4 or W6, RMSNorm with W4); nullptr if not built.
 template <int FMT, int PRO, int XT, int GS, bool DBG>
 KernelFn pick_dot(bool dot4, bool wide) {
     if constexpr (FMT == FMT_CB) {
         return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;   // the codebook runs on MFMA for every M
-    } else if constexpr (PRO == PRO_NONE) {
+    } else if constexpr (PRO == PRO_NONE || (PRO == PRO_RMSNORM && FMT == FMT_W4)) {
         return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>
                : wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true>
                       : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
@@ -1215,7 +1219,7 @@ KernelFn pick_canon_gs(int gs, bool dot4, bool wide) {
 template <int FMT, bool DBG>
 KernelFn pick_format(int pro, int xt, int gs, bool dot4, bool wide) {
     switch (pro) {
-        case PRO_RMSNORM: return pick_xt<FMT, PRO_RMSNORM, DBG>(xt, gs, dot4, false);
+        case PRO_RMSNORM: return pick_xt<FMT, PRO_RMSNORM, DBG>(xt, gs, dot4, wide);
         case PRO_SWIGLU: return pick_xt<FMT, PRO_SWIGLU, DBG>(xt, gs, dot4, false);
         default: return pick_xt<FMT, PRO_NONE, DBG>(xt, gs, dot4, wide);
     }

@@ -213,18 +213,18 @@ def test_rows_do_not_interact_and_runs_repeat():
 # fused prologues
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("m", [1, 3, 5, 8])
 @pytest.mark.parametrize("fmt,g", [(0, 32), (2, 64)])
-def test_fused_rmsnorm(m, fmt, g):
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_fused_rmsnorm(m, fmt, g, xt):
     n, k = 384, 4096
     w, buf = gpu_weight(fmt, n, k, g, 41)
     sk.sk_repack_w4a8(w)
-    x = S.activations(42 + m, m, k) * F32(2.5)
+    x_dev, x = to_dev(S.activations(42 + m, m, k) * F32(2.5), xt)
     gam = S.gamma(43, k)
     eps = 1e-6
-    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_RMSNORM, torch.from_numpy(x).cuda(),
-                                   gamma=torch.from_numpy(gam).cuda(), eps=eps)
-    y_pub = sk.sk_gemm_fused_rmsnorm(w, torch.from_numpy(x).cuda(), torch.from_numpy(gam).cuda(), eps)
+    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_RMSNORM, x_dev, gamma=torch.from_numpy(gam).cuda(), eps=eps)
+    y_pub = sk.sk_gemm_fused_rmsnorm(w, x_dev, torch.from_numpy(gam).cuda(), eps)
     torch.cuda.synchronize()
     h = O.prologue_rmsnorm(x, gam, eps)
     ref = O.reference(fmt, buf, n, k, g, h)
@@ -332,7 +332,13 @@ def test_forced_split_matches_oracle(split, pro, reset_hooks):
         p = sk.gemm_plan(n, k, g, 0, m, prologue=pro)
         sk.set_split(split)
         tpr = (16 // m) * 64
-        ept = 16 if (m == 1 or pro != sk.PRO_NONE) else 32     # activations per thread
+        # the largest budget of activations per thread among the kernel instances
+        if m == 1 or pro == sk.PRO_SWIGLU:
+            ept = 16
+        elif pro == sk.PRO_RMSNORM:
+            ept = 32 if split == 1 else 16           # the one-slice RMSNorm instances
+        else:
+            ept = 40
         if (k // split) // ept > tpr:
             with pytest.raises(sk.SkError):
                 run_prologue(w, pro, k, m, 72 + m)

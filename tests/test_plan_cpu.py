@@ -31,12 +31,20 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert 1 <= S <= 32 and KB % S == 0
     assert p["KBs"] == KB // S and p["KS"] == k // S
     assert p["P"] == S * p["R"] and p["P"] <= 256 and 1 <= p["R"] <= T
-    narrow = m == 1 or pro != sk.PRO_NONE or fmt == sk.SK_W4_CODEBOOK
     ept = p["ept"]
-    assert ept == (16 if narrow else 40 if p["wide"] else 32)
-    if p["wide"] and S == 1:
-        # the 40-activation instances run only where they save K-slices
-        assert k > 32 * 64 * (NW // m)
+    if m == 1 or fmt == sk.SK_W4_CODEBOOK or pro == sk.PRO_SWIGLU or (pro == sk.PRO_RMSNORM and fmt != 0):
+        assert ept == 16 and not p["wide"]
+    elif pro == sk.PRO_RMSNORM:
+        # 32 activations with RMSNorm only in the one-slice instances, and only
+        # where 16 would need a K-split
+        assert ept == (32 if p["wide"] else 16)
+        if p["wide"]:
+            assert S == 1 and k > 16 * 64 * (NW // m)
+    else:
+        assert ept == (40 if p["wide"] else 32)
+        if p["wide"] and S == 1:
+            # the 40-activation instances run only where they save K-slices
+            assert k > 32 * 64 * (NW // m)
     # waves per activation row: as many as the slice needs, at most NW / M
     assert p["WPR"] == min(NW // m, -(-p["KS"] // (ept * 64)))
     assert p["KS"] // ept <= p["WPR"] * 64                 # the slice fits the registers
@@ -106,4 +114,11 @@ def test_forced_split_hook_validates():
 def test_wide_budget_where_measured_faster(n, k, m, S, wide):
     p = sk.gemm_plan(n, k, 32, 0, m)
     assert (p["S"], p["wide"]) == (S, wide), p
+
+
+@pytest.mark.parametrize("m,wide", [(1, 0), (4, 0), (5, 1), (8, 1)])
+def test_rmsnorm_one_slice_budget(m, wide):
+    """RMSNorm + the 9B-class QKV projection: one K-slice at every M."""
+    p = sk.gemm_plan(6144, 4096, 32, 0, m, prologue=sk.PRO_RMSNORM)
+    assert (p["S"], p["wide"]) == (1, wide), p
 
