@@ -360,9 +360,9 @@ def main() -> int:
     ap.add_argument("--profile-calls", type=int, default=0,
                     help="run this many eager steps (no graphs, no timing) and exit: the "
                          "workload for rocprofv3 kernel traces and counters")
-    ap.add_argument("--variants", action="store_true",
-                    help="also time the other workloads (fused prologues, W6 / codebook / "
-                         "lm_head formats, the 27B-class layer) and add them as `variants`")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the other workloads (fused prologues, W6 / codebook / lm_head "
+                         "formats, the 27B-class layer) reported as `variants`")
     ap.add_argument("--no-experts", action="store_true",
                     help="skip the expert-bank workload")
     ap.add_argument("--no-attention", action="store_true",
@@ -574,7 +574,7 @@ def main() -> int:
                           f"({len(os.sched_getaffinity(0))} cores visible)")}
         log(f"cpu oracle: {cpu_s:.1f}s for {nsteps} steps -> {cpu['value']} GB/s")
 
-    variants = time_variants(torch, sk, S, dev, stream) if args.variants else None
+    variants = None if args.no_variants else time_variants(torch, sk, S, dev, stream)
 
     out = {
         "metric": METRIC,
