@@ -571,13 +571,18 @@ Plan make_plan(int m, int hq, int hkv, int len, int cus) {
     if (g_bps_override > 0) {
         bps = g_bps_override;
     } else {
-        // about one workgroup per two compute units over all heads: a
-        // workgroup streams at most ~60 GB/s, so half the units already reach
-        // the HBM rate, and fewer ranges keep the merge short; at least one
-        // block per wave
-        const int per_head = max(1, ((cus > 0 ? cus : 256) / 2 + hkv - 1) / hkv);
+        // About one workgroup per two compute units over all heads: a workgroup
+        // streams at most ~60 GB/s, so half the units already reach the HBM
+        // rate, and fewer ranges keep the merge short.  Ranges hold at least 8
+        // blocks (two per wave), and with two query tiles, which merge in two
+        // rounds, at least 16 from 128 blocks on (measured with Hq 32, Hkv 8 on
+        // 256 units: L = 4096, M = 8 took 16.3 us against 19.1 us with 8-block
+        // ranges, on the same part in alternating runs).
+        const int cu = cus > 0 ? cus : 256;
+        const int per_head = max(1, (cu / 2 + hkv - 1) / hkv);
         bps = (p.nblk + per_head - 1) / per_head;
-        if (bps < AW) bps = AW;
+        const int minb = (p.nqt >= 2 && p.nblk >= 32 * AW) ? 4 * AW : 2 * AW;
+        if (bps < minb) bps = minb;
     }
     if (bps > p.nblk) bps = p.nblk;
     if ((p.nblk + bps - 1) / bps > kMaxSplits) bps = (p.nblk + kMaxSplits - 1) / kMaxSplits;
