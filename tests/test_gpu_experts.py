@@ -59,7 +59,7 @@ def test_expert_bank_single_expert_and_long_k():
     _, _, buf = S.make_weight(0, n, k, g, 1220, 1221)
     bank = sk.QuantWeight(torch.from_numpy(buf.copy()).cuda(), n, k, g, 0)
     sk.sk_repack_w4a8(bank)
-    for m in (1, 8):
+    for m in (1, 3, 8):                    # M = 3: one K-slice with 40 activations per thread
         h = S.activations(1222 + m, m, k)
         y = sk.sk_gemm_experts(bank, rows, [2], torch.from_numpy(h).cuda()).cpu().numpy()
         ref = O.reference(0, expert_rows(buf, 0, n, k, g, 2, rows), rows, k, g, h)
