@@ -129,3 +129,14 @@ def test_split_override():
         sk.set_attention_split(0)
     with pytest.raises(sk.SkError):
         sk.set_attention_split(-1)
+
+
+# Plans measured on the MI355X (Hq 32, Hkv 8, 256 units): about one workgroup per
+# two units, ranges of at least 8 blocks, and at least 16 for two query tiles
+# from 128 blocks on.
+@pytest.mark.parametrize("m,length,plan", [
+    (1, 2048, (8, 8)), (8, 2048, (8, 8)), (1, 4096, (16, 8)), (8, 4096, (8, 16)),
+    (1, 16384, (16, 32)), (8, 16384, (16, 32)), (1, 32768, (16, 64)), (8, 32768, (16, 64)),
+])
+def test_plan_for_measured_lengths(m, length, plan):
+    assert sk.attention_plan(m, 32, 8, length, 256) == plan
