@@ -149,11 +149,13 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     const bool cb = G.fmt == FMT_CB;
     const bool dot4 = (m == 1) && !cb;
     // Each thread quantises at most 16 activations of its row, 32 for M >= 2
-    // without a prologue; the wide instances take 40 (no prologue) or 32
+    // without a prologue (the codebook included); the wide instances take 40
+    // (integer formats without a prologue) or 32
     // (RMSNorm with 4-bit weights, one K-slice only) and are used only where
     // that needs fewer K-slices.  (The split path's PRO_QIN keeps PRO_NONE's
     // plan, so the two compare like for like.)
-    if (dot4 || cb || pro == PRO_SWIGLU) return plan_for(G, m, cus, split_override, 16);
+    if (dot4 || pro == PRO_SWIGLU || (cb && pro != PRO_NONE)) return plan_for(G, m, cus, split_override, 16);
+    if (cb) return plan_for(G, m, cus, split_override, 32);   // no wide codebook instances
     if (pro == PRO_RMSNORM) {
         if (G.fmt != FMT_W4) return plan_for(G, m, cus, split_override, 16);
         const Plan p = plan_for(G, m, cus, split_override, 16);

@@ -16,7 +16,8 @@ SHAPES = [
     (1024, 1024, 32, 0), (6144, 4096, 32, 0), (4096, 4096, 32, 0), (24576, 4096, 32, 0),
     (4096, 12288, 32, 0), (12288, 4096, 64, 2), (151936, 4096, 32, 0), (7168, 5120, 32, 0),
     (5120, 5120, 32, 0), (34816, 5120, 32, 0), (5120, 17408, 32, 0), (17, 256, 64, 0),
-    (5, 128, 128, 0), (1000, 512, 32, 0), (300, 1024, 64, 2),
+    (5, 128, 128, 0), (1000, 512, 32, 0), (300, 1024, 64, 2), (12288, 4096, 16, 1),
+    (2048, 12288, 32, 1),
 ]
 
 
@@ -32,7 +33,10 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert p["KBs"] == KB // S and p["KS"] == k // S
     assert p["P"] == S * p["R"] and p["P"] <= 256 and 1 <= p["R"] <= T
     ept = p["ept"]
-    if m == 1 or fmt == sk.SK_W4_CODEBOOK or pro == sk.PRO_SWIGLU or (pro == sk.PRO_RMSNORM and fmt != 0):
+    if fmt == sk.SK_W4_CODEBOOK:
+        # the codebook runs the MFMA path at every M; 32 without a prologue
+        assert ept == (32 if pro == sk.PRO_NONE else 16) and not p["wide"]
+    elif m == 1 or pro == sk.PRO_SWIGLU or (pro == sk.PRO_RMSNORM and fmt != 0):
         assert ept == 16 and not p["wide"]
     elif pro == sk.PRO_RMSNORM:
         # 32 activations with RMSNorm only in the one-slice instances, and only
