@@ -485,6 +485,8 @@ def main() -> int:
     log(f"timed {args.steps} steps: {elapsed_ms:.3f} ms, {ms_per_step * 1e3:.2f} us/step, {value:.0f} GB/s")
 
     # ---------------- per (linear, M) µs/call ----------------
+    spread = {}                    # (linear, M) -> (p10, p90) of the 7 replays
+
     def time_calls(name, m, reps=4):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -493,7 +495,7 @@ def main() -> int:
         g.replay()
         torch.cuda.synchronize()
         best = []
-        for _ in range(3):
+        for _ in range(7):
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -501,6 +503,7 @@ def main() -> int:
             b.record(stream)
             torch.cuda.synchronize()
             best.append(a.elapsed_time(b) * 1e3 / (reps * R))
+        spread[(name, m)] = (float(np.percentile(best, 10)), float(np.percentile(best, 90)))
         return float(np.median(best))
 
     ms_list = (1, 8) if args.no_sweep else tuple(range(1, 9))
@@ -510,6 +513,7 @@ def main() -> int:
             us = time_calls(name, m)
             b = alg_bytes(n, k, m)
             per.append({"linear": name, "n": n, "k": k, "m": m, "us_per_call": round(us, 3),
+                        "us_p10": round(spread[(name, m)][0], 3), "us_p90": round(spread[(name, m)][1], 3),
                         "GBps": round(b / (us * 1e-6) / 1e9, 1),
                         "frac_peak": round(b / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)})
             log(f"{name:8s} M={m}: {us:8.3f} us/call  {per[-1]['GBps']:7.1f} GB/s  "
