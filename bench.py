@@ -506,6 +506,40 @@ def main() -> int:
         spread[(name, m)] = (float(np.percentile(best, 10)), float(np.percentile(best, 90)))
         return float(np.median(best))
 
+    # the streaming-read probe on the same rotated weight buffers: the best of a
+    # few launch shapes, as the ceiling a kernel reading those bytes can reach
+    probe_out = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def time_probe(name, reps=4):
+        best_us = None
+        for grid in (256, 512, 1024, 2048):
+            for threads in (256, 1024):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for r in range(reps * R):
+                        sk.stream_read(weights[name][r % R].data, grid, threads, probe_out)
+                g.replay()
+                torch.cuda.synchronize()
+                t = []
+                for _ in range(3):
+                    a = torch.cuda.Event(enable_timing=True)
+                    b = torch.cuda.Event(enable_timing=True)
+                    a.record(stream)
+                    g.replay()
+                    b.record(stream)
+                    torch.cuda.synchronize()
+                    t.append(a.elapsed_time(b) * 1e3 / (reps * R))
+                us = float(np.median(t))
+                best_us = us if best_us is None else min(best_us, us)
+        return best_us
+
+    probe = {}
+    for name, n, k in SHAPES:
+        probe[name] = time_probe(name)
+        nb = weights[name][0].data.numel()
+        log(f"probe    {name:8s}: {probe[name]:8.3f} us to read its {nb / 1e6:.1f} MB of weights "
+            f"({nb / (probe[name] * 1e-6) / 1e9:.0f} GB/s)")
+
     ms_list = (1, 8) if args.no_sweep else tuple(range(1, 9))
     per = []
     for name, n, k in SHAPES:
@@ -515,9 +549,11 @@ def main() -> int:
             per.append({"linear": name, "n": n, "k": k, "m": m, "us_per_call": round(us, 3),
                         "us_p10": round(spread[(name, m)][0], 3), "us_p90": round(spread[(name, m)][1], 3),
                         "GBps": round(b / (us * 1e-6) / 1e9, 1),
-                        "frac_peak": round(b / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)})
+                        "frac_peak": round(b / (us * 1e-6) / 1e9 / PEAK_GBPS, 4),
+                        "probe_us": round(probe[name], 3),
+                        "frac_of_probe": round(probe[name] / us, 4)})
             log(f"{name:8s} M={m}: {us:8.3f} us/call  {per[-1]['GBps']:7.1f} GB/s  "
-                f"({100 * per[-1]['frac_peak']:.1f}% of peak)")
+                f"({100 * per[-1]['frac_peak']:.1f}% of peak, {100 * per[-1]['frac_of_probe']:.0f}% of the probe)")
 
     def agg(m):
         rows = [p for p in per if p["m"] == m]

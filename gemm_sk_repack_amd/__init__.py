@@ -38,7 +38,7 @@ EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4
            "sk_gemm_w4a8_canonical_q",
            "sk_debug_gemm",
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
-           "sk_test_set_spin_limit",
+           "sk_test_set_spin_limit", "sk_test_stream_read",
            "sk_kv_append", "sk_decode_attention", "sk_kv_pack_host",
            "sk_test_attention_plan", "sk_test_set_attention_split",
            "sk_mtp_create", "sk_mtp_destroy", "sk_mtp_observe", "sk_mtp_layout", "sk_mtp_layout_of",
@@ -82,6 +82,7 @@ def _load() -> ctypes.CDLL:
         "sk_test_gemm_plan": ([I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_int64)], I),
         "sk_test_set_split": ([I], I),
         "sk_test_set_spin_limit": ([I], I),
+        "sk_test_stream_read": ([P, I64, I, I, P, P], I),
         "sk_kv_append": ([P, I, I, I, I, P, P, P], I),
         "sk_decode_attention": ([P, I, I, I, P, I, I, F, P, P], I),
         "sk_kv_pack_host": ([P, P, I, I, I, P], I),
@@ -294,6 +295,12 @@ def gemm_plan(n: int, k: int, group: int, fmt: int, m: int, cus: int = 256,
 def set_split(s: int) -> None:
     """Test hook: force the number of K-slices (0 = automatic)."""
     _check(LIB.sk_test_set_split(s), "sk_test_set_split")
+
+
+def stream_read(buf: torch.Tensor, grid: int, threads: int, out: torch.Tensor, stream=None) -> None:
+    """Test hook: the streaming-read probe over the bytes of `buf` (see sk_repack_test.h)."""
+    _check(LIB.sk_test_stream_read(_ptr(buf), buf.numel() * buf.element_size(), grid, threads,
+                                   _ptr(out), _stream(stream)), "sk_test_stream_read")
 
 
 def set_spin_limit(polls: int) -> None:

@@ -51,6 +51,17 @@ sk_status sk_test_set_split(int s);
  * forces the local path, which must give identical results. */
 sk_status sk_test_set_spin_limit(int polls);
 
+/* Streaming-read probe, the reference ceiling for the GEMM's weight stream:
+ * `grid` workgroups of `threads` threads (64..1024, a multiple of 64) read the
+ * device buffer `buf` of `bytes` bytes (16-byte aligned, a multiple of 16) once
+ * with 16-byte loads, each workgroup a contiguous share, eight loads in flight
+ * per thread, and fold it into one word; `out` (device, 4 bytes) is written only
+ * if the fold equals a fixed value, so the reads cannot be elided.  Errors: NULL,
+ * SHAPE (bytes < 16 or not a multiple of 16, grid < 1, threads outside
+ * 64..1024 or not a multiple of 64), ALIGN, HIP. */
+sk_status sk_test_stream_read(const void* buf, int64_t bytes, int grid, int threads,
+                              uint32_t* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

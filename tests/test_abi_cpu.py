@@ -156,3 +156,17 @@ def test_failed_call_leaves_descriptor_unchanged():
     w = W(layout=0, data=FAKE + 8)
     assert sk.LIB.sk_repack_w4a8(ctypes.byref(w), None) == sk.SK_ERR_ALIGN
     assert w.layout == 0
+
+
+def test_stream_read_probe_validation():
+    """The probe's checks run on the host before any launch (no GPU needed)."""
+    f = sk.LIB.sk_test_stream_read
+    fake = 1 << 20                                     # never dereferenced: every call is rejected
+    assert f(None, 1024, 256, 256, fake, None) == sk.SK_ERR_NULL
+    assert f(fake, 1024, 256, 256, None, None) == sk.SK_ERR_NULL
+    assert f(fake, 1000, 256, 256, fake, None) == sk.SK_ERR_SHAPE
+    assert f(fake, 0, 256, 256, fake, None) == sk.SK_ERR_SHAPE
+    assert f(fake, 1024, 0, 256, fake, None) == sk.SK_ERR_SHAPE
+    assert f(fake, 1024, 256, 96, fake, None) == sk.SK_ERR_SHAPE
+    assert f(fake, 1024, 256, 2048, fake, None) == sk.SK_ERR_SHAPE
+    assert f(fake + 4, 1024, 256, 256, fake, None) == sk.SK_ERR_ALIGN
