@@ -154,6 +154,16 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     // (RMSNorm with 4-bit weights, one K-slice only) and are used only where
     // that needs fewer K-slices.  (The split path's PRO_QIN keeps PRO_NONE's
     // plan, so the two compare like for like.)
+    if (dot4 && (pro == PRO_NONE || pro == PRO_QIN)) {
+        // M = 1 on v_dot4: 16, or 24 in the wide instances where that saves slices
+        const Plan p = plan_for(G, m, cus, split_override, 16);
+        Plan w = plan_for(G, m, cus, split_override, 24);
+        if (w.ok && (!p.ok || w.S < p.S)) {
+            w.wide = true;
+            return w;
+        }
+        return p;
+    }
     if (dot4 || pro == PRO_SWIGLU || (cb && pro != PRO_NONE)) return plan_for(G, m, cus, split_override, 16);
     if (cb) return plan_for(G, m, cus, split_override, 32);   // no wide codebook instances
     if (pro == PRO_RMSNORM) {

@@ -553,12 +553,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     constexpr float KINV = CB ? 1.0f : (FMT == FMT_W6) ? 0.25f : 0.0625f;
     // Activations per thread: 32 only where the registers allow it.  The wide
     // instances (used only where they save K-slices: their larger prologue code
-    // costs the other calls time) take 40 without a prologue, and 32 with the
+    // costs the other calls time) take 40 without a prologue (24 at M = 1 on
+    // v_dot4, which lets K = 17408 run as one slice), and 32 with the
     // RMSNorm prologue for a single K-slice and 4-bit weights: compiling out the
     // cross-slice exchange (ONE) is what makes room for the latter (the 6-bit
     // unpack needs a few registers more than are left).
-    constexpr bool ONE = WIDE && PRO == PRO_RMSNORM;
-    constexpr int EPT = DOT4 ? 16 : PRO == PRO_NONE ? (WIDE ? 40 : 32) : ONE ? 32 : 16;
+    constexpr bool ONE = WIDE && PRO == PRO_RMSNORM && !DOT4;
+    constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : PRO == PRO_NONE ? (WIDE ? 40 : 32) : ONE ? 32 : 16;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
     const int tid = threadIdx.x;
@@ -1171,7 +1172,13 @@ template <int FMT, int PRO, int XT, int GS, bool DBG>
 KernelFn pick_dot(bool dot4, bool wide) {
     if constexpr (FMT == FMT_CB) {
         return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;   // the codebook runs on MFMA for every M
-    } else if constexpr (PRO == PRO_NONE || (PRO == PRO_RMSNORM && FMT == FMT_W4)) {
+    } else if constexpr (PRO == PRO_NONE) {
+        if (dot4)
+            return wide ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, true>
+                        : gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>;
+        return wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true>
+                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
+    } else if constexpr (PRO == PRO_RMSNORM && FMT == FMT_W4) {
         return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>
                : wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true>
                       : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
@@ -1202,6 +1209,7 @@ template <int PRO, int XT, int GS>
 KernelFn pick_canon_dot(bool dot4, bool wide) {
     if constexpr (PRO == PRO_NONE) {
         if (!dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, true>;
+        if (dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, true>;
     }
     return dot4 ? gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, false>
                 : gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, false>;

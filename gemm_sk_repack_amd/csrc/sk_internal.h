@@ -68,8 +68,8 @@ struct Plan {
     int KBs;      // super-blocks per slice
     int KS;       // K per slice
     int WPR;      // waves per activation row in the prologue
-    int ept;      // activations per thread (16; 32 or 40 for M >= 2 without a prologue)
-    bool wide;    // ept = 40: the kernel instances with the larger activation budget
+    int ept;      // activations per thread (16, 24, 32 or 40)
+    bool wide;    // the kernel instances with the larger activation budget
     int ks;       // LDS row stride of q
     size_t lds;   // dynamic LDS bytes
     size_t part_floats;  // workspace floats for slice partials

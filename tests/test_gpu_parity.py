@@ -115,6 +115,9 @@ GEMM_CASES = [
     (0, 528, 5120, 32, (6, 8)),
     (2, 272, 5120, 64, (7, 8)),
     (0, 300, 12288, 32, (3,)),
+    # M = 1 with 24 activations per thread (K = 17408 in one slice)
+    (0, 96, 17408, 32, (1, 2)),
+    (2, 48, 17408, 64, (1,)),
 ]
 
 

@@ -54,7 +54,7 @@ def test_quantize_rows_ties_take_exact_division():
 
 CASES = [(640, 2048, 32, (1, 2, 8)), (1000, 4096, 64, (1, 8)), (392, 4096, 128, (1, 5)),
          (2048, 12288, 32, (1, 8)), (6144, 4096, 32, (1, 8)), (1040, 5120, 32, (6, 8)),
-         (512, 12288, 32, (3,))]
+         (512, 12288, 32, (3,)), (256, 17408, 32, (1,))]
 
 
 @pytest.mark.parametrize("n,k,g,ms", CASES)

@@ -36,6 +36,11 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     if fmt == sk.SK_W4_CODEBOOK:
         # the codebook runs the MFMA path at every M; 32 without a prologue
         assert ept == (32 if pro == sk.PRO_NONE else 16) and not p["wide"]
+    elif m == 1 and pro == sk.PRO_NONE:
+        # v_dot4: 16, or 24 in the wide instances where that saves K-slices
+        assert ept == (24 if p["wide"] else 16)
+        if p["wide"] and S == 1:
+            assert k > 16 * 64 * NW
     elif m == 1 or pro == sk.PRO_SWIGLU or (pro == sk.PRO_RMSNORM and fmt != 0):
         assert ept == 16 and not p["wide"]
     elif pro == sk.PRO_RMSNORM:
@@ -107,13 +112,14 @@ def test_forced_split_hook_validates():
     sk.set_split(0)
 
 
-# Plans measured on the MI355X: the 40-activation instances where they remove or
-# halve the K-split (27B-class linears at M >= 6, K = 12288 at M = 3, K = 17408),
-# the 32-activation ones where the slice already fits.
+# Plans measured on the MI355X: the wide instances where they remove or halve the
+# K-split (27B-class linears at M >= 6, K = 12288 at M = 3, K = 17408 at M = 1, 2
+# and M >= 6), the others where the slice already fits.
 @pytest.mark.parametrize("n,k,m,S,wide", [
     (6144, 4096, 8, 1, 0), (4096, 4096, 8, 1, 0), (24576, 4096, 8, 1, 0), (4096, 12288, 8, 4, 0),
     (4096, 12288, 3, 1, 1), (4096, 12288, 2, 1, 0), (7168, 5120, 8, 1, 1), (5120, 5120, 6, 1, 1),
     (34816, 5120, 8, 1, 1), (7168, 5120, 5, 1, 0), (5120, 17408, 8, 4, 1), (5120, 17408, 2, 1, 1),
+    (5120, 17408, 1, 1, 1), (4096, 12288, 1, 1, 0),
 ])
 def test_wide_budget_where_measured_faster(n, k, m, S, wide):
     p = sk.gemm_plan(n, k, 32, 0, m)
