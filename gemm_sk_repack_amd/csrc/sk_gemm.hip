@@ -148,12 +148,12 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
 Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     const bool cb = G.fmt == FMT_CB;
     const bool dot4 = (m == 1) && !cb;
-    // Each thread quantises at most 16 activations of its row, 32 for M >= 2
-    // without a prologue (the codebook included); the wide instances take 40
-    // (integer formats without a prologue) or 32
-    // (RMSNorm with 4-bit weights, one K-slice only) and are used only where
-    // that needs fewer K-slices.  (The split path's PRO_QIN keeps PRO_NONE's
-    // plan, so the two compare like for like.)
+    // Each thread quantises at most 16 activations of its row (M = 1 on v_dot4,
+    // or a prologue), 32 on the MFMA path without a prologue (the codebook
+    // included); the wide instances take 24 (v_dot4), 40 (MFMA, integer formats,
+    // no prologue) or 32 (RMSNorm with 4-bit weights, one K-slice only) and are
+    // used only where that needs fewer K-slices.  (The split path's PRO_QIN
+    // keeps PRO_NONE's plan, so the two compare like for like.)
     if (dot4 && (pro == PRO_NONE || pro == PRO_QIN)) {
         // M = 1 on v_dot4: 16, or 24 in the wide instances where that saves slices
         const Plan p = plan_for(G, m, cus, split_override, 16);

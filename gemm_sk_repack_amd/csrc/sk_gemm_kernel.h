@@ -551,13 +551,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // byte), so sign extension is free; the sums are scaled back at the store.
     constexpr int WSH = (FMT == FMT_W6) ? 2 : 4;
     constexpr float KINV = CB ? 1.0f : (FMT == FMT_W6) ? 0.25f : 0.0625f;
-    // Activations per thread: 32 only where the registers allow it.  The wide
-    // instances (used only where they save K-slices: their larger prologue code
-    // costs the other calls time) take 40 without a prologue (24 at M = 1 on
-    // v_dot4, which lets K = 17408 run as one slice), and 32 with the
-    // RMSNorm prologue for a single K-slice and 4-bit weights: compiling out the
-    // cross-slice exchange (ONE) is what makes room for the latter (the 6-bit
-    // unpack needs a few registers more than are left).
+    // Activations per thread: 16 on v_dot4 or with a prologue, 32 on the MFMA
+    // path without one.  The wide instances (used only where they save
+    // K-slices: their larger prologue code costs the other calls time) take 24
+    // on v_dot4 (K = 17408 in one slice), 40 on the MFMA path without a
+    // prologue, and 32 with the RMSNorm prologue for a single K-slice and 4-bit
+    // weights: compiling out the cross-slice exchange (ONE) is what makes room
+    // for the latter (the 6-bit unpack needs a few registers more than are left).
     constexpr bool ONE = WIDE && PRO == PRO_RMSNORM && !DOT4;
     constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : PRO == PRO_NONE ? (WIDE ? 40 : 32) : ONE ? 32 : 16;
     constexpr int E = Act<XT, EPT>::E;
