@@ -265,9 +265,10 @@ def time_ablation(torch, sk, stream, host, xs, R, per):
 
 
 def time_variants(torch, sk, S, dev, stream):
-    """The other workloads: fused prologues at hidden 4096, the W6 / codebook /
-    lm_head formats at K = 4096, and one 27B-class layer (bf16 activations) whose
-    64-layer step time is extrapolated from that layer."""
+    """The other workloads: the single 1024 x 1024 linear, fused prologues at
+    hidden 4096, the W6 / codebook / lm_head formats at K = 4096, and one
+    27B-class layer (bf16 activations) whose 64-layer step time is extrapolated
+    from that layer."""
     rows = []
 
     def weight_copies(fmt, n, k, g, cfg, li):
@@ -292,6 +293,16 @@ def time_variants(torch, sk, S, dev, stream):
                      "us_per_call": round(us, 3), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
                      "frac_peak": round(alg / (us * 1e-6) / 1e9 / PEAK_GBPS, 4)})
         log(f"{group:10s} {name:12s} M={m}: {us:8.3f} us/call {rows[-1]['GBps']:7.1f} GB/s")
+
+    # the single small linear (N = K = 1024, 0.66 MB): latency-bound and
+    # cache-resident, so reported in µs (its GB/s is not a bandwidth figure)
+    cps, nb = weight_copies(sk.SK_W4_SYM, 1024, 1024, 32, 0, 0)
+    for m in (1, 8):
+        x = torch.from_numpy(S.activations(S.seed_of(0, 0, S.TENSOR_X), m, 1024)).to(dev)
+        y = torch.empty((m, 1024), dtype=torch.float32, device=dev)
+        us = time_graph(torch, stream, lambda i: sk.sk_gemm_w4a8(cps[i % len(cps)], x, y=y), 4 * len(cps))
+        record("small", "1024x1024", 1024, 1024, 32, 0, m, us, nb)
+    del cps
 
     # fused prologues at hidden 4096
     cps, nb = weight_copies(sk.SK_W4_SYM, 6144, 4096, 32, 3, 0)
