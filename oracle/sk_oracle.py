@@ -22,8 +22,9 @@ Readings where the pages are silent:
 * Canonical bit encodings (the format table is missing from the page): see
   ``decode_w4``, ``decode_w6``, ``decode_u4``.
 * Activation quantisation is per row (token): a = max|h|, sx = a/127 (fp32
-  division), q = clamp(round-half-even(fp32(h/sx)), -127, 127); an all-zero
-  row gives sx = 0 and q = 0.
+  division), q = clamp(round-half-even(fp32(h/sx)), -127, 127); a row whose
+  sx is 0 (all zeros, or an absmax so small that absmax/127 rounds to 0 in
+  fp32) gets q = 0: with a zero scale every code dequantises to 0.
 * RMSNorm h = (x * r) * gamma with r = 1/sqrt(mean(x^2) + eps); the sum of
   squares in float64, everything else fp32 with each operation rounded once.
 * SwiGLU h = (g / (1 + e^-g)) * u with e^x evaluated by ``sk_expf`` below, a
@@ -223,7 +224,10 @@ def quantize_rows(h: np.ndarray):
     """Per-row symmetric int8 quantisation.
 
     a = max_k |h|; sx = fp32(a / 127); q = clamp(rint(fp32(h / sx)), -127, 127)
-    with rint rounding half to even.  A row with a == 0 gives sx = 0, q = 0.
+    with rint rounding half to even.  A row whose sx is 0 gets q = 0: the
+    all-zero row, and a nonzero row with a < 127 * 2^-150, whose quotient
+    a/127 rounds to 0 in fp32 (the formula would divide by zero; with a zero
+    scale every code dequantises to 0, so 0 is the one consistent code).
     Returns (q int8 [M,K], sx float32 [M]).
     """
     h = np.asarray(h, dtype=F32)
@@ -231,7 +235,7 @@ def quantize_rows(h: np.ndarray):
     a = np.max(np.abs(h), axis=1) if h.shape[1] else np.zeros(h.shape[0], F32)
     sx = (a / F32(127.0)).astype(F32)
     q = np.zeros(h.shape, dtype=np.int8)
-    nz = a > 0
+    nz = sx > 0
     if np.any(nz):
         t = (h[nz] / sx[nz][:, None]).astype(F32)
         q[nz] = np.clip(np.rint(t), -127, 127).astype(np.int8)
@@ -274,14 +278,22 @@ def output(partials: np.ndarray, s: np.ndarray, sx: np.ndarray) -> np.ndarray:
 
 
 def output_magnitude(partials: np.ndarray, s: np.ndarray, sx: np.ndarray) -> np.ndarray:
-    """sx[m] * sum_j |s[n, j] * P[m, n, j]|: the scale Y's rounding error is measured against."""
+    """sx[m] * sum_j |s[n, j] * P[m, n, j]|: the scale Y's rounding error is measured against.
+
+    Reading of the "max relative error" bound on Y: Y is a signed sum of K/G
+    terms and may sit near zero, so the error is normalised by the sum of the
+    terms' magnitudes, each |s * P| (the absolute value covers the scale too).
+    """
     p = np.abs(np.asarray(partials, dtype=np.float64))
-    s64 = np.asarray(s, dtype=F32).astype(np.float64)
+    s64 = np.abs(np.asarray(s, dtype=F32).astype(np.float64))
     return np.asarray(sx, dtype=F32).astype(np.float64)[:, None] * np.sum(p * s64[None], axis=2)
 
 
 def codebook_magnitude(u, cb, q, s, sx, g: int) -> np.ndarray:
-    """Like output_magnitude for the codebook: sx * sum_j s * sum_{k in j} |cb[u] * q|."""
+    """Like output_magnitude for the codebook: sx * sum_j |s| * sum_{k in j} |cb[u] * q|.
+
+    The codebook's group sums have no exact integer form, so every product
+    cb[u] * q counts with its own magnitude."""
     lv = np.abs(np.asarray(cb, dtype=F32).astype(np.float64)[np.asarray(u, dtype=np.int64)])
     aq = np.abs(np.asarray(q, dtype=np.float64))
     n, k = lv.shape

@@ -28,6 +28,16 @@ def test_w4_bytes_fixture():
     assert np.array_equal(S.pack_w4(vals), byts)
 
 
+def test_u4_bytes_fixture():
+    g = load_golden("w4_w6_bytes.txt")
+    vals = np.array(g["u4_values"][0], dtype=np.int64)[None]
+    byts = np.array(g["u4_bytes"][0], dtype=np.uint8)[None]
+    assert np.array_equal(O.decode_u4(byts, vals.shape[1]), vals)
+    assert np.array_equal(S.pack_u4(vals), byts)
+    # the same bytes read as W4 are the two's-complement values of the indices
+    assert np.array_equal(O.decode_w4(byts, vals.shape[1]), np.where(vals >= 8, vals - 16, vals))
+
+
 def test_w6_bytes_fixture():
     g = load_golden("w4_w6_bytes.txt")
     vals = np.array(g["w6_values"][0], dtype=np.int64)[None]
@@ -115,6 +125,17 @@ def test_quant_zero_and_constant_rows():
     assert sx[0] == 0 and np.all(q[0] == 0)
     assert np.all(q[1] == -127)
     assert q[2, 5] == 127 and np.count_nonzero(q[2]) == 1
+
+
+def test_quant_example_e_subnormal_scales():
+    g = load_golden("quant_examples.txt")
+    u = 2.0 ** -149
+    for key in ("e1", "e2"):
+        x = (np.array(g[key + "_x_units"], dtype=np.float64) * u).astype(F32)
+        assert np.array_equal(x[0].astype(np.float64) / u, np.array(g[key + "_x_units"][0]))  # exact
+        q, sx = O.quantize_rows(x)
+        assert float(sx[0]) == g[key + "_sx_units"][0][0] * u
+        assert q.tolist() == g[key + "_q"]
 
 
 def test_quant_power_of_two_scaling_exact():
@@ -343,3 +364,89 @@ def test_rmsnorm_sum_of_squares_is_float64():
     assert r != 1.0 / 64
     assert abs(r - 1.0 / np.sqrt(4097.0)) <= 2 * float(np.spacing(F32(r)))
     assert float(h[0, 0]) == 4096.0 * r          # multiplying by 2^12 is exact
+
+
+# ----------------------------------------------------------------------------
+# the normaliser of Y's error (reading of the "max relative error" bound)
+# ----------------------------------------------------------------------------
+
+def _example_c():
+    g = load_golden("quant_examples.txt")
+    x = np.array(g["c_x"], dtype=F32)
+    q, sx = O.quantize_rows(x)
+    w = np.array([g["c_w0"][0], g["c_w1"][0]], dtype=np.int64)
+    return g, x, q, sx, w
+
+
+def test_output_magnitude_example_c():
+    g, x, q, sx, w = _example_c()
+    s = np.array([g["c_s0"][0], g["c_s1"][0]], dtype=F32)
+    p = O.group_partials(w, q, 8)
+    mag = O.output_magnitude(p, s, sx)
+    assert np.array_equal(mag[0], float(sx[0]) * np.array(g["c_mag_over_sx"][0]))
+    # a negative scale: the normaliser keeps |s * P|, while Y changes sign
+    s_neg = np.array([g["c_s0"][0], g["c_s1_neg"][0]], dtype=F32)
+    mag_neg = O.output_magnitude(p, s_neg, sx)
+    assert np.array_equal(mag_neg[0], float(sx[0]) * np.array(g["c_mag_neg_over_sx"][0]))
+    y_neg = O.output(p, s_neg, sx)
+    assert y_neg[0, 1] == -float(sx[0]) * 2734.0
+    # through the whole-call path the same normaliser is returned
+    buf = S.canonical_buffer(S.pack_w4(w), s)
+    assert np.array_equal(O.reference(0, buf, 2, 16, 8, x)["mag"], mag)
+
+
+def test_output_magnitude_closed_forms():
+    # all-ones weights and scales: mag = sx * sum_j |sum_{k in j} q|, >= |Y| with
+    # equality exactly when every group sum has the row's sign
+    n, k, g = 5, 256, 32
+    h = S.activations(44, 3, k)
+    h[1] = np.abs(h[1])                          # row 1: every q >= 0
+    ref = O.reference(0, S.canonical_buffer(S.pack_w4(np.ones((n, k), np.int64)),
+                                            np.ones((n, k // g), F32)), n, k, g, h)
+    q = ref["q"].astype(np.int64).reshape(3, k // g, g).sum(-1)
+    want = ref["sx"].astype(np.float64) * np.abs(q).sum(1)
+    assert np.array_equal(ref["mag"], np.repeat(want[:, None], n, axis=1))
+    assert np.all(ref["mag"] >= np.abs(ref["Y"]))
+    assert np.array_equal(ref["mag"][1], np.abs(ref["Y"][1]))
+    # scaling every s by 2^j scales the normaliser by 2^j; zero rows give 0
+    h0 = np.zeros((1, k), F32)
+    _, _, buf = S.make_weight(0, n, k, g, 45, 46)
+    assert np.all(O.reference(0, buf, n, k, g, h0)["mag"] == 0)
+
+
+def test_codebook_magnitude_example_d():
+    g, x, q, sx, _ = _example_c()
+    u = np.array(g["d_u"], dtype=np.int64)
+    cb = np.array(g["d_cb"][0], dtype=F32)
+    s = np.array(g["d_s"], dtype=F32)
+    f = O.codebook_partials(u, cb, q, 8)
+    assert f.reshape(-1).tolist() == g["d_f"][0]
+    assert np.array_equal(O.output(f, s, sx)[0], float(sx[0]) * np.array(g["d_y_over_sx"][0]))
+    mag = O.codebook_magnitude(u, cb, q, s, sx, 8)
+    assert np.array_equal(mag[0], float(sx[0]) * np.array(g["d_mag_over_sx"][0]))
+    # the whole-call path on the canonical buffer gives the same values
+    buf = S.canonical_buffer(S.pack_u4(u), s)
+    ref = O.reference(1, buf, 1, 16, 8, x, cb)
+    assert np.array_equal(ref["F"], f) and np.array_equal(ref["mag"], mag)
+
+
+def test_codebook_magnitude_reduces_to_integer_form():
+    # integer levels -8..7: each |level * q| is |w * q|, so the codebook
+    # normaliser is sx * sum_j |s| * sum_k |w q| >= the integer one (|sum| <= sum||)
+    n, k, g = 16, 256, 16
+    u = S.codes_u4(74, n, k)
+    s = S.scales(75, n, k // g)
+    h = S.activations(76, 2, k)
+    cbr = O.reference(1, S.canonical_buffer(S.pack_u4(u), s), n, k, g, h,
+                      np.arange(-8, 8, dtype=F32))
+    w = u.astype(np.int64) - 8
+    q = cbr["q"].astype(np.int64)
+    brute = np.zeros((2, n))
+    for mi in range(2):
+        for ni in range(n):
+            brute[mi, ni] = float(cbr["sx"][mi]) * sum(
+                float(s[ni, j]) * sum(abs(int(w[ni, kk]) * int(q[mi, kk])) for kk in range(j * g, (j + 1) * g))
+                for j in range(k // g))
+    assert np.allclose(cbr["mag"], brute, rtol=1e-14, atol=0)
+    w4 = O.reference(0, S.canonical_buffer(S.pack_w4(w), s), n, k, g, h)
+    assert np.all(cbr["mag"] >= w4["mag"])
