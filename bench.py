@@ -121,11 +121,12 @@ def time_experts(torch, sk, S, stream):
     out = []
     for m, nl in ((1, 2), (8, 8)):
         lists = [sorted(rng.choice(E, nl, replace=False).tolist()) for _ in range(16)]
+        dlists = [torch.tensor(lst, dtype=torch.int32, device=dev) for lst in lists]
         x = torch.from_numpy(S.activations(S.seed_of(5, m, S.TENSOR_X), m, k)).to(dev)
         y = torch.empty((m, nl * rows), dtype=torch.float32, device=dev)
         ys = [torch.empty((m, rows), dtype=torch.float32, device=dev) for _ in range(nl)]
         us_bank = time_graph(torch, stream,
-                             lambda i: sk.sk_gemm_experts(banks[i % R], rows, lists[i % 16], x, y=y), 4 * R)
+                             lambda i: sk.sk_gemm_experts(banks[i % R], rows, dlists[i % 16], x, y=y), 4 * R)
 
         def separate(i):
             for j, e in enumerate(lists[i % 16]):

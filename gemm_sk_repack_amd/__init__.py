@@ -24,7 +24,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsk_repack.so")
 
 SK_OK, SK_ERR_NULL, SK_ERR_SHAPE, SK_ERR_ALIGN, SK_ERR_FORMAT, SK_ERR_LAYOUT, SK_ERR_HIP, \
-    SK_ERR_UNSUPPORTED = range(8)
+    SK_ERR_UNSUPPORTED, SK_ERR_WORKSPACE = range(9)
 SK_F32, SK_BF16 = 0, 1
 SK_W4_SYM, SK_W4_CODEBOOK, SK_W6_SYM = 0, 1, 2
 SK_LAYOUT_CANONICAL, SK_LAYOUT_STREAM = 0, 1
@@ -32,14 +32,15 @@ PRO_NONE, PRO_RMSNORM, PRO_SWIGLU = 0, 1, 2
 BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
 
 # Every symbol include/sk_repack.h and include/sk_repack_test.h declare.
-EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_w4a8",
+EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_workspace_size",
+           "sk_gemm_w4a8",
            "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu",
            "sk_gemm_experts", "sk_quantize_rows", "sk_gemm_w4a8_canonical",
            "sk_gemm_w4a8_canonical_q",
            "sk_debug_gemm",
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
            "sk_test_set_spin_limit", "sk_test_stream_read",
-           "sk_kv_append", "sk_decode_attention", "sk_kv_pack_host",
+           "sk_kv_append", "sk_decode_attention", "sk_attention_workspace_size", "sk_kv_pack_host",
            "sk_test_attention_plan", "sk_test_set_attention_split",
            "sk_mtp_create", "sk_mtp_destroy", "sk_mtp_observe", "sk_mtp_layout", "sk_mtp_layout_of",
            "sk_mtp_accept", "sk_mtp_expected_tokens", "sk_mtp_state"]
@@ -65,26 +66,30 @@ def _load() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, I, I64, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
     W = ctypes.POINTER(SkWeightStruct)
+    Z = ctypes.c_size_t
+    ZP = ctypes.POINTER(ctypes.c_size_t)
     sig = {
         "sk_status_string": ([I], ctypes.c_char_p),
         "sk_repack_w4a8": ([W, P], I),
         "sk_unrepack_w4a8": ([W, P], I),
-        "sk_gemm_w4a8": ([W, P, I, I, P, P], I),
-        "sk_gemm_w6a8": ([W, P, I, I, P, P], I),
-        "sk_gemm_fused_rmsnorm": ([W, P, I, P, F, I, P, P], I),
-        "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P], I),
-        "sk_gemm_experts": ([W, I, ctypes.POINTER(ctypes.c_int32), I, P, I, I, P, P], I),
+        "sk_gemm_workspace_size": ([I, I, I, I, I, I, ZP], I),
+        "sk_gemm_w4a8": ([W, P, I, I, P, P, Z, P], I),
+        "sk_gemm_w6a8": ([W, P, I, I, P, P, Z, P], I),
+        "sk_gemm_fused_rmsnorm": ([W, P, I, P, F, I, P, P, Z, P], I),
+        "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P, Z, P], I),
+        "sk_gemm_experts": ([W, I, P, I, P, I, I, P, P, Z, P], I),
         "sk_quantize_rows": ([P, I, I, I, P, P, P], I),
-        "sk_gemm_w4a8_canonical": ([W, P, I, I, P, P], I),
-        "sk_gemm_w4a8_canonical_q": ([W, P, P, I, P, P], I),
-        "sk_debug_gemm": ([W, I, P, P, I64, I, P, F, I, P, P, P, P, P], I),
+        "sk_gemm_w4a8_canonical": ([W, P, I, I, P, P, Z, P], I),
+        "sk_gemm_w4a8_canonical_q": ([W, P, P, I, P, P, Z, P], I),
+        "sk_debug_gemm": ([W, I, P, P, I64, I, P, F, I, P, P, P, P, P, Z, P], I),
         "sk_test_repack_on_host": ([W, P, I], I),
         "sk_test_gemm_plan": ([I, I, I, I, I, I, I, ctypes.POINTER(ctypes.c_int64)], I),
         "sk_test_set_split": ([I], I),
         "sk_test_set_spin_limit": ([I], I),
         "sk_test_stream_read": ([P, I64, I, I, P, P], I),
         "sk_kv_append": ([P, I, I, I, I, P, P, P], I),
-        "sk_decode_attention": ([P, I, I, I, P, I, I, F, P, P], I),
+        "sk_decode_attention": ([P, I, I, I, P, I, I, F, P, P, Z, P], I),
+        "sk_attention_workspace_size": ([I, I, I, I, ZP], I),
         "sk_kv_pack_host": ([P, P, I, I, I, P], I),
         "sk_test_attention_plan": ([I, I, I, I, I, ctypes.POINTER(I), ctypes.POINTER(I)], I),
         "sk_test_set_attention_split": ([I], I),
@@ -173,38 +178,121 @@ def sk_unrepack_w4a8(w: QuantWeight, stream=None) -> None:
     _check(LIB.sk_unrepack_w4a8(ctypes.byref(w.desc), _stream(stream)), "sk_unrepack_w4a8")
 
 
+# ----------------------------------------------------------------------------
+# workspaces (caller-owned device memory for launches that split their work)
+# ----------------------------------------------------------------------------
+
+class Workspace:
+    """Zero-filled device memory for the library's split launches (see the
+    workspace rules in include/sk_repack.h).  Calls that share one Workspace
+    must be ordered on one stream (or by events); give concurrent streams
+    their own."""
+
+    def __init__(self, nbytes: int, device=None):
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        self.nbytes = max(256, (int(nbytes) + 255) // 256 * 256)
+        self.tensor = torch.zeros(self.nbytes, dtype=torch.uint8, device=dev)
+        if self.tensor.data_ptr() % 256:
+            raise RuntimeError("workspace allocation is not 256-byte aligned")
+
+    @property
+    def ptr(self) -> int:
+        return self.tensor.data_ptr()
+
+
+_DEFAULT_WS_BYTES = 8 << 20
+_default_ws = {}          # device index -> Workspace
+_retired_ws = []          # replaced default workspaces: kept alive, a captured graph may use them
+
+
+def default_workspace(nbytes: int, device=None) -> Workspace:
+    """The per-device workspace the wrappers use when none is given.  It grows
+    (to at least 8 MiB) only outside stream capture; a replaced one is never
+    freed, because a captured graph may still point at it."""
+    dev = torch.cuda.current_device() if device is None else torch.device(device).index
+    ws = _default_ws.get(dev)
+    if ws is None or ws.nbytes < nbytes:
+        if torch.cuda.is_current_stream_capturing():
+            raise RuntimeError(f"the default workspace must grow to {nbytes} bytes, which it cannot "
+                               "do during stream capture: make one call of this shape before "
+                               "capturing, or pass workspace=Workspace(...)")
+        if ws is not None:
+            _retired_ws.append(ws)
+        ws = Workspace(max(nbytes, _DEFAULT_WS_BYTES), device=torch.device("cuda", dev))
+        _default_ws[dev] = ws
+    return ws
+
+
+_ws_sizes = {}
+
+
+def gemm_workspace_size(n: int, k: int, group: int, fmt: int, m: int, prologue: int = 0) -> int:
+    """Bytes of workspace a GEMM call with these sizes needs on the current device."""
+    key = (torch.cuda.current_device() if torch.cuda.is_available() else -1, n, k, group, fmt, m,
+           prologue)
+    v = _ws_sizes.get(key)
+    if v is None:
+        out = ctypes.c_size_t()
+        _check(LIB.sk_gemm_workspace_size(n, k, group, fmt, m, prologue, ctypes.byref(out)),
+               "sk_gemm_workspace_size")
+        v = _ws_sizes[key] = out.value
+    return v
+
+
+def _ws_args(need: int, workspace):
+    if workspace is not None:
+        return workspace.ptr, workspace.nbytes
+    if need == 0:
+        return None, 0
+    ws = default_workspace(need)
+    return ws.ptr, ws.nbytes
+
+
+def _gemm_ws(w: QuantWeight, m: int, prologue: int, workspace, n: int | None = None):
+    if workspace is not None:
+        return workspace.ptr, workspace.nbytes
+    return _ws_args(gemm_workspace_size(w.n if n is None else n, w.k, w.group, w.fmt, m, prologue),
+                    None)
+
+
 def _out(w: QuantWeight, m: int, y):
     if y is None:
         y = torch.empty((m, w.n), dtype=torch.float32, device="cuda")
     return y
 
 
-def sk_gemm_w4a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+def sk_gemm_w4a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None, workspace=None) -> torch.Tensor:
     m = x.shape[0]
     y = _out(w, m, y)
-    _check(LIB.sk_gemm_w4a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
-           "sk_gemm_w4a8")
+    wp, wb = _gemm_ws(w, m, PRO_NONE, workspace)
+    _check(LIB.sk_gemm_w4a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), wp, wb,
+                            _stream(stream)), "sk_gemm_w4a8")
     return y
 
 
-def sk_gemm_w6a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+def sk_gemm_w6a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None, workspace=None) -> torch.Tensor:
     m = x.shape[0]
     y = _out(w, m, y)
-    _check(LIB.sk_gemm_w6a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
-           "sk_gemm_w6a8")
+    wp, wb = _gemm_ws(w, m, PRO_NONE, workspace)
+    _check(LIB.sk_gemm_w6a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), wp, wb,
+                            _stream(stream)), "sk_gemm_w6a8")
     return y
 
 
-def sk_gemm_experts(bank: QuantWeight, rows_per_expert: int, experts, x: torch.Tensor, y=None,
-                    stream=None) -> torch.Tensor:
+def sk_gemm_experts(bank: QuantWeight, rows_per_expert: int, experts: torch.Tensor, x: torch.Tensor,
+                    y=None, stream=None, workspace=None) -> torch.Tensor:
     """Listed experts of a repacked expert bank (E * rows_per_expert rows) times x, in one
-    launch; returns y [M, len(experts) * rows_per_expert]."""
-    ids = (ctypes.c_int32 * len(experts))(*[int(e) for e in experts])
+    launch; `experts` is a device int32 tensor of ids, read when the kernel runs.
+    Returns y [M, len(experts) * rows_per_expert]."""
+    if experts.dtype != torch.int32 or not experts.is_cuda or experts.dim() != 1:
+        raise ValueError("experts must be a 1-D int32 device tensor")
+    nl = experts.shape[0]
     m = x.shape[0]
     if y is None:
-        y = torch.empty((m, len(experts) * rows_per_expert), dtype=torch.float32, device="cuda")
-    _check(LIB.sk_gemm_experts(ctypes.byref(bank.desc), rows_per_expert, ids, len(experts),
-                               _ptr(x), _xt(x), m, _ptr(y), _stream(stream)), "sk_gemm_experts")
+        y = torch.empty((m, nl * rows_per_expert), dtype=torch.float32, device="cuda")
+    wp, wb = _gemm_ws(bank, m, PRO_NONE, workspace, n=nl * rows_per_expert)
+    _check(LIB.sk_gemm_experts(ctypes.byref(bank.desc), rows_per_expert, _ptr(experts), nl,
+                               _ptr(x), _xt(x), m, _ptr(y), wp, wb, _stream(stream)), "sk_gemm_experts")
     return y
 
 
@@ -220,61 +308,72 @@ def sk_quantize_rows(x: torch.Tensor, q=None, sx=None, stream=None):
     return q, sx
 
 
-def sk_gemm_w4a8_canonical(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+def sk_gemm_w4a8_canonical(w: QuantWeight, x: torch.Tensor, y=None, stream=None,
+                           workspace=None) -> torch.Tensor:
     """W4A8 GEMM on a weight left in the canonical layout (no repack)."""
     m = x.shape[0]
     y = _out(w, m, y)
-    _check(LIB.sk_gemm_w4a8_canonical(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y),
+    wp, wb = _gemm_ws(w, m, PRO_NONE, workspace)
+    _check(LIB.sk_gemm_w4a8_canonical(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), wp, wb,
                                       _stream(stream)), "sk_gemm_w4a8_canonical")
     return y
 
 
 def sk_gemm_w4a8_canonical_q(w: QuantWeight, q: torch.Tensor, sx: torch.Tensor, y=None,
-                             stream=None) -> torch.Tensor:
+                             stream=None, workspace=None) -> torch.Tensor:
     """The same GEMM on activations already quantised by sk_quantize_rows."""
     m = q.shape[0]
     y = _out(w, m, y)
-    _check(LIB.sk_gemm_w4a8_canonical_q(ctypes.byref(w.desc), _ptr(q), _ptr(sx), m, _ptr(y),
+    wp, wb = _gemm_ws(w, m, PRO_NONE, workspace)
+    _check(LIB.sk_gemm_w4a8_canonical_q(ctypes.byref(w.desc), _ptr(q), _ptr(sx), m, _ptr(y), wp, wb,
                                         _stream(stream)), "sk_gemm_w4a8_canonical_q")
     return y
 
 
 def sk_gemm_fused_rmsnorm(w: QuantWeight, x: torch.Tensor, gamma: torch.Tensor, eps: float,
-                          y=None, stream=None) -> torch.Tensor:
+                          y=None, stream=None, workspace=None) -> torch.Tensor:
     m = x.shape[0]
     y = _out(w, m, y)
+    wp, wb = _gemm_ws(w, m, PRO_RMSNORM, workspace)
     _check(LIB.sk_gemm_fused_rmsnorm(ctypes.byref(w.desc), _ptr(x), _xt(x), _ptr(gamma),
-                                     ctypes.c_float(eps), m, _ptr(y), _stream(stream)),
+                                     ctypes.c_float(eps), m, _ptr(y), wp, wb, _stream(stream)),
            "sk_gemm_fused_rmsnorm")
     return y
 
 
 def sk_gemm_fused_swiglu(w: QuantWeight, gate: torch.Tensor, up: torch.Tensor, y=None,
-                         stream=None) -> torch.Tensor:
+                         stream=None, workspace=None) -> torch.Tensor:
     """gate and up are [M, K] views sharing one row stride (e.g. halves of [M, 2K])."""
     m = gate.shape[0]
     if gate.stride() != up.stride() or gate.stride(1) != 1:
         raise ValueError("gate and up must be row-major with the same row stride")
     y = _out(w, m, y)
+    wp, wb = _gemm_ws(w, m, PRO_SWIGLU, workspace)
     _check(LIB.sk_gemm_fused_swiglu(ctypes.byref(w.desc), _ptr(gate), _ptr(up), gate.stride(0),
-                                    _xt(gate), m, _ptr(y), _stream(stream)),
+                                    _xt(gate), m, _ptr(y), wp, wb, _stream(stream)),
            "sk_gemm_fused_swiglu")
     return y
 
 
 def sk_debug_gemm(w: QuantWeight, prologue: int, x: torch.Tensor, x2=None, gamma=None,
-                  eps: float = 0.0, want_partials: bool = True, stream=None):
-    """Runs the GEMM with the export flag; returns (y, q, sx, P or None)."""
+                  eps: float = 0.0, want_partials: bool = True, stream=None, workspace=None,
+                  y=None, q=None, sx=None, p=None):
+    """Runs the GEMM with the export flag; returns (y, q, sx, P or None).  The
+    outputs may be given (contiguous device tensors of the right sizes)."""
     m, k = x.shape[0], w.k
     ld = x.stride(0) if prologue == PRO_SWIGLU else k
-    y = torch.empty((m, w.n), dtype=torch.float32, device="cuda")
-    q = torch.empty((m, k), dtype=torch.int8, device="cuda")
-    sx = torch.empty((m,), dtype=torch.float32, device="cuda")
-    p = (torch.empty((m, w.n, k // w.group), dtype=torch.int32, device="cuda")
-         if want_partials else None)
+    if y is None:
+        y = torch.empty((m, w.n), dtype=torch.float32, device="cuda")
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.int8, device="cuda")
+    if sx is None:
+        sx = torch.empty((m,), dtype=torch.float32, device="cuda")
+    if p is None and want_partials:
+        p = torch.empty((m, w.n, k // w.group), dtype=torch.int32, device="cuda")
+    wp, wb = _gemm_ws(w, m, prologue, workspace)
     _check(LIB.sk_debug_gemm(ctypes.byref(w.desc), prologue, _ptr(x), _ptr(x2), ld, _xt(x),
                              _ptr(gamma), ctypes.c_float(eps), m, _ptr(y), _ptr(q), _ptr(sx),
-                             _ptr(p), _stream(stream)), "sk_debug_gemm")
+                             _ptr(p), wp, wb, _stream(stream)), "sk_debug_gemm")
     return y, q, sx, p
 
 
@@ -295,6 +394,7 @@ def gemm_plan(n: int, k: int, group: int, fmt: int, m: int, cus: int = 256,
 def set_split(s: int) -> None:
     """Test hook: force the number of K-slices (0 = automatic)."""
     _check(LIB.sk_test_set_split(s), "sk_test_set_split")
+    _ws_sizes.clear()              # the plans, hence the workspace sizes, change
 
 
 def stream_read(buf: torch.Tensor, grid: int, threads: int, out: torch.Tensor, stream=None) -> None:
@@ -342,7 +442,7 @@ def sk_kv_append(kv: torch.Tensor, hkv: int, cap: int, pos: int, k_new: torch.Te
 
 
 def sk_decode_attention(q: torch.Tensor, hkv: int, kv: torch.Tensor, cap: int, length: int,
-                        scale: float | None = None, out=None, stream=None) -> torch.Tensor:
+                        scale: float | None = None, out=None, stream=None, workspace=None) -> torch.Tensor:
     """O [M, Hq, 128] float32 for query rows q [M, Hq, 128] bf16 over the first ``length`` entries."""
     q = _bf16_bits(q)
     if q.dim() != 3 or not q.is_contiguous():
@@ -354,9 +454,21 @@ def sk_decode_attention(q: torch.Tensor, hkv: int, kv: torch.Tensor, cap: int, l
         scale = HEAD_DIM ** -0.5
     if out is None:
         out = torch.empty((m, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is not None:
+        wp, wb = workspace.ptr, workspace.nbytes
+    else:
+        wp, wb = _ws_args(attention_workspace_size(m, hq, hkv, length), None)
     _check(LIB.sk_decode_attention(_ptr(q), m, hq, hkv, _ptr(kv), cap, length, ctypes.c_float(scale),
-                                   _ptr(out), _stream(stream)), "sk_decode_attention")
+                                   _ptr(out), wp, wb, _stream(stream)), "sk_decode_attention")
     return out
+
+
+def attention_workspace_size(m: int, hq: int, hkv: int, length: int) -> int:
+    """Bytes of workspace sk_decode_attention needs for these sizes on the current device."""
+    out = ctypes.c_size_t()
+    _check(LIB.sk_attention_workspace_size(m, hq, hkv, length, ctypes.byref(out)),
+           "sk_attention_workspace_size")
+    return out.value
 
 
 def sk_kv_pack_host(k, v, hkv: int, length: int, cap: int):

@@ -57,12 +57,14 @@ sk_status from_hip(hipError_t e) { return e == hipSuccess ? SK_OK : SK_ERR_HIP; 
 
 int g_spin_limit = 0;   // test hook: exchange polls before the local fallback (0 = default)
 
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
 // Checks for the GEMM entry points, then the launch.
 sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* x, const void* x2,
                    int64_t ld, int xt, const float* gamma, float eps, int m, float* y,
-                   int8_t* q_out, float* sx_out, int32_t* p_out, void* stream, bool any_format,
-                   bool canon = false, int rows_per_expert = 0, const int32_t* experts = nullptr,
-                   int n_list = 0) {
+                   int8_t* q_out, float* sx_out, int32_t* p_out, void* ws, size_t ws_bytes,
+                   void* stream, bool any_format, bool canon = false, int rows_per_expert = 0,
+                   const int32_t* experts = nullptr, int n_list = 0) {
     sk_status s = check_weight(w);
     if (s != SK_OK) return s;
     if (canon && w->format != SK_W4_SYM) return SK_ERR_FORMAT;
@@ -92,7 +94,10 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     int64_t n_call = w->n;
     if (rows_per_expert) n_call = (int64_t)n_list * rows_per_expert;
     const Geom G = sk::make_geom(n_call, w->k, w->group, w->format);
-    if (!sk::gemm_plan_ok(G, m, prologue)) return SK_ERR_UNSUPPORTED;
+    const sk::Plan plan = sk::gemm_plan(G, m, prologue);
+    if (!plan.ok) return SK_ERR_UNSUPPORTED;
+    const size_t need = sk::workspace_bytes(plan);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return SK_ERR_WORKSPACE;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p_out) {
@@ -118,7 +123,9 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     c.canon = canon;
     c.rows_per_expert = rows_per_expert;
     c.n_list = n_list;
+    c.n_experts = rows_per_expert ? w->n / rows_per_expert : 0;
     c.experts = experts;
+    c.ws = need > 0 ? ws : nullptr;
     return from_hip(sk::launch_gemm(G, c, st));
 }
 
@@ -134,6 +141,7 @@ SK_EXPORT const char* sk_status_string(sk_status s) {
         case SK_ERR_LAYOUT: return "weight is in the wrong layout for this call";
         case SK_ERR_HIP: return "HIP runtime error";
         case SK_ERR_UNSUPPORTED: return "shape not supported by this backend";
+        case SK_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
     }
     return "unknown status";
 }
@@ -160,55 +168,69 @@ SK_EXPORT sk_status sk_unrepack_w4a8(sk_weight* w, void* stream) {
     return s;
 }
 
+SK_EXPORT sk_status sk_gemm_workspace_size(int n, int k, int group, int format, int m, int prologue,
+                                           size_t* bytes) {
+    if (!bytes) return SK_ERR_NULL;
+    if (format != SK_W4_SYM && format != SK_W4_CODEBOOK && format != SK_W6_SYM) return SK_ERR_FORMAT;
+    if (prologue < sk::PRO_NONE || prologue > sk::PRO_SWIGLU) return SK_ERR_FORMAT;
+    if (n < 1 || k < 1 || m < 1 || m > 8 || !page_shape_ok(format, k, group)) return SK_ERR_SHAPE;
+    if (k % sk::SB_K != 0 || k > sk::kMaxGemmK || !backend_group_ok(format, group) || n > (1 << 24))
+        return SK_ERR_UNSUPPORTED;
+    const sk::Plan p = sk::gemm_plan(sk::make_geom(n, k, group, format), m, prologue);
+    if (!p.ok) return SK_ERR_UNSUPPORTED;
+    *bytes = sk::workspace_bytes(p);
+    return SK_OK;
+}
+
 SK_EXPORT sk_status sk_gemm_w4a8(const sk_weight* w, const void* x, int xt, int m, float* y,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
     return run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
-                    nullptr, nullptr, stream, false);
+                    nullptr, nullptr, workspace, workspace_bytes, stream, false);
 }
 
 SK_EXPORT sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m, float* y,
-                                 void* stream) {
+                                 void* workspace, size_t workspace_bytes, void* stream) {
     return run_gemm(w, true, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
-                    nullptr, nullptr, stream, false);
+                    nullptr, nullptr, workspace, workspace_bytes, stream, false);
 }
 
 SK_EXPORT sk_status sk_gemm_fused_rmsnorm(const sk_weight* w, const void* x, int xt,
                                           const float* gamma, float eps, int m, float* y,
-                                          void* stream) {
+                                          void* workspace, size_t workspace_bytes, void* stream) {
     return run_gemm(w, false, sk::PRO_RMSNORM, x, nullptr, 0, xt, gamma, eps, m, y, nullptr,
-                    nullptr, nullptr, stream, true);
+                    nullptr, nullptr, workspace, workspace_bytes, stream, true);
 }
 
 SK_EXPORT sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void* up,
-                                         int64_t ld, int xt, int m, float* y, void* stream) {
+                                         int64_t ld, int xt, int m, float* y, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
     return run_gemm(w, false, sk::PRO_SWIGLU, gate, up, ld, xt, nullptr, 0.0f, m, y, nullptr,
-                    nullptr, nullptr, stream, true);
+                    nullptr, nullptr, workspace, workspace_bytes, stream, true);
 }
 
 SK_EXPORT sk_status sk_gemm_experts(const sk_weight* bank, int rows_per_expert,
                                     const int32_t* experts, int n_list, const void* x, int xt,
-                                    int m, float* y, void* stream) {
+                                    int m, float* y, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
     sk_status s = check_weight(bank);
     if (s != SK_OK) return s;
     if (!experts) return SK_ERR_NULL;
     if (rows_per_expert < 16 || rows_per_expert % 16 != 0 || bank->n % rows_per_expert != 0)
         return SK_ERR_SHAPE;
-    const int n_experts = bank->n / rows_per_expert;
-    if (n_list < 1 || n_list > 64) return SK_ERR_SHAPE;
-    for (int i = 0; i < n_list; ++i)
-        if (experts[i] < 0 || experts[i] >= n_experts) return SK_ERR_SHAPE;
+    if (n_list < 1 || (int64_t)n_list * rows_per_expert > (1 << 24)) return SK_ERR_SHAPE;
+    if ((reinterpret_cast<uintptr_t>(experts) & 3u) != 0) return SK_ERR_ALIGN;
     return run_gemm(bank, bank->format == SK_W6_SYM, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f,
-                    m, y, nullptr, nullptr, nullptr, stream, true, false, rows_per_expert,
-                    experts, n_list);
+                    m, y, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, true, false,
+                    rows_per_expert, experts, n_list);
 }
 
 SK_EXPORT sk_status sk_debug_gemm(const sk_weight* w, int prologue, const void* x, const void* x2,
                                   int64_t ld, int xt, const float* gamma, float eps, int m,
                                   float* y, int8_t* q_out, float* sx_out, int32_t* p_out,
-                                  void* stream) {
+                                  void* workspace, size_t workspace_bytes, void* stream) {
     if (prologue < sk::PRO_NONE || prologue > sk::PRO_SWIGLU) return SK_ERR_FORMAT;
     return run_gemm(w, false, prologue, x, x2, ld, xt, gamma, eps, m, y, q_out, sx_out, p_out,
-                    stream, true);
+                    workspace, workspace_bytes, stream, true);
 }
 
 SK_EXPORT sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t* q, float* sx,
@@ -222,16 +244,18 @@ SK_EXPORT sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t
 }
 
 SK_EXPORT sk_status sk_gemm_w4a8_canonical(const sk_weight* w, const void* x, int xt, int m,
-                                           float* y, void* stream) {
+                                           float* y, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
     return run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
-                    nullptr, nullptr, stream, false, true);
+                    nullptr, nullptr, workspace, workspace_bytes, stream, false, true);
 }
 
 SK_EXPORT sk_status sk_gemm_w4a8_canonical_q(const sk_weight* w, const int8_t* q, const float* sx,
-                                             int m, float* y, void* stream) {
+                                             int m, float* y, void* workspace, size_t workspace_bytes,
+                                             void* stream) {
     if (sx && (reinterpret_cast<uintptr_t>(sx) & 3u) != 0) return SK_ERR_ALIGN;
     return run_gemm(w, false, sk::PRO_QIN, q, sx, 0, SK_F32, nullptr, 0.0f, m, y, nullptr,
-                    nullptr, nullptr, stream, false, true);
+                    nullptr, nullptr, workspace, workspace_bytes, stream, false, true);
 }
 
 SK_EXPORT sk_status sk_test_repack_on_host(const sk_weight* w, void* host_bytes, int inverse) {

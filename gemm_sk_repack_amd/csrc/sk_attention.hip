@@ -593,21 +593,24 @@ Plan make_plan(int m, int hq, int hkv, int len, int cus) {
 
 struct DevState {
     int cus = 0;
-    // [hdr: 256 B][cnt: cap_h][flag: cap_h*kMaxSplits] (u32, padded to 256 B)
-    // [part: cap_part floats]
-    void* ws = nullptr;
-    int cap_h = 0;
-    size_t cap_part = 0;
     bool lds_set[5] = {false, false, false, false, false};
 };
 std::mutex g_mu;
 DevState g_dev[64];
 
-size_t counters_bytes(int cap_h) {
-    return ((size_t)cap_h * (1 + kMaxSplits) * 4 + 255) / 256 * 256;
+// Caller-owned workspace: [hdr: 256 B][cnt: kMaxKvHeads u32][flag: kMaxKvHeads *
+// kMaxSplits u32] (fixed size, so one buffer serves calls of any shape), then
+// the partial states.  Only launches that split the prefix touch it.
+constexpr size_t kCountersBytes = ((size_t)kMaxKvHeads * (1 + kMaxSplits) * 4 + 255) / 256 * 256;
+constexpr size_t kHeaderBytes = 256 + kCountersBytes;
+constexpr int kChunk = PSTRIDE * 16;      // floats of one partial state per query tile
+
+size_t workspace_bytes(const Plan& p, int hkv) {
+    return p.nsplit > 1 ? kHeaderBytes + (size_t)hkv * p.nsplit * p.nqt * kChunk * 4 : 0;
 }
 
 hipError_t device_cus(int dev, int& cus) {
+    std::lock_guard<std::mutex> lk(g_mu);
     DevState& ds = g_dev[dev];
     if (ds.cus == 0) {
         int v = 0;
@@ -619,50 +622,33 @@ hipError_t device_cus(int dev, int& cus) {
     return hipSuccess;
 }
 
-hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const void* kv, int cap, int len,
-                            float scale, float* out, hipStream_t st) {
-    int dev = 0;
+// The plan of a call on the current device.
+hipError_t current_plan(int m, int hq, int hkv, int len, Plan& p, int& dev) {
+    dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     int cus = 0;
     e = device_cus(dev, cus);
     if (e != hipSuccess) return e;
-    const Plan p = make_plan(m, hq, hkv, len, cus);
-    constexpr int kChunk = PSTRIDE * 16;      // floats of one partial state per query tile
-    const size_t part_words = p.nsplit > 1 ? (size_t)hkv * p.nsplit * p.nqt * kChunk : 0;
+    p = make_plan(m, hq, hkv, len, cus);
+    return hipSuccess;
+}
+
+hipError_t launch_attention(const Plan& p, int dev, const uint16_t* q, int m, int hq, int hkv,
+                            const void* kv, int cap, int len, float scale, float* out, void* ws,
+                            hipStream_t st) {
     DevState& ds = g_dev[dev];
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        if (!ds.ws || ds.cap_h < hkv || ds.cap_part < part_words) {
-            const int cap_h = ds.cap_h > hkv ? ds.cap_h : (hkv > 64 ? hkv : 64);
-            const size_t cap_part = ds.cap_part > part_words ? ds.cap_part : part_words;
-            if (ds.ws) {
-                e = hipDeviceSynchronize();
-                if (e != hipSuccess) return e;
-                (void)hipFree(ds.ws);
-                ds.ws = nullptr;
-            }
-            const size_t bytes = 256 + counters_bytes(cap_h) + cap_part * 4;
-            e = hipMalloc(&ds.ws, bytes);
-            if (e != hipSuccess) return e;
-            e = hipMemset(ds.ws, 0, bytes);
-            if (e != hipSuccess) return e;
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return e;
-            ds.cap_h = cap_h;
-            ds.cap_part = cap_part;
-        }
-    }
-    uint8_t* const wsb = static_cast<uint8_t*>(ds.ws);
+    hipError_t e = hipSuccess;
+    uint8_t* const wsb = static_cast<uint8_t*>(ws);
     AttnArgs a;
     a.q = q;
     a.kv = static_cast<const uint8_t*>(kv);
     a.out = out;
     a.hdr = reinterpret_cast<uint32_t*>(wsb);
-    a.cnt = reinterpret_cast<uint32_t*>(wsb + 256);
-    a.flag = a.cnt + ds.cap_h;
-    a.part = reinterpret_cast<float*>(wsb + 256 + counters_bytes(ds.cap_h));
+    a.cnt = wsb ? reinterpret_cast<uint32_t*>(wsb + 256) : nullptr;
+    a.flag = wsb ? a.cnt + kMaxKvHeads : nullptr;
+    a.part = wsb ? reinterpret_cast<float*>(wsb + kHeaderBytes) : nullptr;
     a.m = m;
     a.hq = hq;
     a.g = hq / hkv;
@@ -672,7 +658,7 @@ hipError_t launch_attention(const uint16_t* q, int m, int hq, int hkv, const voi
     a.nblk = p.nblk;
     a.bps = p.bps;
     a.nsplit = p.nsplit;
-    a.part_bytes = (int)(ds.cap_part * 4);
+    a.part_bytes = (int)(workspace_bytes(p, hkv) > 0 ? workspace_bytes(p, hkv) - kHeaderBytes : 0);
     a.nwg = p.nsplit * hkv;
     a.sl2 = scale * 1.4426950408889634f;
     void (*fn)(AttnArgs) = nullptr;
@@ -735,8 +721,20 @@ SK_EXPORT sk_status sk_kv_append(void* kv, int hkv, int cap, int pos, int t, con
     return hipGetLastError() == hipSuccess ? SK_OK : SK_ERR_HIP;
 }
 
+SK_EXPORT sk_status sk_attention_workspace_size(int m, int hq, int hkv, int len, size_t* bytes) {
+    if (!bytes) return SK_ERR_NULL;
+    if (m < 1 || m > 8 || hkv < 1 || hq < 1 || hq % hkv != 0 || len < m) return SK_ERR_SHAPE;
+    if ((int64_t)m * (hq / hkv) > ska::kMaxRows || hkv > ska::kMaxKvHeads) return SK_ERR_UNSUPPORTED;
+    ska::Plan p;
+    int dev = 0;
+    if (ska::current_plan(m, hq, hkv, len, p, dev) != hipSuccess) return SK_ERR_HIP;
+    *bytes = ska::workspace_bytes(p, hkv);
+    return SK_OK;
+}
+
 SK_EXPORT sk_status sk_decode_attention(const uint16_t* q, int m, int hq, int hkv, const void* kv, int cap,
-                                        int len, float scale, float* out, void* stream) {
+                                        int len, float scale, float* out, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
     if (!q || !kv || !out) return SK_ERR_NULL;
     if (m < 1 || m > 8 || hkv < 1 || hq < 1 || hq % hkv != 0 || cap < ska::BK || cap % ska::BK != 0 ||
         len < m || len > cap || !std::isfinite(scale) || !(scale > 0.0f))
@@ -745,7 +743,16 @@ SK_EXPORT sk_status sk_decode_attention(const uint16_t* q, int m, int hq, int hk
     if ((int64_t)m * (hq / hkv) > ska::kMaxRows || hkv > ska::kMaxKvHeads || cap > ska::kMaxEntries)
         return SK_ERR_UNSUPPORTED;
     if (!ska::aligned16(q) || !ska::aligned16(kv) || !ska::aligned16(out)) return SK_ERR_ALIGN;
-    const hipError_t e = ska::launch_attention(q, m, hq, hkv, kv, cap, len, scale, out,
+    ska::Plan p;
+    int dev = 0;
+    if (ska::current_plan(m, hq, hkv, len, p, dev) != hipSuccess) return SK_ERR_HIP;
+    const size_t need = ska::workspace_bytes(p, hkv);
+    if (need > 0 && (!workspace || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+        return SK_ERR_WORKSPACE;
+    if (need > ((size_t)1 << 31)) return SK_ERR_UNSUPPORTED;     // 32-bit offsets into the partials
+    const hipError_t e = ska::launch_attention(p, dev, q, m, hq, hkv, kv, cap, len, scale, out,
+                                               need > 0 ? workspace : nullptr,
                                                static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SK_OK : SK_ERR_HIP;
 }

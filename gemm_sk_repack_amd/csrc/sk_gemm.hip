@@ -24,14 +24,9 @@ KernelFn pick(int fmt, int pro, int xt, int gs, bool dot4, bool dbg, bool wide) 
     }
 }
 
-struct DevState {
-    int cus = 0;
-    void* ws = nullptr;      // [WsHeader][cnt: cap_t uint32][part: cap_part u64]
-    int64_t cap_t = 0;
-    size_t cap_part = 0;
-};
+// Compute units per device, read once per device (a host-side property query).
 std::mutex g_mu;
-DevState g_dev[64];
+int g_cus[64] = {0};
 
 int g_split_override = 0;
 
@@ -45,14 +40,15 @@ namespace {
 
 // Waves of a workgroup: TW tile groups x KW waves along k (KW divides the
 // slice's KBs super-blocks).  Each wave walks ceil(tiles / TW) tile steps of
-// KBs / KW super-blocks, in groups of PIPE slots (a step's last group padded);
-// the split with the fewest slots per wave, padding included, wins, then the
-// one with the fewest tile steps (each ends with a workgroup barrier).
-// Returns the slots per wave.
-int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int& KW, int& TW) {
+// KBs / KW super-blocks, in groups of `pipe` slots (a step's last group padded
+// with slots that load nothing); the split with the fewest slots per wave,
+// padding included (the register pipeline's round trips), wins, then the one
+// with the fewest real slots per wave, then the one with the fewest tile
+// steps (each ends with a workgroup barrier).  Returns the padded slots per wave.
+int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int pipe, int& KW, int& TW) {
     KW = 1;
     TW = 1;
-    int64_t best_slots = -1, best_steps = -1;
+    int64_t best_slots = -1, best_real = -1, best_steps = -1;
     for (int kw = 1; kw <= nwa && KBs > 0; ++kw) {
         if (KBs % kw != 0) continue;
         int tw = nwa / kw;
@@ -60,9 +56,12 @@ int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int& KW, int& TW)
         if (tw > tiles_per_wg) tw = tiles_per_wg;
         const int64_t steps = (tiles_per_wg + tw - 1) / tw;
         const int spw = KBs / kw;
-        const int64_t slots = steps * ((spw + PIPE - 1) / PIPE * PIPE);   // padded to whole groups
-        if (best_slots < 0 || slots < best_slots || (slots == best_slots && steps < best_steps)) {
+        const int64_t slots = steps * ((spw + pipe - 1) / pipe * pipe);   // padded to whole groups
+        const int64_t real = steps * spw;
+        if (best_slots < 0 || slots < best_slots || (slots == best_slots && real < best_real) ||
+            (slots == best_slots && real == best_real && steps < best_steps)) {
             best_slots = slots;
+            best_real = real;
             best_steps = steps;
             KW = kw;
             TW = tw;
@@ -74,6 +73,7 @@ int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int& KW, int& TW)
 int workgroups_per_slice(int cus, int S, int T) {
     int R = cus / S;
     if (R > T) R = T;
+    if (R > kMaxRanges) R = kMaxRanges;
     return R < 1 ? 1 : R;
 }
 
@@ -81,6 +81,7 @@ int workgroups_per_slice(int cus, int S, int T) {
 // budget for the prologue).
 Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
     Plan p;
+    const int pipe = pipe_of(m == 1 && G.fmt != FMT_CB);
     const int KB = (int)G.KB;
     const int T = (int)G.T;
     const bool cb = G.fmt == FMT_CB;
@@ -112,7 +113,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
             const int R = workgroups_per_slice(cus, s, T);
             const int64_t tpw = (T + R - 1) / R;
             int kw, tw;
-            const int64_t slots = split_waves(KB / s, (int)tpw, m, NW - 1, kw, tw);
+            const int64_t slots = split_waves(KB / s, (int)tpw, m, NW - 1, pipe, kw, tw);
             // in units of 1/2048
             const int64_t cost = 8192 * slots + (int64_t)m * (G.k / s) + 128 * tpw * s * m;
             if (best < 0 || cost < best) {
@@ -127,7 +128,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
     const int R = (S > 0) ? workgroups_per_slice(cus, S, T) : 1;
     p.R = R;
     // with S > 1 one wave is reserved for the exchange
-    split_waves(p.KBs, (T + R - 1) / R, m, (S > 1) ? NW - 1 : NW, p.KW, p.TW);
+    split_waves(p.KBs, (T + R - 1) / R, m, (S > 1) ? NW - 1 : NW, pipe, p.KW, p.TW);
     p.spw = p.KW > 0 ? p.KBs / p.KW : 0;
     p.P = S * R;
     p.ks = cb ? 2 * p.KS + 64 : p.KS + 32;
@@ -188,50 +189,32 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
 
 void set_split_override(int s) { g_split_override = s; }
 
-bool gemm_plan_ok(const Geom& G, int m, int pro) {
-    return make_plan(G, m, pro, 256, g_split_override).ok;
+namespace {
+
+// The current device's compute-unit count (256 if it cannot be read: the plan
+// is then the one a 256-unit part would use, and any launch fails anyway).
+int current_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 256;
+        g_cus[dev] = v > 0 ? v : 256;
+    }
+    return g_cus[dev];
+}
+
+}  // namespace
+
+Plan gemm_plan(const Geom& G, int m, int pro) {
+    return make_plan(G, m, pro, current_cus(), g_split_override);
 }
 
 hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    DevState& ds = g_dev[dev];
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        if (ds.cus == 0) {
-            int v = 0;
-            e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
-            if (e != hipSuccess) return e;
-            ds.cus = v > 0 ? v : 256;
-        }
-    }
-    const Plan p = make_plan(G, c.m, c.prologue, ds.cus, g_split_override);
+    const Plan p = gemm_plan(G, c.m, c.prologue);
     if (!p.ok) return hipErrorInvalidValue;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        if (!ds.ws || ds.cap_t < G.T || ds.cap_part < p.part_floats) {
-            int64_t cap_t = ds.cap_t > G.T ? ds.cap_t : G.T;
-            if (cap_t < 4096) cap_t = 4096;
-            size_t cap_part = ds.cap_part > p.part_floats ? ds.cap_part : p.part_floats;
-            if (ds.ws) {
-                e = hipDeviceSynchronize();
-                if (e != hipSuccess) return e;
-                (void)hipFree(ds.ws);
-                ds.ws = nullptr;
-            }
-            const size_t bytes = sizeof(WsHeader) + (size_t)cap_t * 4 + cap_part * 8;
-            e = hipMalloc(&ds.ws, bytes);
-            if (e != hipSuccess) return e;
-            e = hipMemset(ds.ws, 0, bytes);
-            if (e != hipSuccess) return e;
-            e = hipDeviceSynchronize();
-            if (e != hipSuccess) return e;
-            ds.cap_t = cap_t;
-            ds.cap_part = cap_part;
-        }
-    }
+    if (p.S > 1 && !c.ws) return hipErrorInvalidValue;
 
     const bool dot4 = (c.m == 1) && G.fmt != FMT_CB;
     const int gs = (int)(G.g / 32);                // 0 for the codebook's G = 16
@@ -252,9 +235,8 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.q_out = c.q_out;
     a.sx_out = c.sx_out;
     a.p_out = c.p_out;
-    a.ws = static_cast<WsHeader*>(ds.ws);
-    a.cnt = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ds.ws) + sizeof(WsHeader));
-    a.part = reinterpret_cast<u64*>(a.cnt + ds.cap_t);
+    a.ws = static_cast<WsHeader*>(c.ws);
+    a.part = c.ws ? reinterpret_cast<u64*>(static_cast<uint8_t*>(c.ws) + kWsHeaderBytes) : nullptr;
     a.n = (int)G.n;
     a.k = (int)G.k;
     a.m = c.m;
@@ -286,8 +268,8 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.ks = p.ks;
     a.spin_limit = c.spin_limit > 0 ? c.spin_limit : (1 << 20);
     a.tpe = c.rows_per_expert / TILE_ROWS;
-    for (int i = 0; i < kMaxExperts; ++i)
-        a.emap[i] = (uint16_t)((c.rows_per_expert && i < c.n_list) ? c.experts[i] : 0);
+    a.n_experts = c.n_experts;
+    a.experts = c.experts;
     a.tq = (int)(G.T / p.R);
     a.trem = (int)(G.T % p.R);
     a.jn0 = (a.tq + p.TW - 1) / p.TW;
@@ -306,7 +288,7 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     }
 
     if (p.lds > 64 * 1024) {
-        e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
         if (e != hipSuccess) return e;
     }

@@ -50,11 +50,42 @@ namespace sk {
 
 constexpr int NW = 16;         // waves per workgroup
 constexpr int NT = NW * 64;    // threads per workgroup
-constexpr int PIPE = 4;        // super-blocks in flight per wave
-constexpr int PRIME = 2;       // of which issued before the activation prologue
+// Register pipeline of the weight stream: super-blocks in flight per wave, and
+// how many of them each wave issues before the activation prologue, for the
+// v_dot4 instances (M = 1) and the MFMA instances (M >= 2, the codebook).
+#ifndef SK_PIPE_DOT4
+#define SK_PIPE_DOT4 4
+#endif
+#ifndef SK_PRIME_DOT4
+#define SK_PRIME_DOT4 2
+#endif
+#ifndef SK_PIPE_MFMA
+#define SK_PIPE_MFMA 4
+#endif
+#ifndef SK_PRIME_MFMA
+#define SK_PRIME_MFMA 2
+#endif
+#ifndef SK_MFMA_ACT_FIRST
+#define SK_MFMA_ACT_FIRST 1
+#endif
+constexpr int kPipeDot4 = SK_PIPE_DOT4, kPrimeDot4 = SK_PRIME_DOT4;
+constexpr int kPipeMfma = SK_PIPE_MFMA, kPrimeMfma = SK_PRIME_MFMA;
+constexpr int pipe_of(bool dot4) { return dot4 ? kPipeDot4 : kPipeMfma; }
 constexpr int SMAX = 32;       // largest number of K-slices
-constexpr int kMaxTilesPerGroup = 64;
 constexpr int kMaxExperts = 64;          // experts per expert-bank call
+// Weight-stream buffer loads: the resource of a slot group spans kRsrcMax bytes
+// from the group's first byte (every real slot lies inside), and an offset of
+// kOutside lies past it, so such a load returns zeros without touching memory.
+constexpr int kRsrcMax = 0x7FFFFFFF;
+constexpr int kOutside = (int)0x80000000u;
+constexpr int kRsrcFlags = 0x00020000;   // raw (untyped) 32-bit dword access
+#ifndef SK_STREAM_POLICY
+#define SK_STREAM_POLICY 18
+#endif
+// Cache policy of the weight stream: non-temporal (2) at device scope (16).
+// Each weight byte is read once per call; on a streaming probe of the decoder
+// and lm_head sizes this policy read 10-17% faster than the default one.
+constexpr int kStreamPolicy = SK_STREAM_POLICY;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -72,9 +103,8 @@ struct KArgs {
     int8_t* q_out;
     float* sx_out;
     int32_t* p_out;
-    WsHeader* ws;
-    uint32_t* cnt;
-    u64* part;
+    WsHeader* ws;           // caller-owned workspace (S > 1 only)
+    u64* part;              // its tagged split-K partials
     int n, k, m;
     int T, KB, kg;
     int S, R, P, TW, KW, spw, KBs, KS, WPR, ks;
@@ -94,10 +124,12 @@ struct KArgs {
     // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
     // wave index within the row (14-18) and activation chunk steps (19-22)
     uint32_t wtab[NW];
-    // expert banks: logical tile t is tile t % tpe of expert emap[t / tpe] in
-    // the bank (tpe = tiles per expert; 0 for a plain weight)
+    // expert banks: logical tile t is tile t % tpe of expert experts[t / tpe]
+    // (a device array) in the bank of n_experts experts (tpe = tiles per
+    // expert; 0 for a plain weight)
     int tpe;
-    uint16_t emap[kMaxExperts];
+    int n_experts;
+    const int32_t* experts;
 };
 
 struct Smem {
@@ -110,7 +142,7 @@ struct Smem {
     float rr[8];
     int miss[SMAX];
     uint32_t tag;
-    int last[kMaxTilesPerGroup];
+    int last;
 };
 
 typedef void (*KernelFn)(KArgs);
@@ -536,6 +568,16 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
     }
 }
 
+// y of output row omm in tile ot from its scaled sum: sx * sum, or NaN for a
+// tile of an expert-bank call whose listed id lies outside the bank.
+__device__ inline float out_value(const KArgs& a, const Smem& sm, int ot, int omm, float sum) {
+    if (a.tpe) {
+        const int e = a.experts[ot / a.tpe];
+        if (e < 0 || e >= a.n_experts) return __builtin_nanf("");
+    }
+    return sm.sx[omm] * sum;
+}
+
 // --------------------------------------------------------------------------
 // the kernel
 // --------------------------------------------------------------------------
@@ -562,6 +604,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : PRO == PRO_NONE ? (WIDE ? 40 : 32) : ONE ? 32 : 16;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
+    constexpr int PIPE = DOT4 ? kPipeDot4 : kPipeMfma;
+    constexpr int PRIME = DOT4 ? kPrimeDot4 : kPrimeMfma;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
@@ -602,7 +646,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
         if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
     }
-    const uint32_t gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the launch generation (only launches that split K touch the workspace)
+    const uint32_t gen = (!ONE && a.S > 1) ? __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
 
     // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
     // wave wv works on tile group tg (every TW-th tile) and super-blocks
@@ -649,17 +694,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int lh_full = 16 * 64 + lane * 8, lh_rag = lane_rag_ok ? nr_rag * 64 + (hl * nr_rag + nl) * 8 : 0;
     const int ls_full = nl * NG * 4, ls_rag = lane_rag_ok ? nl * NG * 4 : 0;
 
-    // Load-side cursor: group lg of tile step lj.  Its slots' weights and
-    // scales start at byte offsets gw / gs and step by gws / gss; grg marks the
-    // ragged tile; gnv counts the slots that hold work.  A stand-in group has
-    // zero offsets and strides.  All of it is wave-uniform and set once per
-    // group, so a slot's load is a few scalar operations.
+    // Load-side cursor: group lg of tile step lj.  Its slots' weights start at
+    // byte offset gw of the weight and step by gws; their scales sit gso bytes
+    // after the weights and step by gss; grg marks the ragged tile; gnv counts
+    // the slots that hold work.  All of it is wave-uniform and set once per
+    // group, so a slot's load is a few scalar operations.  The loads go through
+    // a buffer resource based at the group's first byte: padding slots and
+    // stand-in groups (no work) use an offset past the resource, which reads
+    // zeros without a memory access, so every wave issues the same loads (the
+    // compiler's wait counts stay exact) and no stand-in load costs bandwidth.
     int lj = 0, lg = 0;
-    int64_t gw = 0, gs = 0;
-    int gws = 0, gss = 0, gnv = 0;
+    int64_t gw = 0;
+    int gso = 0, gws = 0, gss = 0, gnv = 0;
     bool grg = false;
+    __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.data), (short)0, 0, kRsrcFlags);
     // canonical layout (CANON, W4 only): per-lane offsets of the group's tile
     // (rows past N read row N - 1; those lanes' sums are never stored)
+    int64_t gs = 0;
     int glw = 0, gls = 0;
     const int rb = a.k / 2;                          // bytes per canonical weight row
     auto group_setup = [&]() {
@@ -679,14 +730,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         } else {
             grg = valid && t == a.t_rag;
             // the bank's tile behind logical tile t (expert banks), else t; a
-            // stand-in group maps tile 0 so the map is never read past the list
+            // stand-in group maps tile 0 so the list is never read past its end,
+            // and an id outside the bank reads expert 0 (its rows are written as NaN)
             const int tv = valid ? t : 0;
-            const int tb = a.tpe ? a.emap[tv / a.tpe] * a.tpe + tv % a.tpe : t;
+            int tb = t;
+            if (a.tpe) {
+                const int e = a.experts[tv / a.tpe];
+                tb = ((e >= 0 && e < a.n_experts) ? e : 0) * a.tpe + tv % a.tpe;
+            }
             const int64_t wo = (int64_t)tb * a.tile_full + (int64_t)kb * a.sbf;
             gw = !valid ? 0 : grg ? a.rag_w + (int64_t)kb * a.rag_sbw : wo;
-            gs = !valid ? 0 : grg ? a.rag_s + (int64_t)kb * a.rag_sbs : wo + a.swo;
-            gws = !valid ? 0 : grg ? a.rag_sbw : a.sbf;
-            gss = !valid ? 0 : grg ? a.rag_sbs : a.sbf;
+            // scales relative to the weights: the ragged tile keeps them after all
+            // of its weight parts, (KB - kb) weight parts and kb scale parts on
+            gso = grg ? (a.KB - kb) * a.rag_sbw + kb * a.rag_sbs : a.swo;
+            gws = grg ? a.rag_sbw : a.sbf;
+            gss = grg ? a.rag_sbs : a.sbf;
+            grs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.data) + gw, (short)0,
+                                                    valid ? kRsrcMax : 0, kRsrcFlags);
         }
     };
     auto group_next = [&]() {
@@ -697,40 +757,61 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         group_setup();
     };
     group_setup();
-    // Slot d of the load group into registers (padding slots re-read slot 0).
-    // Every wave issues the same load instructions, so the compiler's wait
-    // counts are exact.
+    // Slot d of the load group into registers.  Every wave issues the same
+    // load instructions, so the compiler's wait counts are exact.
     auto load_slot = [&](const int d, uint4& w4, uint2& h2, float4& sv, float4& sv2) {
-        const int dd = d < gnv ? d : 0;
-        const uint8_t* wb = a.data + gw + dd * gws;
-        const uint8_t* sb = a.data + gs + dd * gss;
-        const int lw = CANON ? glw : grg ? lw_rag : lw_full;
-        const int ls = CANON ? gls : grg ? ls_rag : ls_full;
-        if (CANON) {
+        if constexpr (CANON) {
             // octet hl of each 32-k block j: 4 bytes, 16 bytes apart in the row
-            const uint32_t* p = reinterpret_cast<const uint32_t*>(wb + lw);
-            w4 = make_uint4(p[0], p[4], p[8], p[12]);
+            // (padding slots re-read slot 0)
+            const int dd = d < gnv ? d : 0;
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(a.data + gw + dd * gws + glw);
+            w4 = make_uint4(__builtin_nontemporal_load(p), __builtin_nontemporal_load(p + 4),
+                            __builtin_nontemporal_load(p + 8), __builtin_nontemporal_load(p + 12));
+            const float* sp = reinterpret_cast<const float*>(a.data + gs + dd * gss + gls);
+            if (NG == 8) {
+                sv = make_float4(__builtin_nontemporal_load(sp), __builtin_nontemporal_load(sp + 1),
+                                 __builtin_nontemporal_load(sp + 2), __builtin_nontemporal_load(sp + 3));
+                sv2 = make_float4(__builtin_nontemporal_load(sp + 4), __builtin_nontemporal_load(sp + 5),
+                                  __builtin_nontemporal_load(sp + 6), __builtin_nontemporal_load(sp + 7));
+            } else if (NG == 4) {
+                sv = make_float4(__builtin_nontemporal_load(sp), __builtin_nontemporal_load(sp + 1),
+                                 __builtin_nontemporal_load(sp + 2), __builtin_nontemporal_load(sp + 3));
+            } else if (NG == 2) {
+                sv = make_float4(__builtin_nontemporal_load(sp), __builtin_nontemporal_load(sp + 1), 0.0f, 0.0f);
+            } else {
+                sv = make_float4(__builtin_nontemporal_load(sp), 0.0f, 0.0f, 0.0f);
+            }
         } else {
-            w4 = *reinterpret_cast<const uint4*>(wb + lw);
-        }
-        if (FMT == FMT_W6) h2 = *reinterpret_cast<const uint2*>(wb + (grg ? lh_rag : lh_full));
-        if (NG == 8) {
-            sv = *reinterpret_cast<const float4*>(sb + ls);
-            sv2 = *reinterpret_cast<const float4*>(sb + ls + 16);
-        } else if (NG == 4) {
-            sv = *reinterpret_cast<const float4*>(sb + ls);
-        } else if (NG == 2) {
-            const float2 v = *reinterpret_cast<const float2*>(sb + ls);
-            sv = make_float4(v.x, v.y, 0.0f, 0.0f);
-        } else {
-            sv = make_float4(*reinterpret_cast<const float*>(sb + ls), 0.0f, 0.0f, 0.0f);
+            const bool on = d < gnv;
+            const int lw = grg ? lw_rag : lw_full;
+            const int ls = grg ? ls_rag : ls_full;
+            const int wo = on ? d * gws + lw : kOutside;
+            const int so = on ? gso + d * gss + ls : kOutside;
+            w4 = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(grs, wo, 0, kStreamPolicy));
+            if (FMT == FMT_W6)
+                h2 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   grs, on ? d * gws + (grg ? lh_rag : lh_full) : kOutside, 0,
+                                                   kStreamPolicy));
+            if (NG == 8) {
+                sv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, so, 0, kStreamPolicy));
+                sv2 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, on ? so + 16 : kOutside, 0,
+                                                                                       kStreamPolicy));
+            } else if (NG == 4) {
+                sv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, so, 0, kStreamPolicy));
+            } else if (NG == 2) {
+                const float2 v = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(grs, so, 0, kStreamPolicy));
+                sv = make_float4(v.x, v.y, 0.0f, 0.0f);
+            } else {
+                sv = make_float4(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(grs, so, 0, kStreamPolicy)),
+                                 0.0f, 0.0f, 0.0f);
+            }
         }
     };
 
     // M >= 2 (more activation loads, and with S > 1 every slice's statistics
     // gate the exchange): the weight stream starts once the activations are in,
     // so their loads do not queue behind a burst of cold weight requests.
-    if (!DOT4) {
+    if (!DOT4 && SK_MFMA_ACT_FIRST) {
         __builtin_amdgcn_s_waitcnt(0xF70);    // vmcnt(0)
         __syncthreads();
     }
@@ -809,7 +890,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             }
         }
         const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
-        const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+        const float inv = (sx > 0.0f) ? 1.0f / sx : 0.0f;   // sx == 0: every code is 0
         if (row_lead) {
             sm.sx[am.m] = sx;
             if (DBG && a.sx_out && r == 0 && s == 0) a.sx_out[am.m] = sx;
@@ -1089,7 +1170,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 }
                 if (ONE || a.S == 1) {
                     if (ot * TILE_ROWS + onn < a.n)
-                        a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (osum * KINV);
+                        a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = out_value(a, sm, ot, omm, osum * KINV);
                 } else {
                     const u64 v = ((u64)sm.tag << 32) | __float_as_uint(osum);
                     __hip_atomic_store(&a.part[(((int64_t)ot * a.S + s) * M + omm) * 16 + onn], v,
@@ -1117,29 +1198,26 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         for (int rr = 0; rr < 4; ++rr) acc[rr] = 0.0f;
     }
 
-    // 5. merge the slices' partials: the last workgroup of each tile adds them
+    // 5. merge the slices' partials: the last of range r's S workgroups to
+    //    arrive adds them, for every tile of the range, in slice order
     if (!ONE && a.S > 1) {
         __syncthreads();
-        for (int c0 = 0; c0 < ntile; c0 += kMaxTilesPerGroup) {
-            const int nc = min(kMaxTilesPerGroup, ntile - c0);
-            if (tid < nc) {
-                const int tt = t_begin + c0 + tid;
-                const uint32_t old =
-                    __hip_atomic_fetch_add(&a.cnt[tt], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const int lst = (old == (uint32_t)(a.S - 1));
-                if (lst) __hip_atomic_store(&a.cnt[tt], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sm.last[tid] = lst;
-            }
-            __syncthreads();
-            for (int e = tid; e < nc * M * 16; e += NT) {
+        if (tid == 0) {
+            const uint32_t old = __hip_atomic_fetch_add(&a.ws->cnt[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const int lst = old == (uint32_t)(a.S - 1);
+            if (lst) __hip_atomic_store(&a.ws->cnt[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            sm.last = lst;
+        }
+        __syncthreads();
+        if (sm.last) {
+            for (int e = tid; e < ntile * M * 16; e += NT) {
                 const int ci = e / (M * 16);
-                if (!sm.last[ci]) continue;
                 const int omm = (e / 16) % M;
                 const int onn = e & 15;
-                const int ot = t_begin + c0 + ci;
+                const int ot = t_begin + ci;
                 float tot = 0.0f;
                 for (int sl = 0; sl < a.S; ++sl) {
-                    // Every partial was stored before its workgroup counted the tile, so its
+                    // Every partial was stored before its workgroup counted itself, so its
                     // tag shows up shortly; the bound only guards against a hang (a missing
                     // partial would turn y into NaN rather than stall the GPU).
                     const u64* p = &a.part[(((int64_t)ot * a.S + sl) * M + omm) * 16 + onn];
@@ -1149,9 +1227,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     tot += ((uint32_t)(v >> 32) == sm.tag) ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
                 }
                 if (ot * TILE_ROWS + onn < a.n)
-                    a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = sm.sx[omm] * (tot * KINV);
+                    a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = out_value(a, sm, ot, omm, tot * KINV);
             }
-            __syncthreads();
         }
         // generation bookkeeping for the exchange words and tags
         if (tid == 0) {

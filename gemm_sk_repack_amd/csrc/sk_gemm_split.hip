@@ -51,7 +51,7 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const void* x, int k, int8
 #pragma unroll
     for (int w = 0; w < QT / 64; ++w) amx = fmaxf(amx, wmax[w]);
     const float sx = (amx > 0.0f) ? amx / 127.0f : 0.0f;
-    const float inv = (amx > 0.0f) ? 1.0f / sx : 0.0f;
+    const float inv = (sx > 0.0f) ? 1.0f / sx : 0.0f;   // sx == 0: every code is 0
     const float inv_lo = inv * kInvLo, inv_hi = inv * kInvHi;
     if (tid == 0) sx_out[m] = sx;
     for (int c = tid; c < nch; c += QT) {

@@ -38,25 +38,38 @@ struct GemmCall {
     int spin_limit;        // polls of an exchange slot before computing it locally (0 = default)
     bool canon;            // weight in the canonical [codes | scales] layout (no repack)
     // expert bank: the call's N is n_list experts x rows_per_expert rows, drawn
-    // from the bank by `experts` (host ids); rows_per_expert == 0 otherwise
+    // from the bank by `experts` (device ids); rows_per_expert == 0 otherwise
     int rows_per_expert;
     int n_list;
+    int n_experts;         // experts in the bank (ids outside [0, n_experts) give NaN rows)
     const int32_t* experts;
+    void* ws;              // caller-owned workspace (null when the plan needs none)
 };
 
 // Largest K a GEMM call accepts.
 constexpr int64_t kMaxGemmK = 17408;
+// Largest number of workgroups per K-slice (one arrival counter each).
+constexpr int kMaxRanges = 1024;
 
-// Device workspace header (zeroed once when allocated).  `gen` counts launches
-// that used the cross-slice exchange; slots carry gen + 1 as their tag.
+// Header of the caller-owned GEMM workspace; only launches that split K into
+// S > 1 slices touch it.  It must be zero before its first use; every launch
+// leaves it ready for the next.  `gen` counts those launches; exchange slots
+// and partials carry gen + 1 as their tag, so stale words from earlier calls
+// (of any shape) are never taken for fresh ones.  `cnt[r]` counts the slices
+// of workgroup range r that have stored their partials; the last to arrive
+// resets it and merges.
 struct WsHeader {
     uint32_t gen;
     uint32_t done;
-    uint32_t pad[30];
+    uint32_t pad[62];
+    uint32_t cnt[kMaxRanges];
     unsigned long long amax[32 * 8];   // (tag << 32) | float bits, [slice][row]
     unsigned long long ssh[32 * 8];    // (tag << 32) | high half of the double sum of squares
     unsigned long long ssl[32 * 8];    // (tag << 32) | low half
 };
+// Bytes reserved for the header; the tagged split-K partials follow it.
+constexpr size_t kWsHeaderBytes = 16384;
+static_assert(sizeof(WsHeader) <= kWsHeaderBytes, "workspace header too large");
 
 // How one GEMM call is laid out on the GPU (pure host arithmetic).
 struct Plan {
@@ -72,12 +85,18 @@ struct Plan {
     bool wide;    // the kernel instances with the larger activation budget
     int ks;       // LDS row stride of q
     size_t lds;   // dynamic LDS bytes
-    size_t part_floats;  // workspace floats for slice partials
+    size_t part_floats;  // workspace words (8 bytes) for slice partials
     bool ok;
 };
 
+// Workspace bytes a launch with this plan needs (0 when K is not split).
+inline size_t workspace_bytes(const Plan& p) {
+    return p.S > 1 ? kWsHeaderBytes + p.part_floats * 8 : 0;
+}
+
 Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override);
-bool gemm_plan_ok(const Geom& G, int m, int pro);
+// The plan a call on the current device would use (ok == false if none).
+Plan gemm_plan(const Geom& G, int m, int pro);
 void set_split_override(int s);
 hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st);
 // Per-row int8 quantisation of x [M][K] into q [M][K] and sx [M] as its own

@@ -40,13 +40,16 @@
  *
  * Conventions: pointers are DEVICE pointers to caller-owned memory unless
  * stated; `stream` is a hipStream_t as void*; validation is synchronous and a
- * rejected call launches nothing.  sk_decode_attention uses a per-device
- * workspace: a generation word, one arrival counter per KV head, one flag per
- * (KV head, prefix range) and Hkv * ranges * 16*ceil(M*G/16) * 130 floats of
- * partial results (at most 64 ranges per head).  It is allocated and zeroed
- * by the first call that needs it and grown with a device synchronisation (so
- * such a call must not be under stream capture); calls on one device must not
- * overlap in time.  Each launch leaves the counters at zero for the next one.
+ * rejected call launches nothing.  Nothing here allocates, frees or
+ * synchronises.  A launch that splits the prefix over several ranges per KV
+ * head exchanges partial results through a caller-owned device `workspace`
+ * (same rules as the GEMM workspace of sk_repack.h: 256-byte aligned, zero
+ * before its first use, left ready for the next call of any shape; calls
+ * sharing one workspace must be ordered): a generation word, one arrival
+ * counter per KV head and one flag per (KV head, prefix range), 133376 bytes
+ * in all, then Hkv * ranges * 16*ceil(M*G/16) * 130 floats of partial
+ * results (at most 64 ranges per head).  sk_attention_workspace_size gives the
+ * bytes a call needs (0 when the prefix is not split).
  */
 #ifndef SK_ATTENTION_H
 #define SK_ATTENTION_H
@@ -84,11 +87,19 @@ sk_status sk_kv_append(void* kv, int hkv, int cap, int pos, int t,
  * launch.
  * Errors: NULL, SHAPE (M not in 1..8, hq % hkv, L < M, L > cap, cap % 32,
  *         scale not finite and > 0), UNSUPPORTED (M * Hq / Hkv > 64,
- *         Hkv > 512, cap > 4194304), ALIGN, HIP.
+ *         Hkv > 512, cap > 4194304), ALIGN, WORKSPACE, HIP.
  */
 sk_status sk_decode_attention(const uint16_t* q, int m, int hq, int hkv,
                               const void* kv, int cap, int len, float scale,
-                              float* out, void* stream);
+                              float* out, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * Bytes of workspace sk_decode_attention needs for these sizes on the current
+ * device (0 when the prefix is not split).
+ * Errors: NULL, SHAPE, UNSUPPORTED (as sk_decode_attention), HIP (no device).
+ */
+sk_status sk_attention_workspace_size(int m, int hq, int hkv, int len, size_t* bytes);
 
 /*
  * Host-side packing into the cache layout (no GPU): k and v are host arrays

@@ -22,18 +22,19 @@
  *
  * Conventions for every entry point
  *  - All pointers except `sk_weight*` itself are DEVICE pointers to memory the
- *    caller owns.  The repack entry points allocate no device memory.  The
- *    GEMM entry points share one per-device workspace: a header of about 6 KiB (a
- *    generation counter and the activation-statistics exchange), a 4-byte
- *    arrival counter per 16-row tile and, for launches that split K into S
- *    slices, 8 bytes per (slice, output element).  It is allocated and zeroed
- *    by the first GEMM call on the device and grown (with a device
- *    synchronisation) by the first call that needs more, so such a call must
- *    not be inside a stream capture; it is kept until the process ends.  A
- *    call that fits the current workspace allocates nothing (graph capture of
- *    such calls works).  GEMM calls on one device must not overlap in time:
- *    issue them on one stream, or order them with events.  Every launch
- *    leaves the workspace in the state the next launch expects.
+ *    caller owns.  No entry point allocates, frees or synchronises anything:
+ *    every call validates on the host, enqueues its kernels and returns.
+ *  - Workspace.  A GEMM launch whose K is split over several workgroups
+ *    exchanges row statistics and partial sums through a caller-owned device
+ *    buffer `workspace` of `workspace_bytes` bytes; sk_gemm_workspace_size
+ *    gives the bytes a call needs (0 for most calls: then `workspace` may be
+ *    NULL).  The buffer must be 256-byte aligned and its contents must be zero
+ *    before the first call that uses it (e.g. one hipMemset after
+ *    allocation); each launch leaves it ready for the next, whatever the
+ *    shapes of the calls that share it.  Calls that share one workspace must
+ *    be ordered (one stream, or events); calls with different workspaces may
+ *    run concurrently on different streams.  A missing, misaligned or too
+ *    small workspace is SK_ERR_WORKSPACE.
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Calls only enqueue work and return; nothing synchronises the host.
  *  - Validation is synchronous and happens before any GPU work: on any status
@@ -65,7 +66,9 @@ typedef enum {
     SK_ERR_LAYOUT = 5,      /* GEMM on a canonical (not repacked) weight, repack of an
                                already repacked weight, or unrepack of a canonical one      */
     SK_ERR_HIP = 6,         /* a HIP runtime call failed (launch error, no device, ...)    */
-    SK_ERR_UNSUPPORTED = 7  /* allowed by [FMT] but not by this backend (see below)         */
+    SK_ERR_UNSUPPORTED = 7, /* allowed by [FMT] but not by this backend (see below)         */
+    SK_ERR_WORKSPACE = 8    /* the call needs a workspace and `workspace` is NULL, not
+                               256-byte aligned, or smaller than sk_gemm_workspace_size   */
 } sk_status;
 
 typedef enum { SK_F32 = 0, SK_BF16 = 1 } sk_dtype;
@@ -144,6 +147,20 @@ sk_status sk_repack_w4a8(sk_weight* w, void* stream);
 sk_status sk_unrepack_w4a8(sk_weight* w, void* stream);
 
 /*
+ * Bytes of workspace a GEMM call needs: a call of any GEMM entry point with a
+ * weight of n x k, group size `group`, format `format`, M = m rows and
+ * `prologue` (0 none, 1 RMSNorm, 2 SwiGLU; the split-path entry points use 0;
+ * for sk_gemm_experts, n = n_list * rows_per_expert).  *bytes = 0 when the
+ * call needs none.  The size depends on the device the call runs on (its
+ * compute-unit count): query with that device current.  It is 16 KiB plus
+ * 128 * M * S bytes per 16-row tile, S being the number of K-slices the
+ * launch uses (at most 32).
+ * Errors: NULL, FORMAT, SHAPE, UNSUPPORTED (as for the GEMM calls).
+ */
+sk_status sk_gemm_workspace_size(int n, int k, int group, int format, int m, int prologue,
+                                 size_t* bytes);
+
+/*
  * Skinny W4A8 linear [LIN]: y[M][N] = sx[m] * sum_j s[n][j] * P[m][n][j],
  * P = per-group integer dot product of the weights (or, for the codebook,
  * the float levels) with q, where (q, sx) = per-row int8 quantisation of x
@@ -156,14 +173,16 @@ sk_status sk_unrepack_w4a8(sk_weight* w, void* stream);
  *   x  : device [M][K], row-major, dtype xt (SK_F32 or SK_BF16), 16-byte aligned
  *   m  : 1..8
  *   y  : device [M][N] float32, row-major, 16-byte aligned (fully overwritten)
- * Errors: NULL, SHAPE, ALIGN, FORMAT (not a W4 format), LAYOUT, UNSUPPORTED, HIP.
+ *   workspace, workspace_bytes : see the conventions above
+ * Errors: NULL, SHAPE, ALIGN, FORMAT (not a W4 format), LAYOUT, UNSUPPORTED,
+ *         WORKSPACE, HIP.
  */
 sk_status sk_gemm_w4a8(const sk_weight* w, const void* x, int xt, int m,
-                       float* y, void* stream);
+                       float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Same for a repacked SK_W6_SYM weight [LIN] [FMT]. */
 sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m,
-                       float* y, void* stream);
+                       float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * RMSNorm prologue fused into the quantisation [LIN]:
@@ -176,7 +195,7 @@ sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m,
  */
 sk_status sk_gemm_fused_rmsnorm(const sk_weight* w, const void* x, int xt,
                                 const float* gamma, float eps, int m,
-                                float* y, void* stream);
+                                float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * SwiGLU prologue fused into the quantisation [LIN]:
@@ -189,7 +208,8 @@ sk_status sk_gemm_fused_rmsnorm(const sk_weight* w, const void* x, int xt,
  * Any weight format.
  */
 sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void* up,
-                               int64_t ld, int xt, int m, float* y, void* stream);
+                               int64_t ld, int xt, int m, float* y, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /*
  * Expert bank [FMT, embeddings and MoE: grouped W4A8/W6A8 banks store their
@@ -198,18 +218,24 @@ sk_status sk_gemm_fused_swiglu(const sk_weight* w, const void* gate, const void*
  * [e * rows_per_expert, (e + 1) * rows_per_expert).  One launch computes, for
  * each of the n_list listed experts, its rows times x (quantised once):
  *   y[m][i * rows_per_expert + j] = (expert experts[i], row j) . x[m]
- *   experts : HOST array of n_list expert ids in [0, E) (repeats allowed),
- *             read at the call (a captured graph keeps the list it saw)
+ *   experts : DEVICE array of n_list int32 expert ids (4-byte aligned), read
+ *             by the kernel when it runs, so a captured graph replays with
+ *             whatever ids the array then holds (e.g. a router's output).
+ *             Repeats are allowed.  An id outside [0, E) cannot be rejected on
+ *             the host: that expert's block of y is written as NaN (no memory
+ *             outside the bank is read).
  *   y       : device [M][n_list * rows_per_expert] float32, 16-byte aligned
- *   rows_per_expert a multiple of 16 dividing bank->n; 1 <= n_list <= 64.
+ *   rows_per_expert a multiple of 16 dividing bank->n; n_list >= 1 and
+ *   n_list * rows_per_expert <= 2^24.
  * Each listed expert's output is what sk_gemm_w4a8 / sk_gemm_w6a8 gives on
  * that expert's rows alone: the same q and the same int32 partials; only the
  * grouping of the fp32 sums across waves may differ with the launch plan.
- * Errors: NULL, SHAPE (rows_per_expert, n_list or an id out of range), ALIGN,
- * FORMAT, LAYOUT, UNSUPPORTED, HIP.
+ * Errors: NULL, SHAPE (rows_per_expert, n_list), ALIGN, FORMAT, LAYOUT,
+ * UNSUPPORTED, WORKSPACE, HIP.
  */
 sk_status sk_gemm_experts(const sk_weight* bank, int rows_per_expert, const int32_t* experts,
-                          int n_list, const void* x, int xt, int m, float* y, void* stream);
+                          int n_list, const void* x, int xt, int m, float* y, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /*
  * The split path, kept to measure what the stream layout and the fused
@@ -242,7 +268,7 @@ sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t* q, float
  * not SK_W4_SYM).
  */
 sk_status sk_gemm_w4a8_canonical(const sk_weight* w, const void* x, int xt, int m,
-                                 float* y, void* stream);
+                                 float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The same GEMM with the activations already quantised (by sk_quantize_rows):
@@ -250,7 +276,7 @@ sk_status sk_gemm_w4a8_canonical(const sk_weight* w, const void* x, int xt, int 
  * Errors: as sk_gemm_w4a8_canonical.
  */
 sk_status sk_gemm_w4a8_canonical_q(const sk_weight* w, const int8_t* q, const float* sx, int m,
-                                   float* y, void* stream);
+                                   float* y, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Test hook: the GEMM kernels instantiated with an export flag.  Runs the same
@@ -266,7 +292,7 @@ sk_status sk_gemm_w4a8_canonical_q(const sk_weight* w, const int8_t* q, const fl
 sk_status sk_debug_gemm(const sk_weight* w, int prologue, const void* x, const void* x2,
                         int64_t ld, int xt, const float* gamma, float eps, int m,
                         float* y, int8_t* q_out, float* sx_out, int32_t* p_out,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert sk.status_string(s)
     assert sk.status_string(99) == "unknown status"
 
@@ -42,8 +42,8 @@ def W(n=64, k=256, g=32, fmt=0, layout=0, data=FAKE, nbytes=None, cb=None, reser
     return sk.SkWeightStruct(n, k, g, fmt, layout, reserved, data, nbytes, cb)
 
 
-def gemm(w, x=FAKE, xt=0, m=1, y=FAKE):
-    return sk.LIB.sk_gemm_w4a8(ctypes.byref(w), x, xt, m, y, None)
+def gemm(w, x=FAKE, xt=0, m=1, y=FAKE, ws=None, wsb=0):
+    return sk.LIB.sk_gemm_w4a8(ctypes.byref(w), x, xt, m, y, ws, wsb, None)
 
 
 def test_null_pointers():
@@ -52,9 +52,9 @@ def test_null_pointers():
     assert gemm(W(layout=1), x=None) == sk.SK_ERR_NULL
     assert gemm(W(layout=1), y=None) == sk.SK_ERR_NULL
     w = W(layout=1)
-    assert sk.LIB.sk_gemm_fused_rmsnorm(ctypes.byref(w), FAKE, 0, None, 1e-6, 1, FAKE, None) \
+    assert sk.LIB.sk_gemm_fused_rmsnorm(ctypes.byref(w), FAKE, 0, None, 1e-6, 1, FAKE, None, 0, None) \
         == sk.SK_ERR_NULL
-    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, None, 256, 0, 1, FAKE, None) \
+    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, None, 256, 0, 1, FAKE, None, 0, None) \
         == sk.SK_ERR_NULL
 
 
@@ -68,7 +68,7 @@ def test_format_errors():
     w6 = W(fmt=2, g=64, layout=1)
     assert gemm(w6) == sk.SK_ERR_FORMAT
     w4 = W(layout=1)
-    assert sk.LIB.sk_gemm_w6a8(ctypes.byref(w4), FAKE, 0, 1, FAKE, None) == sk.SK_ERR_FORMAT
+    assert sk.LIB.sk_gemm_w6a8(ctypes.byref(w4), FAKE, 0, 1, FAKE, None, 0, None) == sk.SK_ERR_FORMAT
     assert gemm(W(reserved=1, layout=1)) == sk.SK_ERR_FORMAT
 
 
@@ -83,7 +83,7 @@ def test_shape_errors():
     assert gemm(W(n=0, layout=1)) == sk.SK_ERR_SHAPE
     assert gemm(W(layout=1, nbytes=12345)) == sk.SK_ERR_SHAPE
     w = W(layout=1)
-    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, FAKE, 255, 0, 1, FAKE, None) \
+    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, FAKE, 255, 0, 1, FAKE, None, 0, None) \
         == sk.SK_ERR_SHAPE
 
 
@@ -93,7 +93,7 @@ def test_align_errors():
     assert gemm(W(layout=1), y=FAKE + 4) == sk.SK_ERR_ALIGN
     w = W(layout=1)
     # ld * 4 bytes must be a multiple of 16
-    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, FAKE, 258, 0, 1, FAKE, None) \
+    assert sk.LIB.sk_gemm_fused_swiglu(ctypes.byref(w), FAKE, FAKE, 258, 0, 1, FAKE, None, 0, None) \
         == sk.SK_ERR_ALIGN
 
 
@@ -117,19 +117,50 @@ def test_backend_restrictions():
 
 
 def test_expert_bank_validation():
+    """The expert list is a device array read by the kernel: the host checks the
+    pointer, its alignment, rows_per_expert and the list length, not the ids."""
     ex = sk.LIB.sk_gemm_experts
-    ids = (ctypes.c_int32 * 2)(0, 1)
-    bad = (ctypes.c_int32 * 1)(4)
+    ids = FAKE
     bank = W(n=512, layout=1)                       # 4 experts of 128 rows
-    assert ex(ctypes.byref(bank), 128, None, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_NULL
-    assert ex(ctypes.byref(bank), 100, ids, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
-    assert ex(ctypes.byref(bank), 96, ids, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
-    assert ex(ctypes.byref(bank), 128, ids, 0, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
-    assert ex(ctypes.byref(bank), 128, ids, 65, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
-    assert ex(ctypes.byref(bank), 128, bad, 1, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_SHAPE
-    assert ex(ctypes.byref(bank), 128, ids, 2, FAKE, 0, 9, FAKE, None) == sk.SK_ERR_SHAPE
-    assert ex(ctypes.byref(W(n=512, layout=0)), 128, ids, 2, FAKE, 0, 1, FAKE, None) == sk.SK_ERR_LAYOUT
-    assert ex(ctypes.byref(bank), 128, ids, 2, FAKE + 4, 0, 1, FAKE, None) == sk.SK_ERR_ALIGN
+
+    def call(b=bank, rows=128, e=ids, nl=2, x=FAKE, m=1):
+        return ex(ctypes.byref(b), rows, e, nl, x, 0, m, FAKE, None, 0, None)
+    assert call(e=None) == sk.SK_ERR_NULL
+    assert call(rows=100) == sk.SK_ERR_SHAPE
+    assert call(rows=96) == sk.SK_ERR_SHAPE
+    assert call(nl=0) == sk.SK_ERR_SHAPE
+    assert call(nl=(1 << 24) // 128 + 1) == sk.SK_ERR_SHAPE
+    assert call(m=9) == sk.SK_ERR_SHAPE
+    assert call(e=FAKE + 2) == sk.SK_ERR_ALIGN
+    assert call(b=W(n=512, layout=0)) == sk.SK_ERR_LAYOUT
+    assert call(x=FAKE + 4) == sk.SK_ERR_ALIGN
+
+
+def test_workspace_size_and_validation():
+    """Launches that split K need a caller-owned workspace; the size query and
+    the checks are host arithmetic."""
+    size = sk.gemm_workspace_size
+    # K = 4096 at M = 1 runs in one slice: no workspace
+    assert size(6144, 4096, 32, 0, 1) == 0
+    # the 27B-class down projection at M = 8 splits K
+    plan = sk.gemm_plan(5120, 17408, 32, 0, 8)
+    assert plan["S"] > 1
+    need = size(5120, 17408, 32, 0, 8)
+    assert need == 16384 + plan["part_floats"] * 8
+    assert need == 16384 + 320 * plan["S"] * 8 * 128
+    w = W(n=5120, k=17408, layout=1)
+    assert gemm(w, m=8) == sk.SK_ERR_WORKSPACE                       # missing
+    assert gemm(w, m=8, ws=FAKE, wsb=need - 256) == sk.SK_ERR_WORKSPACE   # too small
+    assert gemm(w, m=8, ws=FAKE + 16, wsb=need) == sk.SK_ERR_WORKSPACE   # not 256-byte aligned
+    # query errors
+    out = ctypes.c_size_t()
+    f = sk.LIB.sk_gemm_workspace_size
+    assert f(64, 256, 32, 0, 1, 0, None) == sk.SK_ERR_NULL
+    assert f(64, 256, 32, 9, 1, 0, ctypes.byref(out)) == sk.SK_ERR_FORMAT
+    assert f(64, 256, 32, 0, 1, 5, ctypes.byref(out)) == sk.SK_ERR_FORMAT
+    assert f(64, 256, 32, 0, 9, 0, ctypes.byref(out)) == sk.SK_ERR_SHAPE
+    assert f(64, 48, 12, 0, 1, 0, ctypes.byref(out)) == sk.SK_ERR_SHAPE
+    assert f(64, 20480, 32, 0, 1, 0, ctypes.byref(out)) == sk.SK_ERR_UNSUPPORTED
 
 
 def test_split_path_validation():
@@ -143,13 +174,13 @@ def test_split_path_validation():
     assert q(FAKE + 4, 0, 1, 256, FAKE, FAKE, None) == sk.SK_ERR_ALIGN
     assert q(FAKE, 0, 1, 256, FAKE, FAKE + 2, None) == sk.SK_ERR_ALIGN
     can = sk.LIB.sk_gemm_w4a8_canonical
-    assert can(ctypes.byref(W(layout=1)), FAKE, 0, 1, FAKE, None) == sk.SK_ERR_LAYOUT
-    assert can(ctypes.byref(W(fmt=2, g=64, layout=0)), FAKE, 0, 1, FAKE, None) == sk.SK_ERR_FORMAT
-    assert can(ctypes.byref(W(layout=0)), None, 0, 1, FAKE, None) == sk.SK_ERR_NULL
+    assert can(ctypes.byref(W(layout=1)), FAKE, 0, 1, FAKE, None, 0, None) == sk.SK_ERR_LAYOUT
+    assert can(ctypes.byref(W(fmt=2, g=64, layout=0)), FAKE, 0, 1, FAKE, None, 0, None) == sk.SK_ERR_FORMAT
+    assert can(ctypes.byref(W(layout=0)), None, 0, 1, FAKE, None, 0, None) == sk.SK_ERR_NULL
     cq = sk.LIB.sk_gemm_w4a8_canonical_q
-    assert cq(ctypes.byref(W(layout=0)), FAKE, None, 1, FAKE, None) == sk.SK_ERR_NULL
-    assert cq(ctypes.byref(W(layout=0)), FAKE, FAKE + 2, 1, FAKE, None) == sk.SK_ERR_ALIGN
-    assert cq(ctypes.byref(W(layout=1)), FAKE, FAKE, 1, FAKE, None) == sk.SK_ERR_LAYOUT
+    assert cq(ctypes.byref(W(layout=0)), FAKE, None, 1, FAKE, None, 0, None) == sk.SK_ERR_NULL
+    assert cq(ctypes.byref(W(layout=0)), FAKE, FAKE + 2, 1, FAKE, None, 0, None) == sk.SK_ERR_ALIGN
+    assert cq(ctypes.byref(W(layout=1)), FAKE, FAKE, 1, FAKE, None, 0, None) == sk.SK_ERR_LAYOUT
 
 
 def test_failed_call_leaves_descriptor_unchanged():

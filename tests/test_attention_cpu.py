@@ -58,7 +58,8 @@ def test_key_order_in_v_tile_is_the_score_layout():
 
 
 def attn(q=FAKE, m=1, hq=32, hkv=8, kv=FAKE, cap=1024, length=100, scale=0.0883883, out=FAKE):
-    return sk.LIB.sk_decode_attention(q, m, hq, hkv, kv, cap, length, ctypes.c_float(scale), out, None)
+    return sk.LIB.sk_decode_attention(q, m, hq, hkv, kv, cap, length, ctypes.c_float(scale), out, None, 0,
+                                      None)
 
 
 def test_decode_attention_validation():

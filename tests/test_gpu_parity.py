@@ -48,9 +48,32 @@ def assert_y_close(y, ref, tol=TOL):
     assert rel.size == 0 or rel.max() <= tol, f"max normalised error {rel.max():.3e}"
 
 
+SENTINEL = 0x5A
+TAIL = 4096
+
+
+def sentinel_out(shape, dtype):
+    """A device tensor of `shape` followed by TAIL elements of sentinel bytes,
+    so a store past the end of the output shows up."""
+    n = int(np.prod(shape))
+    buf = torch.empty(n + TAIL, dtype=dtype, device="cuda")
+    buf.view(torch.uint8).fill_(SENTINEL)
+    return buf[:n].view(shape), buf[n:]
+
+
+def assert_tails_untouched(*tails):
+    for t in tails:
+        assert bool((t.view(torch.uint8) == SENTINEL).all()), "a kernel wrote past the end of its output"
+
+
 def check_call(w, buf, fmt, n, k, g, h_dev, h_ref, m):
-    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_NONE, h_dev, want_partials=(fmt != 1))
+    yo, yt = sentinel_out((m, n), torch.float32)
+    qo, qt = sentinel_out((m, k), torch.int8)
+    so, st = sentinel_out((m,), torch.float32)
+    po, pt = sentinel_out((m, n, k // g), torch.int32) if fmt != 1 else (None, None)
+    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_NONE, h_dev, want_partials=(fmt != 1), y=yo, q=qo, sx=so, p=po)
     torch.cuda.synchronize()
+    assert_tails_untouched(yt, qt, st, *([pt] if pt is not None else []))
     cb = w.codebook.cpu().numpy() if fmt == 1 else None
     ref = O.reference(fmt, buf, n, k, g, h_ref, cb)
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
@@ -143,8 +166,10 @@ def test_public_entry_points_equal_debug_run(xt):
         for m in (1, 3, 8):
             x, _ = to_dev(S.activations(12 + m, m, k), xt)
             y_dbg = sk.sk_debug_gemm(w, sk.PRO_NONE, x, want_partials=False)[0]
-            y = (sk.sk_gemm_w6a8 if fmt == 2 else sk.sk_gemm_w4a8)(w, x)
+            y, yt = sentinel_out((m, n), torch.float32)
+            (sk.sk_gemm_w6a8 if fmt == 2 else sk.sk_gemm_w4a8)(w, x, y=y)
             torch.cuda.synchronize()
+            assert_tails_untouched(yt)
             assert torch.equal(y, y_dbg), (fmt, g, m, xt)
 
 
@@ -159,6 +184,43 @@ def test_zero_and_constant_rows():
     h[3, 17] = 1e-30
     y, ref = check_call(w, buf, 0, n, k, g, torch.from_numpy(h).cuda(), h, 4)
     assert np.all(y.cpu().numpy()[1] == 0)
+
+
+def tiny_rows(k):
+    """Rows whose scale sx = absmax/127 falls below 2^-125 (the quantiser's exact-
+    division branch), down into the subnormal range, and rows of subnormal h."""
+    rng = np.random.default_rng(27)
+    base = S.activations(28, 8, k).astype(np.float64)
+    base /= np.abs(base).max(axis=1, keepdims=True)
+    amx = [127.0 * 2.0 ** -125,        # sx = 2^-125 exactly: the last normal-path scale
+           127.0 * 2.0 ** -125 * 0.75, # sx just below it
+           1e-37, 3e-39, 1e-40, 2e-44,  # sx subnormal; the last rows' h are subnormal too
+           1e-38, 1e-30]
+    h = (base * np.array(amx)[:, None]).astype(F32)
+    h[5, rng.integers(0, k, 16)] = F32(2.0 ** -149)     # smallest subnormal values
+    h[7, ::3] = F32(3e-41)                              # subnormal h in a row of normal scale
+    return h
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_tiny_scale_and_subnormal_activations_bit_exact(m, xt):
+    """Denormals are not flushed anywhere in the quantiser: q, sx and P stay
+    bit-exact for scales below 2^-125 and for subnormal activations."""
+    n, k, g = 272, 2048, 32
+    w, buf = gpu_weight(0, n, k, g, 29)
+    sk.sk_repack_w4a8(w)
+    h = tiny_rows(k)
+    rows = {1: [3], 3: [0, 1, 5], 8: list(range(8))}[m]
+    h_dev, h_ref = to_dev(np.ascontiguousarray(h[rows]), xt)
+    sx_ref = O.quantize_rows(h_ref)[1]
+    assert np.any(sx_ref < 2.0 ** -125)
+    check_call(w, buf, 0, n, k, g, h_dev, h_ref, m)
+    q, sx = sk.sk_quantize_rows(h_dev)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = O.quantize_rows(h_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
 
 
 def near_tie_rows(seed, m, k):
@@ -202,14 +264,22 @@ def test_rows_do_not_interact_and_runs_repeat():
     torch.cuda.synchronize()
     assert torch.equal(y8, y8b)                        # deterministic
     ref = O.reference(0, buf, n, k, g, x.cpu().numpy())
+    y8h = y8.cpu().numpy().astype(np.float64)
+    worst = 0.0
     for m in range(1, 8):
         # q and the integer partials of a row never depend on M; y may differ in the
-        # last bits because M selects the K-split (fp32 summation order)
+        # last bits because M selects the kernel and the K-split (fp32 summation order)
         ym, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_NONE, x[:m].contiguous())
         torch.cuda.synchronize()
         assert np.array_equal(q.cpu().numpy(), ref["q"][:m])
         assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"][:m])
         assert_y_close(ym.cpu().numpy(), {"Y": ref["Y"][:m], "mag": ref["mag"][:m]})
+        d = np.abs(ym.cpu().numpy().astype(np.float64) - y8h[:m]) / ref["mag"][:m]
+        worst = max(worst, float(d.max()))
+    # the row-for-row difference of y across M, reported, and bounded by the two
+    # calls' own bounds against the oracle
+    print(f"max |y(M=m)[i] - y(M=8)[i]| / mag over m = 1..7: {worst:.3e}")
+    assert worst <= 2 * TOL
 
 
 # ----------------------------------------------------------------------------
@@ -367,29 +437,66 @@ def test_exchange_local_fallback_is_identical(pro, reset_hooks):
 
 
 def test_back_to_back_calls_in_one_graph(reset_hooks):
-    """Repeated launches reuse the exchange slots and merge counters; replaying
-    a captured graph with new activations must still match the oracle."""
+    """Replays of one captured graph that mixes launches with and without a
+    K-split: the split ones reuse the workspace's exchange slots, arrival
+    counters and generation word on every launch, and every replay with new
+    activations must still match the oracle."""
     n, k, g = 2048, 4096, 32
     w, buf = gpu_weight(0, n, k, g, 91)
     sk.sk_repack_w4a8(w)
     x = torch.zeros((8, k), dtype=torch.float32, device="cuda")
-    ys = [torch.empty((8, n), dtype=torch.float32, device="cuda") for _ in range(3)]
+    ys = [torch.empty((8, n), dtype=torch.float32, device="cuda") for _ in range(4)]
+    ws = sk.Workspace(16 << 20)
+    splits = [1, 4, 1, 8]
+    for sp in splits:
+        sk.set_split(sp)
+        assert (sk.gemm_workspace_size(n, k, g, 0, 8) > 0) == (sp > 1)
     x.copy_(torch.from_numpy(S.activations(92, 8, k)))
-    sk.sk_gemm_w4a8(w, x, y=ys[0])            # warm: workspace allocated outside capture
-    torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        for y in ys:
-            sk.sk_gemm_w4a8(w, x, y=y)
+        for sp, y in zip(splits, ys):
+            sk.set_split(sp)                  # host-side plan choice, fixed at capture
+            sk.sk_gemm_w4a8(w, x, y=y, workspace=ws)
+    sk.set_split(0)
     for rep in range(4):
         xh = S.activations(93 + rep, 8, k)
         x.copy_(torch.from_numpy(xh))
+        # eager calls of other shapes on the same workspace between replays
+        sk.set_split(2)
+        sk.sk_gemm_w4a8(w, x[:3].contiguous(), workspace=ws)
+        sk.set_split(0)
         graph.replay()
         torch.cuda.synchronize()
         ref = O.reference(0, buf, n, k, g, xh)
         for y in ys:
             assert_y_close(y.cpu().numpy(), ref)
-        assert torch.equal(ys[0], ys[1]) and torch.equal(ys[1], ys[2])
+
+
+def test_concurrent_streams_with_own_workspaces(reset_hooks):
+    """Two streams run split-K GEMMs at the same time, each with its own
+    workspace; both results match the oracle."""
+    n, k, g = 1040, 4096, 32
+    wa, bufa = gpu_weight(0, n, k, g, 95)
+    wb, bufb = gpu_weight(0, n, k, g, 96)
+    sk.sk_repack_w4a8(wa)
+    sk.sk_repack_w4a8(wb)
+    sk.set_split(4)
+    xa_h, xb_h = S.activations(97, 8, k), S.activations(98, 5, k)
+    xa, xb = torch.from_numpy(xa_h).cuda(), torch.from_numpy(xb_h).cuda()
+    wsa, wsb = sk.Workspace(4 << 20), sk.Workspace(4 << 20)
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    ya = [torch.empty((8, n), dtype=torch.float32, device="cuda") for _ in range(6)]
+    yb = [torch.empty((5, n), dtype=torch.float32, device="cuda") for _ in range(6)]
+    for i in range(6):
+        sk.sk_gemm_w4a8(wa, xa, y=ya[i], stream=sa, workspace=wsa)
+        sk.sk_gemm_w4a8(wb, xb, y=yb[i], stream=sb, workspace=wsb)
+    torch.cuda.synchronize()
+    ra = O.reference(0, bufa, n, k, g, xa_h)
+    rb = O.reference(0, bufb, n, k, g, xb_h)
+    for i in range(6):
+        assert_y_close(ya[i].cpu().numpy(), ra)
+        assert_y_close(yb[i].cpu().numpy(), rb)
 
 
 @pytest.mark.parametrize("pro", [sk.PRO_RMSNORM, sk.PRO_SWIGLU])
