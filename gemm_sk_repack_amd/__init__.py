@@ -33,7 +33,7 @@ BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
 
 # Every symbol include/sk_repack.h and include/sk_repack_test.h declare.
 EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_workspace_size",
-           "sk_gemm_w4a8",
+           "sk_gemm_w4a8", "sk_gemm_w4a8_noalloc",
            "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu",
            "sk_gemm_experts", "sk_quantize_rows", "sk_gemm_w4a8_canonical",
            "sk_gemm_w4a8_canonical_q",
@@ -74,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "sk_unrepack_w4a8": ([W, P], I),
         "sk_gemm_workspace_size": ([I, I, I, I, I, I, ZP], I),
         "sk_gemm_w4a8": ([W, P, I, I, P, P, Z, P], I),
+        "sk_gemm_w4a8_noalloc": ([W, P, I, I, P, P], I),
         "sk_gemm_w6a8": ([W, P, I, I, P, P, Z, P], I),
         "sk_gemm_fused_rmsnorm": ([W, P, I, P, F, I, P, P, Z, P], I),
         "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P, Z, P], I),
@@ -267,6 +268,15 @@ def sk_gemm_w4a8(w: QuantWeight, x: torch.Tensor, y=None, stream=None, workspace
     wp, wb = _gemm_ws(w, m, PRO_NONE, workspace)
     _check(LIB.sk_gemm_w4a8(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), wp, wb,
                             _stream(stream)), "sk_gemm_w4a8")
+    return y
+
+
+def sk_gemm_w4a8_noalloc(w: QuantWeight, x: torch.Tensor, y=None, stream=None) -> torch.Tensor:
+    """sk_gemm_w4a8 with the library's fixed device scratch instead of a workspace."""
+    m = x.shape[0]
+    y = _out(w, m, y)
+    _check(LIB.sk_gemm_w4a8_noalloc(ctypes.byref(w.desc), _ptr(x), _xt(x), m, _ptr(y), _stream(stream)),
+           "sk_gemm_w4a8_noalloc")
     return y
 
 

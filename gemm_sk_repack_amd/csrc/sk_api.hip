@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 
 #include "../../include/sk_repack.h"
 #include "../../include/sk_repack_test.h"
@@ -64,7 +65,7 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
                    int64_t ld, int xt, const float* gamma, float eps, int m, float* y,
                    int8_t* q_out, float* sx_out, int32_t* p_out, void* ws, size_t ws_bytes,
                    void* stream, bool any_format, bool canon = false, int rows_per_expert = 0,
-                   const int32_t* experts = nullptr, int n_list = 0) {
+                   const int32_t* experts = nullptr, int n_list = 0, bool validate_only = false) {
     sk_status s = check_weight(w);
     if (s != SK_OK) return s;
     if (canon && w->format != SK_W4_SYM) return SK_ERR_FORMAT;
@@ -98,6 +99,7 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
     if (!plan.ok) return SK_ERR_UNSUPPORTED;
     const size_t need = sk::workspace_bytes(plan);
     if (need > 0 && (!ws || ws_bytes < need || !aligned256(ws))) return SK_ERR_WORKSPACE;
+    if (validate_only) return SK_OK;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (p_out) {
@@ -186,6 +188,65 @@ SK_EXPORT sk_status sk_gemm_w4a8(const sk_weight* w, const void* x, int xt, int 
                                  void* workspace, size_t workspace_bytes, void* stream) {
     return run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
                     nullptr, nullptr, workspace, workspace_bytes, stream, false);
+}
+
+namespace {
+
+// Fixed device scratch of sk_gemm_w4a8_noalloc: one array per device (each GPU
+// the library runs on holds its own copy until the process ends), used as the
+// workspace of launches that split K.  Host code uses the per-device address
+// from hipGetSymbolAddress, never the array's name.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+__global__ void clear_scratch_kernel(uint4* p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {nullptr};
+
+// The current device's scratch address; the first call on a device looks it
+// up and enqueues a clear of the whole array on `st` (a kernel, so it may be
+// captured: a captured clear runs before every replay, which is harmless).
+hipError_t noalloc_scratch(hipStream_t st, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidValue;
+        hipLaunchKernelGGL(clear_scratch_kernel, dim3(256), dim3(256), 0, st, static_cast<uint4*>(p),
+                           kNoAllocScratchBytes / 16);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+SK_EXPORT sk_status sk_gemm_w4a8_noalloc(const sk_weight* w, const void* x, int xt, int m, float* y,
+                                         void* stream) {
+    // the same checks as sk_gemm_w4a8 (validation never touches the device),
+    // with the scratch's size standing in for the workspace's: a call that
+    // would need more is SK_ERR_WORKSPACE
+    const sk_status s = run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr,
+                                 nullptr, nullptr, reinterpret_cast<void*>(static_cast<uintptr_t>(256)),
+                                 kNoAllocScratchBytes, stream, false, false, 0, nullptr, 0,
+                                 /*validate_only=*/true);
+    if (s != SK_OK) return s;
+    void* ws = nullptr;
+    if (from_hip(noalloc_scratch(static_cast<hipStream_t>(stream), &ws)) != SK_OK) return SK_ERR_HIP;
+    return run_gemm(w, false, sk::PRO_NONE, x, nullptr, 0, xt, nullptr, 0.0f, m, y, nullptr, nullptr,
+                    nullptr, ws, kNoAllocScratchBytes, stream, false);
 }
 
 SK_EXPORT sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m, float* y,

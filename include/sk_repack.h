@@ -180,6 +180,22 @@ sk_status sk_gemm_workspace_size(int n, int k, int group, int format, int m, int
 sk_status sk_gemm_w4a8(const sk_weight* w, const void* x, int xt, int m,
                        float* y, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * sk_gemm_w4a8 for callers that cannot allocate or pass device memory (code
+ * under stream capture that must not reach the allocator, tight serving
+ * loops, harnesses that forbid allocation): the same checks, kernels and
+ * results, with the workspace replaced by a fixed scratch array in the
+ * library's device memory (4 MiB per device, held by each GPU the library
+ * runs on until the process ends).  Calls that would need a larger workspace
+ * return SK_ERR_WORKSPACE.  The first call on a device also enqueues a clear
+ * of that device's scratch on `stream` (a kernel launch).  All calls of this
+ * entry point on one device share its scratch: calls that overlap in time on
+ * one GPU race and must be ordered (one stream, or events).
+ * Errors: as sk_gemm_w4a8.
+ */
+sk_status sk_gemm_w4a8_noalloc(const sk_weight* w, const void* x, int xt, int m,
+                               float* y, void* stream);
+
 /* Same for a repacked SK_W6_SYM weight [LIN] [FMT]. */
 sk_status sk_gemm_w6a8(const sk_weight* w, const void* x, int xt, int m,
                        float* y, void* workspace, size_t workspace_bytes, void* stream);
