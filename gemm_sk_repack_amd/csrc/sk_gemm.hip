@@ -92,7 +92,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
     auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
-        const size_t red = 2 * (size_t)NW * 128 * 4;
+        const size_t red = 2 * (size_t)kRedHalf * 4;
         if (cb) return 64 + (size_t)m * (2 * KS + 64) + red;      // levels, bf16 q, partials
         return (size_t)m * (KS + 32) + red;
     };
@@ -274,7 +274,6 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.trem = (int)(G.T % p.R);
     a.jn0 = (a.tq + p.TW - 1) / p.TW;
     a.jn1 = (a.tq + 1 + p.TW - 1) / p.TW;
-    a.tstep = (int64_t)p.TW * G.tile_full - (int64_t)p.spw * a.sbf;
     const int epc = (c.xt == 1) ? 8 : 4;           // activations per 16-byte chunk
     const int nch = p.ept / epc;                   // chunks per thread
     a.cpr = p.KS / epc;

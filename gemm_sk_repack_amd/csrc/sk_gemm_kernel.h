@@ -72,7 +72,9 @@ constexpr int kPipeDot4 = SK_PIPE_DOT4, kPrimeDot4 = SK_PRIME_DOT4;
 constexpr int kPipeMfma = SK_PIPE_MFMA, kPrimeMfma = SK_PRIME_MFMA;
 constexpr int pipe_of(bool dot4) { return dot4 ? kPipeDot4 : kPipeMfma; }
 constexpr int SMAX = 32;       // largest number of K-slices
-constexpr int kMaxExperts = 64;          // experts per expert-bank call
+// Tile-epilogue LDS: per half, [8 rows][16 columns][kRedPitch >= NW waves] floats.
+constexpr int kRedPitch = 20;
+constexpr int kRedHalf = 8 * 16 * kRedPitch;
 // Weight-stream buffer loads: the resource of a slot group spans kRsrcMax bytes
 // from the group's first byte (every real slot lies inside), and an offset of
 // kOutside lies past it, so such a load returns zeros without touching memory.
@@ -92,11 +94,36 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned long long u64;
 struct KArgs {
+    // Read at kernel entry, before the first loads: one contiguous block, so
+    // every wave fetches it with a few wide scalar loads in one round trip.
     const uint8_t* data;
-    const float* codebook;  // 16 levels (codebook format only)
     const void* x;
-    const void* x2;
     int64_t ld;
+    // stream-layout addressing: full tiles (16 rows) and the ragged last tile
+    int64_t tile_full;      // bytes per full tile
+    int64_t rag_w, rag_s;   // byte offsets of the ragged tile's weights and scales
+    int m, KS, S, KBs;
+    // tiles of block r: [r * tq + min(r, trem), ... + tq + (r < trem)); jn1 / jn0
+    // = tiles per tile group, rounded up, for the two block sizes
+    int tq, trem, jn0, jn1;
+    int TW, spw, KB;
+    int sbf, swo;           // bytes per super-block of a full tile; offset of its scales
+    int t_rag;              // index of the ragged tile, -1 if N % 16 == 0
+    int nr_last;            // rows of the ragged tile (16 if none)
+    int rag_sbw, rag_sbs;   // its weight and scale bytes per super-block
+    int cpr, tpr;           // activation chunks per row of the slice; threads per row
+    // expert banks: logical tile t is tile t % tpe of expert experts[t / tpe]
+    // (a device array) in the bank of n_experts experts (tpe = tiles per
+    // expert; 0 for a plain weight)
+    int tpe;
+    // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
+    // wave index within the row (14-18) and activation chunk steps (19-22)
+    uint32_t wtab[NW];
+    // used later in the launch
+    int n_experts;
+    const int32_t* experts;
+    const float* codebook;  // 16 levels (codebook format only)
+    const void* x2;
     const float* gamma;
     float eps;
     float* y;
@@ -105,31 +132,10 @@ struct KArgs {
     int32_t* p_out;
     WsHeader* ws;           // caller-owned workspace (S > 1 only)
     u64* part;              // its tagged split-K partials
-    int n, k, m;
-    int T, KB, kg;
-    int S, R, P, TW, KW, spw, KBs, KS, WPR, ks;
+    int n, k;
+    int T, kg;
+    int R, P, KW, WPR, ks;
     int spin_limit;
-    // tiles of block r: [r * tq + min(r, trem), ... + tq + (r < trem)); jn1 / jn0
-    // = tiles per tile group, rounded up, for the two block sizes
-    int tq, trem, jn0, jn1;
-    // stream-layout addressing: full tiles (16 rows) and the ragged last tile
-    int64_t tile_full;      // bytes per full tile
-    int64_t tstep;          // TW * tile_full - spw * sbf: from a tile's last slot to the next tile
-    int sbf, swo;           // bytes per super-block of a full tile; offset of its scales
-    int cpr, tpr;           // activation chunks per row of the slice; threads per row
-    int t_rag;              // index of the ragged tile, -1 if N % 16 == 0
-    int nr_last;            // rows of the ragged tile (16 if none)
-    int64_t rag_w, rag_s;   // byte offsets of the ragged tile's weights and scales
-    int rag_sbw, rag_sbs;   // their bytes per super-block
-    // per wave: tile group (bits 0-4), k-part (5-9), activation row (10-13),
-    // wave index within the row (14-18) and activation chunk steps (19-22)
-    uint32_t wtab[NW];
-    // expert banks: logical tile t is tile t % tpe of expert experts[t / tpe]
-    // (a device array) in the bank of n_experts experts (tpe = tiles per
-    // expert; 0 for a plain weight)
-    int tpe;
-    int n_experts;
-    const int32_t* experts;
 };
 
 struct Smem {
@@ -327,23 +333,31 @@ __device__ inline int chunk_of(const Act<XT, EPT>& am, int i) {
 }
 
 // Raw 16-byte chunks of slice [k_lo, k_lo + KS) (SwiGLU: gate in xr, up in ur).
+// The loads go through a buffer resource spanning the row's slice: a chunk past
+// its end reads zeros, and the chunks of steps i >= nw are not loaded (zero),
+// so every invalid element is 0 without a select.
 template <int PRO, int XT, int EPT>
 __device__ inline void load_act(const KArgs& a, const Act<XT, EPT>& am, int k_lo,
                                 uint4 xr[Act<XT, EPT>::NCH], uint4 ur[Act<XT, EPT>::NCH]) {
     constexpr int CB = Act<XT, EPT>::E * Act<XT, EPT>::ES;     // 16 bytes per chunk
     // the row's slice start (wave-uniform) and this thread's byte offsets in it
     const int64_t row = ((int64_t)am.m * a.ld + k_lo) * Act<XT, EPT>::ES;
-    const uint8_t* xb = static_cast<const uint8_t*>(a.x) + row;
-    const uint8_t* ub = static_cast<const uint8_t*>(a.x2) + row;
+    const int nrec = am.cpr * CB;
+    const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(static_cast<const uint8_t*>(a.x)) + row, (short)0, nrec, kRsrcFlags);
+    __amdgpu_buffer_rsrc_t us = xs;
+    if (PRO == PRO_SWIGLU)
+        us = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(static_cast<const uint8_t*>(a.x2)) + row,
+                                               (short)0, nrec, kRsrcFlags);
 #pragma unroll
     for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
         xr[i] = make_uint4(0u, 0u, 0u, 0u);
         ur[i] = make_uint4(0u, 0u, 0u, 0u);
         if (i < am.nw) {
-            const int c = chunk_of(am, i);
-            const int off = c < am.cpr ? c * CB : 0;
-            xr[i] = *reinterpret_cast<const uint4*>(xb + off);
-            if (PRO == PRO_SWIGLU) ur[i] = *reinterpret_cast<const uint4*>(ub + off);
+            const int off = chunk_of(am, i) * CB;
+            xr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(xs, off, 0, 0));
+            if (PRO == PRO_SWIGLU)
+                ur[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(us, off, 0, 0));
         }
     }
 }
@@ -377,7 +391,6 @@ __device__ inline void finish_act(const Act<XT, EPT>& am, const uint4 xr[Act<XT,
     constexpr int E = Act<XT, EPT>::E;
 #pragma unroll
     for (int i = 0; i < Act<XT, EPT>::NCH; ++i) {
-        const bool ok = i < am.nw && chunk_of(am, i) < am.cpr;
         const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
         const uint32_t uw[4] = {ur[i].x, ur[i].y, ur[i].z, ur[i].w};
 #pragma unroll
@@ -390,8 +403,8 @@ __device__ inline void finish_act(const Act<XT, EPT>& am, const uint4 xr[Act<XT,
                 xv = __uint_as_float((e & 1) ? (xw[e >> 1] & 0xFFFF0000u) : (xw[e >> 1] << 16));
                 uv = __uint_as_float((e & 1) ? (uw[e >> 1] & 0xFFFF0000u) : (uw[e >> 1] << 16));
             }
-            const float v = (PRO == PRO_SWIGLU) ? silu_mul(xv, uv) : xv;
-            h[i * E + e] = ok ? v : 0.0f;
+            // invalid elements load as 0, and every prologue maps 0 to 0
+            h[i * E + e] = (PRO == PRO_SWIGLU) ? silu_mul(xv, uv) : xv;
         }
     }
 }
@@ -403,12 +416,29 @@ __device__ inline double sum_sq(const float h[Act<XT, EPT>::NCH * Act<XT, EPT>::
     for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) ss += (double)h[j] * (double)h[j];
     return ss;
 }
+// max |h| as an integer maximum of the magnitude bits (equal to the float
+// maximum for finite values, and cheaper: no NaN handling).
 template <int XT, int EPT>
 __device__ inline float abs_max(const float h[Act<XT, EPT>::NCH * Act<XT, EPT>::E]) {
-    float mx = 0.0f;
+    uint32_t mx = 0u;
 #pragma unroll
-    for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) mx = fmaxf(mx, fabsf(h[j]));
-    return mx;
+    for (int j = 0; j < Act<XT, EPT>::NCH * Act<XT, EPT>::E; ++j) mx = max(mx, __float_as_uint(h[j]) & 0x7FFFFFFFu);
+    return __uint_as_float(mx);
+}
+// The same for bf16 activations taken as they are, on the packed words: a
+// packed 16-bit maximum of the magnitude bits, two elements per operation.
+template <int EPT>
+__device__ inline float abs_max_bf16(const uint4 xr[Act<1, EPT>::NCH]) {
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mx = {0, 0};
+#pragma unroll
+    for (int i = 0; i < Act<1, EPT>::NCH; ++i) {
+        const uint32_t w[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) mx = __builtin_elementwise_max(mx, __builtin_bit_cast(us2, w[d] & 0x7FFF7FFFu));
+    }
+    const uint32_t top = max((uint32_t)mx.x, (uint32_t)mx.y);
+    return __uint_as_float(top << 16);
 }
 
 // A row's slice statistic from its waves' values, in wave order.
@@ -570,9 +600,17 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
 
 // y of output row omm in tile ot from its scaled sum: sx * sum, or NaN for a
 // tile of an expert-bank call whose listed id lies outside the bank.
+// Entry i of the expert list (i wave-uniform), by a scalar load: the list is
+// read-only during the launch, and a vector load's wait would also wait for
+// every activation and weight load the wave has in flight.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ inline int expert_id(const KArgs& a, int i) {
+    return ((const_i32*)(a.experts))[__builtin_amdgcn_readfirstlane(i)];
+}
+
 __device__ inline float out_value(const KArgs& a, const Smem& sm, int ot, int omm, float sum) {
     if (a.tpe) {
-        const int e = a.experts[ot / a.tpe];
+        const int e = expert_id(a, ot / a.tpe);
         if (e < 0 || e >= a.n_experts) return __builtin_nanf("");
     }
     return sm.sx[omm] * sum;
@@ -609,6 +647,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    // The entry block of the arguments, all requested before anything waits on
+    // one of them (otherwise the first loads would wait for a chain of
+    // dependent argument fetches).
+    __asm__ volatile("" ::"s"(a.data), "s"(a.x), "s"(a.ld), "s"(a.tile_full), "s"(a.rag_w), "s"(a.rag_s),
+                     "s"(a.m), "s"(a.KS), "s"(a.S), "s"(a.KBs), "s"(a.tq), "s"(a.trem), "s"(a.jn0),
+                     "s"(a.jn1), "s"(a.TW), "s"(a.spw), "s"(a.KB), "s"(a.sbf), "s"(a.swo), "s"(a.t_rag),
+                     "s"(a.nr_last), "s"(a.rag_sbw), "s"(a.rag_sbs), "s"(a.cpr), "s"(a.tpr), "s"(a.tpe),
+                     "s"(a.wtab[wv]));
     const int nl = lane & 15;
     const int hl = lane >> 4;
     const int M = a.m;
@@ -620,6 +666,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    statistics -> q -> every dot product), so their loads go out before
     //    any other address arithmetic; then the call's tag and the weight stream
     //    (a wave's loads complete in issue order)
+    // The launch generation first: loads complete in issue order, so waiting
+    // for it later never waits for the activations or weights issued after
+    // it.  The load is unconditional (a conditional one would be waited for
+    // where the two paths join); a launch that does not split K has no
+    // workspace and reads a word of the activations instead, unused.
+    const uint32_t* gen_p = (!ONE && a.S > 1) ? &a.ws->gen : static_cast<const uint32_t*>(a.x);
+    const uint32_t gen = __hip_atomic_load(gen_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t wt = a.wtab[wv];
     const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
     uint4 xr[NCH], ur[NCH];
@@ -646,8 +699,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
         if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
     }
-    // the launch generation (only launches that split K touch the workspace)
-    const uint32_t gen = (!ONE && a.S > 1) ? __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
 
     // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
     // wave wv works on tile group tg (every TW-th tile) and super-blocks
@@ -735,7 +786,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const int tv = valid ? t : 0;
             int tb = t;
             if (a.tpe) {
-                const int e = a.experts[tv / a.tpe];
+                const int e = expert_id(a, tv / a.tpe);
                 tb = ((e >= 0 && e < a.n_experts) ? e : 0) * a.tpe + tv % a.tpe;
             }
             const int64_t wo = (int64_t)tb * a.tile_full + (int64_t)kb * a.sbf;
@@ -847,6 +898,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
         if (tid < M) sm.sx[tid] = static_cast<const float*>(a.x2)[tid];
     } else {
+        // bf16 activations taken as they are: their maximum from the packed
+        // words, before they are widened (the raw words are dead after that)
+        float mx_packed = 0.0f;
+        if constexpr (PRO == PRO_NONE && XT == 1) mx_packed = abs_max_bf16<EPT>(xr);
         float h[NCH * E];
         finish_act<PRO, XT, EPT>(am, xr, ur, h);
         const int mrow = am.m < M ? am.m : 0;
@@ -876,7 +931,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
         float amx;
         {
-            const float mx = wave_max(abs_max<XT, EPT>(h));
+            const float mx = wave_max((PRO == PRO_NONE && XT == 1) ? mx_packed : abs_max<XT, EPT>(h));
             if (lane == 0) sm.wf[wv] = mx;
             __syncthreads();
             if (ONE || a.S == 1) {
@@ -907,8 +962,19 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 #pragma unroll
             for (int j = 0; j < NCH * E; ++j) b[j] = code_bits(h[j], inv_lo, inv_hi, split);
             if (__builtin_expect((split != 0 || sx < kTinySx) && sx > 0.0f, 0)) {
+                // The exact quotient for the elements whose two products round
+                // apart (all of them for a tiny sx).  Every launch has some
+                // workgroup on this path, so it must be short; the opaque copy of
+                // inv_hi keeps each element's product in its own step (computed
+                // all at once, the products would need a register each).
+                const bool tiny = sx < kTinySx;
 #pragma unroll
-                for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+                for (int j = 0; j < NCH * E; ++j) {
+                    float ih = inv_hi;
+                    __asm__ volatile("" : "+v"(ih));
+                    const uint32_t hb = __float_as_uint(__builtin_fmaf(h[j], ih, kRoundMagic));
+                    if (tiny || hb != b[j]) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+                }
             }
             uint32_t pk[NCH * E / 4];
 #pragma unroll
@@ -1138,19 +1204,22 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    of the waves' partials.  The partials buffer alternates between two
     //    halves, so one barrier per tile is enough (a wave cannot reuse a half
     //    before every thread passed the next barrier).
+    // The partials are stored output-major, [row][column][wave] with a pitch of
+    // kRedPitch floats, so one thread reads all the waves' values of its output
+    // with four 16-byte LDS reads (the 16 lanes of a row write to distinct banks).
     auto tile_epilogue = [&](const float* v4, const int j) {
-        float* red = red_l + (j & 1) * (NW * 128);
+        float* red = red_l + (j & 1) * kRedHalf;
         if (DOT4) {
             // the four k-quarters of a row sit 16 lanes apart
             float v = v4[0];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
-            if (lane < 16) red[wv * 16 + nl] = v;
+            if (lane < 16) red[nl * kRedPitch + wv] = v;
         } else {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int mm = 4 * hl + rr;
-                if (mm < M) red[(wv * 8 + mm) * 16 + nl] = v4[rr];
+                if (mm < M) red[(mm * 16 + nl) * kRedPitch + wv] = v4[rr];
             }
         }
         __syncthreads();
@@ -1161,12 +1230,23 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const int onn = tid & 15;
             const int ot = t_begin + ogrp + j * a.TW;
             if (ot < t_end) {
-                float osum = 0.0f;
+                // the KW k-parts of tile group ogrp are waves w0 .. w0 + KW - 1,
+                // added in wave order
                 const int w0 = ogrp * a.KW;
-                if (DOT4) {
-                    for (int w = w0; w < w0 + a.KW; ++w) osum += red[w * 16 + onn];
-                } else {
-                    for (int w = w0; w < w0 + a.KW; ++w) osum += red[(w * 8 + omm) * 16 + onn];
+                const float4* rp = reinterpret_cast<const float4*>(red + (omm * 16 + onn) * kRedPitch);
+                float osum = 0.0f;
+                // all four reads first: one LDS round trip
+                float4 t4[NW / 4];
+#pragma unroll
+                for (int q4 = 0; q4 < NW / 4; ++q4) t4[q4] = rp[q4];
+#pragma unroll
+                for (int q4 = 0; q4 < NW / 4; ++q4) {
+                    const float wv4[4] = {t4[q4].x, t4[q4].y, t4[q4].z, t4[q4].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int w = 4 * q4 + e;
+                        osum = (w >= w0 && w < w0 + a.KW) ? osum + wv4[e] : osum;
+                    }
                 }
                 if (ONE || a.S == 1) {
                     if (ot * TILE_ROWS + onn < a.n)
