@@ -543,6 +543,13 @@ __device__ inline void slice_stat(const KArgs& a, Smem& sm, uint32_t wt, int lan
     __syncthreads();
 }
 
+// How long the chiplet-local exchange words are polled before the
+// device-scope ones, in ticks of the 100 MHz constant clock.
+#ifndef SK_XCD_POLL_TICKS
+#define SK_XCD_POLL_TICKS 200
+#endif
+constexpr uint64_t kXcdPollTicks = SK_XCD_POLL_TICKS;
+
 // Exchange this slice's per-row value with the other slices (S > 1), run by
 // the poller wave only, after the waves' values are in sm.wd / sm.wf.  Every
 // word carries the call's tag in its high half, so no fence is needed: a
@@ -564,8 +571,12 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
         } else {
             const float v = combine_f(a, sm, lane);
             sm.exf[lane * SMAX + s] = v;
-            __hip_atomic_store(&a.ws->amax[slot], ((u64)tag << 32) | __float_as_uint(v),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const u64 w = ((u64)tag << 32) | __float_as_uint(v);
+            // the chiplet-local copy first: a store reaches this XCD's L2
+            // (sc0: written through the CU's L1), where the other slices of
+            // the range read it when they run on the same XCD
+            __asm__ volatile("global_store_dwordx2 %0, %1, off sc0" ::"v"(&a.ws->amax_xcd[slot]), "v"(w) : "memory");
+            __hip_atomic_store(&a.ws->amax[slot], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     if (lane < SMAX) sm.miss[lane] = 0;
@@ -574,7 +585,27 @@ __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, 
         const int slot = sl * 8 + mm;
         if (sl == s) continue;
         bool ok = false;
-        for (int it = 0; it < a.spin_limit; ++it) {
+        if (!is_ss) {
+            // The slices of a range are workgroups r, r + R, r + 2R, ...; with R
+            // a multiple of the 8 chiplets and round-robin dispatch they share
+            // an XCD, so the value shows up in this L2 within a few hundred ns.
+            // Only a short bounded poll: when the slices sit on other XCDs it
+            // never shows, and the device-scope words below serve.
+            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+            for (int it = 0; (a.R & 7) == 0 && it < a.spin_limit; ++it) {
+                u64 v;
+                __asm__ volatile("global_load_dwordx2 %0, %1, off sc0\n\ts_waitcnt vmcnt(0)"
+                                 : "=v"(v) : "v"(&a.ws->amax_xcd[slot]) : "memory");
+                if ((uint32_t)(v >> 32) == tag) {
+                    sm.exf[mm * SMAX + sl] = __uint_as_float((uint32_t)v);
+                    ok = true;
+                    break;
+                }
+                if (__builtin_amdgcn_s_memrealtime() - t0 > kXcdPollTicks) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        for (int it = 0; !ok && it < a.spin_limit; ++it) {
             if (is_ss) {
                 const u64 hi = __hip_atomic_load(&a.ws->ssh[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 const u64 lo = __hip_atomic_load(&a.ws->ssl[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1290,21 +1321,40 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
         __syncthreads();
         if (sm.last) {
+            // The partials' first reads go out together and through this XCD's
+            // L2 (sc0: past the CU's L1), where the slices of the range wrote
+            // them when they share the XCD; a word whose tag is not there yet
+            // (or that sits in another XCD's L2) is then read at device scope.
+            const __amdgpu_buffer_rsrc_t prs =
+                __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, kRsrcMax, kRsrcFlags);
+            constexpr int kSc0 = 1;
             for (int e = tid; e < ntile * M * 16; e += NT) {
                 const int ci = e / (M * 16);
                 const int omm = (e / 16) % M;
                 const int onn = e & 15;
                 const int ot = t_begin + ci;
                 float tot = 0.0f;
-                for (int sl = 0; sl < a.S; ++sl) {
-                    // Every partial was stored before its workgroup counted itself, so its
-                    // tag shows up shortly; the bound only guards against a hang (a missing
-                    // partial would turn y into NaN rather than stall the GPU).
-                    const u64* p = &a.part[(((int64_t)ot * a.S + sl) * M + omm) * 16 + onn];
-                    u64 v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    for (int it = 0; (uint32_t)(v >> 32) != sm.tag && it < (1 << 24); ++it)
-                        v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    tot += ((uint32_t)(v >> 32) == sm.tag) ? __uint_as_float((uint32_t)v) : __builtin_nanf("");
+                for (int sl0 = 0; sl0 < a.S; sl0 += 4) {
+                    u64 v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int sl = min(sl0 + u, a.S - 1);
+                        const int off = (int)(((((int64_t)ot * a.S + sl) * M + omm) * 16 + onn) * 8);
+                        v[u] = __builtin_bit_cast(u64, __builtin_amdgcn_raw_buffer_load_b64(prs, off, 0, kSc0));
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int sl = sl0 + u;
+                        if (sl >= a.S) break;
+                        // Every partial was stored before its workgroup counted itself, so
+                        // its tag shows up shortly; the bound only guards against a hang (a
+                        // missing partial would turn y into NaN rather than stall the GPU).
+                        const u64* p = &a.part[(((int64_t)ot * a.S + sl) * M + omm) * 16 + onn];
+                        u64 w = v[u];
+                        for (int it = 0; (uint32_t)(w >> 32) != sm.tag && it < (1 << 24); ++it)
+                            w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        tot += ((uint32_t)(w >> 32) == sm.tag) ? __uint_as_float((uint32_t)w) : __builtin_nanf("");
+                    }
                 }
                 if (ot * TILE_ROWS + onn < a.n)
                     a.y[(int64_t)omm * a.n + (int64_t)ot * TILE_ROWS + onn] = out_value(a, sm, ot, omm, tot * KINV);

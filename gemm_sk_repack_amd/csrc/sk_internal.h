@@ -66,6 +66,9 @@ struct WsHeader {
     unsigned long long amax[32 * 8];   // (tag << 32) | float bits, [slice][row]
     unsigned long long ssh[32 * 8];    // (tag << 32) | high half of the double sum of squares
     unsigned long long ssl[32 * 8];    // (tag << 32) | low half
+    // the absmax words again, written and read through the L2 of the writer's
+    // chiplet (XCD) only: the fast path between slices that share an XCD
+    unsigned long long amax_xcd[32 * 8];
 };
 // Bytes reserved for the header; the tagged split-K partials follow it.
 constexpr size_t kWsHeaderBytes = 16384;
