@@ -692,7 +692,34 @@ def time_variants(torch, sk, S, dev, stream):
         record("small", "1024x1024", 1024, 1024, 32, 0, m, us, nb)
     del cps
 
-    # fused prologues at hidden 4096
+    # fused prologues at hidden 4096, beside the same calls split into launches:
+    # (a) the prologue launch writing h, then the GEMM quantising in its launch;
+    # (b) the prologue launch, the quantisation launch, then the GEMM on the
+    #     weight in the canonical layout
+    def split_times(cps, n, k, m, prologue):
+        can = [sk.QuantWeight(c.data.clone(), n, k, 32, sk.SK_W4_SYM) for c in cps]
+        for c in can:                                     # canonical bytes of the same weight
+            c.desc.layout = sk.SK_LAYOUT_STREAM
+            sk.sk_unrepack_w4a8(c)
+        h = torch.empty((m, k), dtype=torch.float32, device=dev)
+        q = torch.empty((m, k), dtype=torch.int8, device=dev)
+        sx = torch.empty((m,), dtype=torch.float32, device=dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        R = len(cps)
+
+        def a(i):
+            prologue(h)
+            sk.sk_gemm_w4a8(cps[i % R], h, y=y)
+
+        def b(i):
+            prologue(h)
+            sk.sk_quantize_rows(h, q=q, sx=sx)
+            sk.sk_gemm_w4a8_canonical_q(can[i % R], q, sx, y=y)
+        us_a = time_graph(torch, stream, a, 4 * R)
+        us_b = time_graph(torch, stream, b, 4 * R)
+        del can
+        return us_a, us_b
+
     cps, nb = weight_copies(sk.SK_W4_SYM, 6144, 4096, 32, 3, 0)
     gam = torch.from_numpy(S.gamma(S.seed_of(3, 0, S.TENSOR_GAMMA), 4096)).to(dev)
     for m in (1, 3, 8):
@@ -701,6 +728,11 @@ def time_variants(torch, sk, S, dev, stream):
         us = time_graph(torch, stream, lambda i: sk.sk_gemm_fused_rmsnorm(
             cps[i % len(cps)], x, gam, 1e-6, y=y), 4 * len(cps))
         record("fused", "rmsnorm+qkv", 6144, 4096, 32, 0, m, us, nb, extra=4096 * 4)
+        us_a, us_b = split_times(cps, 6144, 4096, m, lambda h: sk.sk_prologue_rmsnorm(x, gam, 1e-6, h=h))
+        rows[-1].update({"split_prologue_us": round(us_a, 3), "split_prologue_quant_canonical_us": round(us_b, 3)})
+        log(f"{'':10s} {'':12s} split: prologue launch + GEMM {us_a:8.3f} us; "
+            f"+ quantisation launch + canonical GEMM {us_b:8.3f} us")
+    del cps
     cps, nb = weight_copies(sk.SK_W4_SYM, 4096, 12288, 32, 3, 1)
     for m in (1, 3, 8):
         gu = torch.from_numpy(np.concatenate(
@@ -710,6 +742,11 @@ def time_variants(torch, sk, S, dev, stream):
         us = time_graph(torch, stream, lambda i: sk.sk_gemm_fused_swiglu(
             cps[i % len(cps)], gu[:, :12288], gu[:, 12288:], y=y), 4 * len(cps))
         record("fused", "swiglu+down", 4096, 12288, 32, 0, m, us, nb, extra=m * 12288 * 4)
+        us_a, us_b = split_times(cps, 4096, 12288, m,
+                                 lambda h: sk.sk_prologue_swiglu(gu[:, :12288], gu[:, 12288:], h=h))
+        rows[-1].update({"split_prologue_us": round(us_a, 3), "split_prologue_quant_canonical_us": round(us_b, 3)})
+        log(f"{'':10s} {'':12s} split: prologue launch + GEMM {us_a:8.3f} us; "
+            f"+ quantisation launch + canonical GEMM {us_b:8.3f} us")
     del cps
     # formats at K = 4096
     for li, (name, fmt, n, g) in enumerate([("w6_g64", sk.SK_W6_SYM, 12288, 64),

@@ -35,7 +35,8 @@ BITS = {SK_W4_SYM: 4, SK_W4_CODEBOOK: 4, SK_W6_SYM: 6}
 EXPORTS = ["sk_status_string", "sk_repack_w4a8", "sk_unrepack_w4a8", "sk_gemm_workspace_size",
            "sk_gemm_w4a8", "sk_gemm_w4a8_noalloc",
            "sk_gemm_w6a8", "sk_gemm_fused_rmsnorm", "sk_gemm_fused_swiglu",
-           "sk_gemm_experts", "sk_quantize_rows", "sk_gemm_w4a8_canonical",
+           "sk_gemm_experts", "sk_quantize_rows", "sk_prologue_rmsnorm", "sk_prologue_swiglu",
+           "sk_gemm_w4a8_canonical",
            "sk_gemm_w4a8_canonical_q",
            "sk_debug_gemm",
            "sk_test_repack_on_host", "sk_test_gemm_plan", "sk_test_set_split",
@@ -80,6 +81,8 @@ def _load() -> ctypes.CDLL:
         "sk_gemm_fused_swiglu": ([W, P, P, I64, I, I, P, P, Z, P], I),
         "sk_gemm_experts": ([W, I, P, I, P, I, I, P, P, Z, P], I),
         "sk_quantize_rows": ([P, I, I, I, P, P, P], I),
+        "sk_prologue_rmsnorm": ([P, I, P, F, I, I, P, P], I),
+        "sk_prologue_swiglu": ([P, P, I64, I, I, I, P, P], I),
         "sk_gemm_w4a8_canonical": ([W, P, I, I, P, P, Z, P], I),
         "sk_gemm_w4a8_canonical_q": ([W, P, P, I, P, P, Z, P], I),
         "sk_debug_gemm": ([W, I, P, P, I64, I, P, F, I, P, P, P, P, P, Z, P], I),
@@ -316,6 +319,29 @@ def sk_quantize_rows(x: torch.Tensor, q=None, sx=None, stream=None):
     _check(LIB.sk_quantize_rows(_ptr(x), _xt(x), m, k, _ptr(q), _ptr(sx), _stream(stream)),
            "sk_quantize_rows")
     return q, sx
+
+
+def sk_prologue_rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float, h=None, stream=None) -> torch.Tensor:
+    """h = RMSNorm(x) written to memory as float32 (the split path's prologue launch)."""
+    m, k = x.shape
+    if h is None:
+        h = torch.empty((m, k), dtype=torch.float32, device=x.device)
+    _check(LIB.sk_prologue_rmsnorm(_ptr(x), _xt(x), _ptr(gamma), eps, m, k, _ptr(h), _stream(stream)),
+           "sk_prologue_rmsnorm")
+    return h
+
+
+def sk_prologue_swiglu(gate: torch.Tensor, up: torch.Tensor, h=None, stream=None) -> torch.Tensor:
+    """h = SwiGLU(gate, up) written to memory as float32; gate and up are [M, K]
+    views sharing a row stride (the split path's prologue launch)."""
+    m, k = gate.shape
+    if up.shape != gate.shape or gate.stride() != up.stride() or gate.stride(1) != 1:
+        raise ValueError("gate and up must be row-major [M, K] views with the same row stride")
+    if h is None:
+        h = torch.empty((m, k), dtype=torch.float32, device=gate.device)
+    _check(LIB.sk_prologue_swiglu(_ptr(gate), _ptr(up), gate.stride(0), _xt(gate), m, k, _ptr(h),
+                                  _stream(stream)), "sk_prologue_swiglu")
+    return h
 
 
 def sk_gemm_w4a8_canonical(w: QuantWeight, x: torch.Tensor, y=None, stream=None,

@@ -304,6 +304,27 @@ SK_EXPORT sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t
     return from_hip(sk::launch_quantize(x, xt, m, k, q, sx, static_cast<hipStream_t>(stream)));
 }
 
+SK_EXPORT sk_status sk_prologue_rmsnorm(const void* x, int xt, const float* gamma, float eps, int m, int k,
+                                        float* h, void* stream) {
+    if (!x || !gamma || !h) return SK_ERR_NULL;
+    if (xt != SK_F32 && xt != SK_BF16) return SK_ERR_FORMAT;
+    if (m < 1 || m > 8 || k < 16 || k % 16 != 0) return SK_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(gamma) || !aligned16(h)) return SK_ERR_ALIGN;
+    return from_hip(sk::launch_prologue(sk::PRO_RMSNORM, x, nullptr, k, xt, gamma, eps, m, k, h,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+SK_EXPORT sk_status sk_prologue_swiglu(const void* gate, const void* up, int64_t ld, int xt, int m, int k,
+                                       float* h, void* stream) {
+    if (!gate || !up || !h) return SK_ERR_NULL;
+    if (xt != SK_F32 && xt != SK_BF16) return SK_ERR_FORMAT;
+    if (m < 1 || m > 8 || k < 16 || k % 16 != 0 || ld < k) return SK_ERR_SHAPE;
+    const int esize = (xt == SK_BF16) ? 2 : 4;
+    if ((ld * esize) % 16 != 0 || !aligned16(gate) || !aligned16(up) || !aligned16(h)) return SK_ERR_ALIGN;
+    return from_hip(sk::launch_prologue(sk::PRO_SWIGLU, gate, up, ld, xt, nullptr, 0.0f, m, k, h,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 SK_EXPORT sk_status sk_gemm_w4a8_canonical(const sk_weight* w, const void* x, int xt, int m,
                                            float* y, void* workspace, size_t workspace_bytes,
                                            void* stream) {

@@ -106,7 +106,10 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
         // do, the cheapest by a cost fitted to measured launch times: 4 per
         // weight slot of a wave, 1/2048 per activation a workgroup quantises
         // (M * KS) and 1/16 per (tile, slice, row) partial a workgroup's merges
-        // read (tiles per workgroup * S * M); ties: fewer slices.
+        // read (tiles per workgroup * S * M), plus 24 slots when the slices of
+        // a range cannot share an XCD (R not a multiple of 8: their exchange
+        // then takes device-scope round trips, about 3 us more per launch);
+        // ties: fewer slices.
         int64_t best = -1;
         for (int s = 2; s <= SMAX; ++s) {
             if (!valid(s)) continue;
@@ -115,7 +118,8 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
             int kw, tw;
             const int64_t slots = split_waves(KB / s, (int)tpw, m, NW - 1, pipe, kw, tw);
             // in units of 1/2048
-            const int64_t cost = 8192 * slots + (int64_t)m * (G.k / s) + 128 * tpw * s * m;
+            const int64_t cost = 8192 * slots + (int64_t)m * (G.k / s) + 128 * tpw * s * m +
+                                 ((R & 7) ? 8192 * 24 : 0);
             if (best < 0 || cost < best) {
                 best = cost;
                 S = s;

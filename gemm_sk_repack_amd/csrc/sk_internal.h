@@ -106,5 +106,7 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st);
 // launch (the split path); the same arithmetic as inside the GEMM.
 hipError_t launch_quantize(const void* x, int xt, int m, int64_t k, int8_t* q, float* sx,
                            hipStream_t st);
+hipError_t launch_prologue(int pro, const void* x, const void* x2, int64_t ld, int xt, const float* gamma,
+                           float eps, int m, int64_t k, float* h, hipStream_t st);
 
 }  // namespace sk

@@ -276,6 +276,24 @@ sk_status sk_quantize_rows(const void* x, int xt, int m, int k, int8_t* q, float
                            void* stream);
 
 /*
+ * The prologues as launches of their own, for the split path: h (device
+ * [M][K] float32, rows K apart, 16-byte aligned) is written to memory with
+ * the fused entry points' arithmetic, so sk_gemm_w4a8(w, h) or
+ * sk_quantize_rows(h) then sees the h the fused call keeps on chip [LIN].
+ *   sk_prologue_rmsnorm: h = RMSNorm(x) exactly as sk_gemm_fused_rmsnorm;
+ *     x [M][K] of dtype xt, gamma [K] float32, both 16-byte aligned.
+ *   sk_prologue_swiglu: h = SwiGLU(gate, up) exactly as sk_gemm_fused_swiglu;
+ *     gate, up rows of K elements with row stride `ld` elements (ld >= K,
+ *     ld * element size a multiple of 16 bytes), dtype xt, 16-byte aligned.
+ *   m 1..8, K a positive multiple of 16.
+ * Errors: NULL, SHAPE, ALIGN, FORMAT (dtype), HIP.
+ */
+sk_status sk_prologue_rmsnorm(const void* x, int xt, const float* gamma, float eps, int m, int k,
+                              float* h, void* stream);
+sk_status sk_prologue_swiglu(const void* gate, const void* up, int64_t ld, int xt, int m, int k,
+                             float* h, void* stream);
+
+/*
  * sk_gemm_w4a8 on a weight left in the canonical layout
  * (w->layout == SK_LAYOUT_CANONICAL, no repack): the workgroups read each
  * tile's codes and its scales from the two regions.  SK_W4_SYM only; the

@@ -183,6 +183,29 @@ def test_split_path_validation():
     assert cq(ctypes.byref(W(layout=1)), FAKE, FAKE, 1, FAKE, None, 0, None) == sk.SK_ERR_LAYOUT
 
 
+def test_prologue_launch_validation():
+    r = sk.LIB.sk_prologue_rmsnorm
+    assert r(None, 0, FAKE, 1e-6, 1, 256, FAKE, None) == sk.SK_ERR_NULL
+    assert r(FAKE, 0, None, 1e-6, 1, 256, FAKE, None) == sk.SK_ERR_NULL
+    assert r(FAKE, 0, FAKE, 1e-6, 1, 256, None, None) == sk.SK_ERR_NULL
+    assert r(FAKE, 7, FAKE, 1e-6, 1, 256, FAKE, None) == sk.SK_ERR_FORMAT
+    assert r(FAKE, 0, FAKE, 1e-6, 0, 256, FAKE, None) == sk.SK_ERR_SHAPE
+    assert r(FAKE, 0, FAKE, 1e-6, 9, 256, FAKE, None) == sk.SK_ERR_SHAPE
+    assert r(FAKE, 0, FAKE, 1e-6, 1, 24, FAKE, None) == sk.SK_ERR_SHAPE
+    assert r(FAKE + 4, 0, FAKE, 1e-6, 1, 256, FAKE, None) == sk.SK_ERR_ALIGN
+    assert r(FAKE, 0, FAKE + 8, 1e-6, 1, 256, FAKE, None) == sk.SK_ERR_ALIGN
+    assert r(FAKE, 0, FAKE, 1e-6, 1, 256, FAKE + 4, None) == sk.SK_ERR_ALIGN
+    sw = sk.LIB.sk_prologue_swiglu
+    assert sw(None, FAKE, 256, 0, 1, 256, FAKE, None) == sk.SK_ERR_NULL
+    assert sw(FAKE, None, 256, 0, 1, 256, FAKE, None) == sk.SK_ERR_NULL
+    assert sw(FAKE, FAKE, 256, 0, 1, 256, None, None) == sk.SK_ERR_NULL
+    assert sw(FAKE, FAKE, 256, 3, 1, 256, FAKE, None) == sk.SK_ERR_FORMAT
+    assert sw(FAKE, FAKE, 255, 0, 1, 256, FAKE, None) == sk.SK_ERR_SHAPE          # ld < K
+    assert sw(FAKE, FAKE, 256, 0, 9, 256, FAKE, None) == sk.SK_ERR_SHAPE
+    assert sw(FAKE, FAKE, 260, 1, 1, 256, FAKE, None) == sk.SK_ERR_ALIGN          # 520-byte rows
+    assert sw(FAKE + 4, FAKE, 256, 0, 1, 256, FAKE, None) == sk.SK_ERR_ALIGN
+
+
 def test_failed_call_leaves_descriptor_unchanged():
     w = W(layout=0, data=FAKE + 8)
     assert sk.LIB.sk_repack_w4a8(ctypes.byref(w), None) == sk.SK_ERR_ALIGN

@@ -111,3 +111,70 @@ def test_split_entry_points_reject_wrong_layout_and_format():
     with pytest.raises(sk.SkError) as e:
         sk.sk_gemm_w4a8_canonical(w6, x)
     assert e.value.status == sk.SK_ERR_FORMAT
+
+
+# ----------------------------------------------------------------------------
+# the prologues as launches of their own
+# ----------------------------------------------------------------------------
+
+F32 = np.float32
+
+
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+@pytest.mark.parametrize("m,k", [(1, 4096), (3, 4096), (8, 12288), (2, 17408), (5, 2064)])
+def test_prologue_rmsnorm_launch_bit_exact(xt, m, k):
+    h = S.activations(800 + m + k, m, k) * F32(2.5)
+    h[0, :32] *= F32(300.0)                         # a wide spread inside one row
+    x_dev, x = to_dev(h, xt)
+    gam = S.gamma(801 + k, k)
+    out = sk.sk_prologue_rmsnorm(x_dev, torch.from_numpy(gam).cuda(), 1e-6)
+    torch.cuda.synchronize()
+    ref = O.prologue_rmsnorm(x, gam, 1e-6)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+@pytest.mark.parametrize("m,k,pad", [(1, 12288, 0), (3, 12288, 16), (8, 4096, 48), (2, 2064, 0)])
+def test_prologue_swiglu_launch_bit_exact(xt, m, k, pad):
+    gu = np.zeros((m, 2 * k + pad), np.float32)
+    gu[:, :k] = S.activations(810 + m, m, k)
+    gu[:, k:2 * k] = S.activations(811 + m, m, k)
+    gu[:, :64] *= F32(30.0)                         # exp overflow and underflow branches
+    dev, vals = to_dev(gu, xt)
+    out = sk.sk_prologue_swiglu(dev[:, :k], dev[:, k:2 * k])
+    torch.cuda.synchronize()
+    ref = O.prologue_swiglu(vals[:, :k], vals[:, k:2 * k])
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("pro", ["rmsnorm", "swiglu"])
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_split_prologue_chains_match_oracle(pro, m):
+    """prologue launch -> GEMM quantising in its launch (stream layout), and
+    prologue launch -> quantisation launch -> canonical-layout GEMM: q and sx
+    bit-exact, y within the parity bound, both against the oracle."""
+    n, k, g = (384, 4096, 32) if pro == "rmsnorm" else (256, 12288, 32)
+    w_can, buf = gpu_weight(0, n, k, g, 820 + m)
+    w_str, _ = gpu_weight(0, n, k, g, 820 + m)
+    sk.sk_repack_w4a8(w_str)
+    if pro == "rmsnorm":
+        x_dev, x = to_dev(S.activations(821 + m, m, k) * F32(2.5), "bf16")
+        gam = S.gamma(822, k)
+        h = sk.sk_prologue_rmsnorm(x_dev, torch.from_numpy(gam).cuda(), 1e-6)
+        h_ref = O.prologue_rmsnorm(x, gam, 1e-6)
+        y_fused = sk.sk_gemm_fused_rmsnorm(w_str, x_dev, torch.from_numpy(gam).cuda(), 1e-6)
+    else:
+        gu = np.concatenate([S.activations(823 + m, m, k), S.activations(824 + m, m, k)], axis=1)
+        dev, vals = to_dev(np.ascontiguousarray(gu), "f32")
+        h = sk.sk_prologue_swiglu(dev[:, :k], dev[:, k:])
+        h_ref = O.prologue_swiglu(vals[:, :k], vals[:, k:])
+        y_fused = sk.sk_gemm_fused_swiglu(w_str, dev[:, :k], dev[:, k:])
+    y_a = sk.sk_gemm_w4a8(w_str, h)
+    q, sx = sk.sk_quantize_rows(h)
+    y_b = sk.sk_gemm_w4a8_canonical_q(w_can, q, sx)
+    torch.cuda.synchronize()
+    ref = O.reference(0, buf, n, k, g, h_ref)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    for y in (y_a, y_b, y_fused):
+        assert_y_close(y.cpu().numpy(), ref)
