@@ -134,7 +134,11 @@ sk_status run_gemm(const sk_weight* w, bool w6_entry, int prologue, const void* 
 }  // namespace
 
 SK_EXPORT const char* sk_status_string(sk_status s) {
-    switch (s) {
+    // Callers may pass any integer (C enums are ints); read it as one, since
+    // an out-of-range value loaded as the enum type is undefined in C++.
+    int v;
+    std::memcpy(&v, &s, sizeof v);
+    switch (v) {
         case SK_OK: return "ok";
         case SK_ERR_NULL: return "a required pointer is NULL";
         case SK_ERR_SHAPE: return "shape rule violated (format rules, M range, bytes or ld)";

@@ -122,7 +122,8 @@ typedef struct {
  *   K <= 17408 for the GEMM entry points.
  */
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL; any other
+ * integer gives "unknown status"). */
 const char* sk_status_string(sk_status s);
 
 /*
