@@ -472,6 +472,40 @@ def test_back_to_back_calls_in_one_graph(reset_hooks):
             assert_y_close(y.cpu().numpy(), ref)
 
 
+def test_graph_replays_after_the_default_workspace_grows(reset_hooks):
+    """A graph captured on the binding's default workspace keeps pointing at
+    that buffer; an eager call that needs more replaces the default with a
+    larger one but never frees the old, so the graph's replays stay correct."""
+    n, k, g, m = 1040, 4096, 32, 8
+    w, buf = gpu_weight(0, n, k, g, 95)
+    sk.sk_repack_w4a8(w)
+    x = torch.zeros((m, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    sk.set_split(4)
+    sk.sk_gemm_w4a8(w, x, y=y)                      # the default workspace fits it before capture
+    old = sk.default_workspace(1)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sk.sk_gemm_w4a8(w, x, y=y)
+    # a call that needs more than the default holds now: enough 16-row tiles,
+    # split 8 ways at M = 8 (128 * M * S bytes of partials per tile)
+    rows = 16 * (old.nbytes // (128 * m * 8) + 1)
+    big, _ = gpu_weight(0, rows, k, g, 96)
+    sk.sk_repack_w4a8(big)
+    sk.set_split(8)
+    need = sk.gemm_workspace_size(rows, k, g, 0, m)
+    assert need > old.nbytes
+    sk.sk_gemm_w4a8(big, torch.from_numpy(S.activations(97, m, k)).cuda())
+    assert sk.default_workspace(1) is not old and sk.default_workspace(1).nbytes >= need
+    sk.set_split(0)
+    for rep in range(3):
+        xh = S.activations(98 + rep, m, k)
+        x.copy_(torch.from_numpy(xh))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert_y_close(y.cpu().numpy(), O.reference(0, buf, n, k, g, xh))
+
+
 def test_concurrent_streams_with_own_workspaces(reset_hooks):
     """Two streams run split-K GEMMs at the same time, each with its own
     workspace; both results match the oracle."""
