@@ -218,13 +218,15 @@ __device__ inline float rms_apply(float x, float r, float g) {
 // (1 + 2^-24) / sx (three relative errors of at most 2^-24 each), and
 // fp32(h/sx) is within a factor 1 +- 2^-24 of h/sx, so fp32(h/sx) lies between
 // h inv_lo and h inv_hi.  Rounding to the nearest integer is monotone: where the
-// two products round to the same integer, fp32(h/sx) rounds to it too.  Only
-// where they differ (the quotient within about |h/sx| 2^-22 of a half-integer),
-// or for a tiny sx, is the quotient formed by IEEE division.
+// two products round to the same integer, fp32(h/sx) rounds to it too.  Where
+// they differ (the quotient within about |h/sx| 2^-22 of a half-integer: with
+// bf16 activations every element equal to half the row's maximum, 63.5 before
+// sx is rounded, is such a case) the quotient itself is formed, by
+// corrected_code_bits; a row with a tiny sx takes IEEE division throughout.
 constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
 constexpr float kInvLo = 0x1.fffff8p-1f;      // 1 - 2^-22
 constexpr float kInvHi = 0x1.000004p+0f;      // 1 + 2^-22
-constexpr float kTinySx = 2.3509887e-38f;     // 2^-125: below it 1/sx may not be normal
+constexpr float kMinCorrectedSx = 0x1p-100f;  // below it, IEEE division for every element
 // Code bits of h (its low byte is the int8 code) from the lower product; `split`
 // becomes nonzero when the two products round differently.  Both results are
 // 1.5 * 2^23 plus an integer of magnitude <= 128, so their low 16 bits differ
@@ -235,6 +237,20 @@ __device__ inline uint32_t code_bits(float h, float inv_lo, float inv_hi, uint32
     const uint32_t hi = __float_as_uint(__builtin_fmaf(h, inv_hi, kRoundMagic));
     split = __builtin_amdgcn_sad_u16(lo, hi, split);
     return lo;
+}
+// Code bits of h from the correctly rounded quotient fp32(h/sx), formed without
+// a division: q0 = fp32(h inv) is within two ulps of h/sx; one correction
+// q1 = fp32(q0 + r0 inv), r0 = fp32(h - sx q0) by an FMA, leaves it within one
+// ulp; for such a q1 the residual r1 = h - sx q1 is exact in fp32 and, inv being
+// the correctly rounded reciprocal, fp32(q1 + r1 inv) is the correctly rounded
+// quotient (Markstein's theorem on FMA division).  That needs the residuals
+// clear of the subnormal range: sx >= 2^-100 with |h/sx| >= 1/4.  A smaller
+// quotient may end an ulp off, but it rounds to the code 0 either way.
+__device__ inline uint32_t corrected_code_bits(float h, float sx, float inv) {
+    const float q0 = h * inv;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-sx, q0, h), inv, q0);
+    const float q2 = __builtin_fmaf(__builtin_fmaf(-sx, q1, h), inv, q1);
+    return __float_as_uint(q2 + kRoundMagic);
 }
 // bytes 0..3 <- low bytes of b0..b3
 __device__ inline uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
@@ -985,26 +1001,32 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         // quantise this slice into LDS (straight-line code: it runs once per
         // launch, so every instruction of it is a cold instruction-cache fetch)
         if (am.nw > 0) {
-            // codes of all elements first; the exact division, rarely needed, is one
-            // out-of-line block for the whole thread
+            // Codes of all elements from the bracketing products, noting the chunks
+            // that hold an element whose products round apart.  Such elements are
+            // common (with bf16 data most rows have some), so their chunks are
+            // redone with the corrected quotient: a few short blocks, each skipped
+            // by the waves that do not need it, rather than a division per
+            // element, whose cold code would cost more than the quantiser.
             uint32_t b[NCH * E];
-            uint32_t split = 0;
+            uint32_t rare = 0;             // bit i: chunk i needs the corrected quotient
             const float inv_lo = inv * kInvLo, inv_hi = inv * kInvHi;
 #pragma unroll
-            for (int j = 0; j < NCH * E; ++j) b[j] = code_bits(h[j], inv_lo, inv_hi, split);
-            if (__builtin_expect((split != 0 || sx < kTinySx) && sx > 0.0f, 0)) {
-                // The exact quotient for the elements whose two products round
-                // apart (all of them for a tiny sx).  Every launch has some
-                // workgroup on this path, so it must be short; the opaque copy of
-                // inv_hi keeps each element's product in its own step (computed
-                // all at once, the products would need a register each).
-                const bool tiny = sx < kTinySx;
+            for (int i = 0; i < NCH; ++i) {
+                uint32_t split = 0;
 #pragma unroll
-                for (int j = 0; j < NCH * E; ++j) {
-                    float ih = inv_hi;
-                    __asm__ volatile("" : "+v"(ih));
-                    const uint32_t hb = __float_as_uint(__builtin_fmaf(h[j], ih, kRoundMagic));
-                    if (tiny || hb != b[j]) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+                for (int e = 0; e < E; ++e) b[i * E + e] = code_bits(h[i * E + e], inv_lo, inv_hi, split);
+                rare |= (split != 0 ? 1u : 0u) << i;
+            }
+            if (__builtin_expect(sx < kMinCorrectedSx && sx > 0.0f, 0)) {
+#pragma unroll
+                for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+            } else if (__builtin_expect(rare != 0, 0)) {
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    if (rare & (1u << i)) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) b[i * E + e] = corrected_code_bits(h[i * E + e], sx, inv);
+                    }
                 }
             }
             uint32_t pk[NCH * E / 4];

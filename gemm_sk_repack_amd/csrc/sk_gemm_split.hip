@@ -61,9 +61,12 @@ __global__ __launch_bounds__(QT) void quantize_kernel(const void* x, int k, int8
         uint32_t split = 0;
 #pragma unroll
         for (int e = 0; e < E; ++e) b[e] = code_bits(v[e], inv_lo, inv_hi, split);
-        if ((split != 0 || sx < kTinySx) && sx > 0.0f) {
+        if (sx < kMinCorrectedSx && sx > 0.0f) {
 #pragma unroll
             for (int e = 0; e < E; ++e) b[e] = __float_as_uint(v[e] / sx + kRoundMagic);
+        } else if (split != 0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) b[e] = corrected_code_bits(v[e], sx, inv);
         }
         int8_t* dst = q + (int64_t)m * k + (int64_t)c * E;
         if constexpr (E == 4) {
