@@ -187,16 +187,21 @@ def test_zero_and_constant_rows():
 
 
 def tiny_rows(k):
-    """Rows whose scale sx = absmax/127 falls below 2^-125 (the quantiser's exact-
-    division branch), down into the subnormal range, and rows of subnormal h."""
+    """Rows on both sides of the smallest scale the quantiser's bracket and
+    corrected quotient take (sx = 2^-100; below it every element goes through IEEE
+    division), with exact ties at that scale, scales down into the subnormal range,
+    and rows of subnormal h."""
     rng = np.random.default_rng(27)
     base = S.activations(28, 8, k).astype(np.float64)
     base /= np.abs(base).max(axis=1, keepdims=True)
-    amx = [127.0 * 2.0 ** -125,        # sx = 2^-125 exactly: the last normal-path scale
-           127.0 * 2.0 ** -125 * 0.75, # sx just below it
-           1e-37, 3e-39, 1e-40, 2e-44,  # sx subnormal; the last rows' h are subnormal too
-           1e-38, 1e-30]
+    amx = [127.0 * 2.0 ** -100,         # sx = 2^-100 exactly: the smallest bracket scale
+           127.0 * 2.0 ** -100 * 0.75,  # sx just below it: division throughout
+           127.0 * 2.0 ** -125,         # a normal sx far below it
+           1e-37, 3e-39, 2e-44, 1e-40,  # sx subnormal; the last rows' h are subnormal too
+           1e-30]
     h = (base * np.array(amx)[:, None]).astype(F32)
+    for r in (0, 1):                    # h = absmax / 2: quotient 63.5 exactly, a tie to even
+        h[r, rng.integers(0, k, 24)] = F32(amx[r] / 2.0) * np.where(rng.random(24) < 0.5, F32(1), F32(-1))
     h[5, rng.integers(0, k, 16)] = F32(2.0 ** -149)     # smallest subnormal values
     h[7, ::3] = F32(3e-41)                              # subnormal h in a row of normal scale
     return h
@@ -206,7 +211,8 @@ def tiny_rows(k):
 @pytest.mark.parametrize("xt", ["f32", "bf16"])
 def test_tiny_scale_and_subnormal_activations_bit_exact(m, xt):
     """Denormals are not flushed anywhere in the quantiser: q, sx and P stay
-    bit-exact for scales below 2^-125 and for subnormal activations."""
+    bit-exact at the smallest scale of the bracket path (with exact ties), below it
+    (IEEE division), for subnormal scales and for subnormal activations."""
     n, k, g = 272, 2048, 32
     w, buf = gpu_weight(0, n, k, g, 29)
     sk.sk_repack_w4a8(w)
@@ -215,6 +221,8 @@ def test_tiny_scale_and_subnormal_activations_bit_exact(m, xt):
     h_dev, h_ref = to_dev(np.ascontiguousarray(h[rows]), xt)
     sx_ref = O.quantize_rows(h_ref)[1]
     assert np.any(sx_ref < 2.0 ** -125)
+    if m > 1:
+        assert np.any(sx_ref == F32(2.0 ** -100)) and np.any((sx_ref < 2.0 ** -100) & (sx_ref > 2.0 ** -101))
     check_call(w, buf, 0, n, k, g, h_dev, h_ref, m)
     q, sx = sk.sk_quantize_rows(h_dev)
     torch.cuda.synchronize()
