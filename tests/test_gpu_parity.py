@@ -249,7 +249,7 @@ def near_tie_rows(seed, m, k):
 
 @pytest.mark.parametrize("m", [1, 3, 8])
 def test_near_tie_activations_bit_exact(m):
-    """Quotients next to half-integers take the kernels' exact-division branch."""
+    """Quotients next to half-integers take the kernels' corrected-quotient branch."""
     n, k, g = 256, 4096, 32
     w, buf = gpu_weight(0, n, k, g, 25)
     sk.sk_repack_w4a8(w)
