@@ -29,6 +29,7 @@ pytestmark = pytest.mark.gpu
 import gemm_sk_repack_amd as sk  # noqa: E402
 
 from test_gpu_parity import assert_y_close  # noqa: E402
+from test_quant_rule_cpu import rule  # noqa: E402
 
 
 def sample_rows(n, seed, count=64):
@@ -146,5 +147,9 @@ def test_27b_layer_bf16(li):
     for m in (1, 8):
         bits = S.to_bf16_bits(S.activations(S.seed_of(2, li, S.TENSOR_X), m, k))
         xd = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        h = O.bf16_to_f32(bits)
+        # bf16 rows hold elements at half the row maximum: their bracketing
+        # products round apart, so q checks the corrected-quotient branch too
+        assert rule(h, O.quantize_rows(h)[1])[1].any()
         out = sk.sk_debug_gemm(w, sk.PRO_NONE, xd)
-        compare(S.FMT_W4, buf, n, k, g, rows, O.bf16_to_f32(bits), out, sk.sk_gemm_w4a8(w, xd))
+        compare(S.FMT_W4, buf, n, k, g, rows, h, out, sk.sk_gemm_w4a8(w, xd))
