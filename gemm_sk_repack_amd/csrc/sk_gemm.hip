@@ -78,8 +78,8 @@ int workgroups_per_slice(int cus, int S, int T) {
 }
 
 // The plan for a given number of activations per thread (the kernel's register
-// budget for the prologue).
-Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
+// budget for the prologue).  An RMSNorm launch also keeps the slice's gamma in LDS.
+Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pro) {
     Plan p;
     const int pipe = pipe_of(m == 1 && G.fmt != FMT_CB);
     const int KB = (int)G.KB;
@@ -93,8 +93,9 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept) {
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
         const size_t red = 2 * (size_t)kRedHalf * 4;
-        if (cb) return 64 + (size_t)m * (2 * KS + 64) + red;      // levels, bf16 q, partials
-        return (size_t)m * (KS + 32) + red;
+        const size_t gam = (pro == PRO_RMSNORM) ? 4 * KS : 0;     // RMSNorm: the slice's gamma
+        if (cb) return 64 + (size_t)m * (2 * KS + 64) + red + gam;   // levels, bf16 q, partials
+        return (size_t)m * (KS + 32) + red + gam;
     };
     const size_t kLdsMax = 150 * 1024;
     auto valid = [&](int s) { return s >= 1 && s <= SMAX && KB % s == 0 && fits(s) && lds_of(s) <= kLdsMax; };
@@ -156,34 +157,34 @@ Plan make_plan(const Geom& G, int m, int pro, int cus, int split_override) {
     // Each thread quantises at most 16 activations of its row (M = 1 on v_dot4,
     // or a prologue), 32 on the MFMA path without a prologue (the codebook
     // included); the wide instances take 24 (v_dot4), 40 (MFMA, integer formats,
-    // no prologue) or 32 (RMSNorm with 4-bit weights, one K-slice only) and are
-    // used only where that needs fewer K-slices.  (The split path's PRO_QIN
+    // no prologue, or RMSNorm with 4-bit weights and one K-slice) and are used
+    // only where that needs fewer K-slices.  (The split path's PRO_QIN
     // keeps PRO_NONE's plan, so the two compare like for like.)
     if (dot4 && (pro == PRO_NONE || pro == PRO_QIN)) {
         // M = 1 on v_dot4: 16, or 24 in the wide instances where that saves slices
-        const Plan p = plan_for(G, m, cus, split_override, 16);
-        Plan w = plan_for(G, m, cus, split_override, 24);
+        const Plan p = plan_for(G, m, cus, split_override, 16, pro);
+        Plan w = plan_for(G, m, cus, split_override, 24, pro);
         if (w.ok && (!p.ok || w.S < p.S)) {
             w.wide = true;
             return w;
         }
         return p;
     }
-    if (dot4 || pro == PRO_SWIGLU || (cb && pro != PRO_NONE)) return plan_for(G, m, cus, split_override, 16);
-    if (cb) return plan_for(G, m, cus, split_override, 32);   // no wide codebook instances
+    if (dot4 || pro == PRO_SWIGLU || (cb && pro != PRO_NONE)) return plan_for(G, m, cus, split_override, 16, pro);
+    if (cb) return plan_for(G, m, cus, split_override, 32, pro);   // no wide codebook instances
     if (pro == PRO_RMSNORM) {
-        if (G.fmt != FMT_W4) return plan_for(G, m, cus, split_override, 16);
-        const Plan p = plan_for(G, m, cus, split_override, 16);
+        if (G.fmt != FMT_W4) return plan_for(G, m, cus, split_override, 16, pro);
+        const Plan p = plan_for(G, m, cus, split_override, 16, pro);
         if (p.ok && p.S == 1) return p;
-        Plan w = plan_for(G, m, cus, split_override, 32);
+        Plan w = plan_for(G, m, cus, split_override, 40, pro);
         if (w.ok && w.S == 1) {
             w.wide = true;
             return w;
         }
         return p;
     }
-    const Plan p = plan_for(G, m, cus, split_override, 32);
-    Plan w = plan_for(G, m, cus, split_override, 40);
+    const Plan p = plan_for(G, m, cus, split_override, 32, pro);
+    Plan w = plan_for(G, m, cus, split_override, 40, pro);
     if (w.ok && (!p.ok || w.S < p.S)) {
         w.wide = true;
         return w;

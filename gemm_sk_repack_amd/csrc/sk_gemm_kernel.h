@@ -458,6 +458,21 @@ __device__ inline float abs_max_bf16(const uint4 xr[Act<1, EPT>::NCH]) {
 }
 
 // A row's slice statistic from its waves' values, in wave order.
+// Sum over the waves of row m (m wave-uniform): lane k of each 16-lane row takes
+// wave k's value (0 for the waves of other rows), then a fixed tree within the
+// 16 lanes leaves the sum in every lane (each step adds two equal-shaped halves,
+// so every lane computes the same sum, in the same order every launch).
+__device__ inline double row_sum_d(const KArgs& a, const Smem& sm, int m) {
+    const int k = threadIdx.x & 15;
+    const int lo = m * a.WPR;
+    const double w = sm.wd[k];
+    double v = (k >= lo && k < lo + a.WPR) ? w : 0.0;
+    v += dpp_d<DPP_XOR1>(v);
+    v += dpp_d<DPP_XOR2>(v);
+    v += dpp_d<DPP_HMIRROR>(v);
+    v += dpp_d<DPP_MIRROR>(v);
+    return v;
+}
 __device__ inline double combine_d(const KArgs& a, const Smem& sm, int m) {
     const int lo = m * a.WPR, hi = lo + a.WPR;
     const double2* p = reinterpret_cast<const double2*>(sm.wd);
@@ -681,12 +696,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // Activations per thread: 16 on v_dot4 or with a prologue, 32 on the MFMA
     // path without one.  The wide instances (used only where they save
     // K-slices: their larger prologue code costs the other calls time) take 24
-    // on v_dot4 (K = 17408 in one slice), 40 on the MFMA path without a
-    // prologue, and 32 with the RMSNorm prologue for a single K-slice and 4-bit
-    // weights: compiling out the cross-slice exchange (ONE) is what makes room
-    // for the latter (the 6-bit unpack needs a few registers more than are left).
+    // on v_dot4 (K = 17408 in one slice), and 40 on the MFMA path without a
+    // prologue or with the RMSNorm prologue for a single K-slice and 4-bit
+    // weights: compiling out the cross-slice exchange (ONE), and keeping gamma
+    // in LDS rather than beside each activation, is what makes room for the
+    // latter (the 6-bit unpack needs a few registers more than are left).
     constexpr bool ONE = WIDE && PRO == PRO_RMSNORM && !DOT4;
-    constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : PRO == PRO_NONE ? (WIDE ? 40 : 32) : ONE ? 32 : 16;
+    constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : (PRO == PRO_NONE || ONE) ? (WIDE ? 40 : 32) : 16;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
     constexpr int PIPE = DOT4 ? kPipeDot4 : kPipeMfma;
@@ -723,7 +739,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const uint32_t wt = a.wtab[wv];
     const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
     uint4 xr[NCH], ur[NCH];
-    float gv[NCH * E];
+    // RMSNorm: the slice's gamma, float4 i = tid + j * NT, on its way to LDS.  A
+    // slice holds at most EPT activations per thread of its row, and a row has
+    // all NT threads only at M = 1 (v_dot4, or the codebook), NT / 2 or fewer
+    // otherwise: EPT / 4, or EPT / 8, float4 per thread (and K <= 17408).
+    constexpr int GQ_ROWS = (DOT4 || CB) ? EPT / 4 : EPT / 8;
+    constexpr int GQ_MAXK = (int)((kMaxGemmK / 4 + NT - 1) / NT);
+    constexpr int GQ = (PRO != PRO_RMSNORM) ? 1 : GQ_ROWS < GQ_MAXK ? GQ_ROWS : GQ_MAXK;
+    float4 gq[GQ];
     // Split path (PRO_QIN): the slice's q arrives ready, M rows of KS / 8
     // octets; thread tid takes octets tid + i * NT, QMAX per pass.
     constexpr int QMAX = 4;
@@ -744,7 +767,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         q_load(0);
     } else {
         load_act<PRO, XT, EPT>(a, am, k_lo, xr, ur);
-        if (PRO == PRO_RMSNORM) load_gamma<XT, EPT>(a, am, k_lo, gv);
+        if (PRO == PRO_RMSNORM) {
+            // every row scales by the same gamma: it is loaded once per
+            // workgroup, coalesced, and kept in LDS instead of in registers
+            // beside each activation
+            const float4* gp = reinterpret_cast<const float4*>(a.gamma + k_lo);
+#pragma unroll
+            for (int j = 0; j < GQ; ++j)
+                gq[j] = ((tid + j * NT) * 4 < a.KS) ? gp[tid + j * NT] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
     }
 
     // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
@@ -768,6 +799,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     uint32_t* lut_l = reinterpret_cast<uint32_t*>(lds);
     int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
     float* red_l = reinterpret_cast<float*>(q_l + (size_t)M * a.ks);
+    float* gam_l = red_l + 2 * kRedHalf;          // RMSNorm: the slice's gamma, KS floats
 
     // Slots: the wave's weight stream is a sequence of super-blocks, spw per
     // tile step, walked in groups of PIPE slots (a tile step's last group is
@@ -957,10 +989,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         if (PRO == PRO_RMSNORM) {
             const double ss = wave_sum(sum_sq<XT, EPT>(h));
             if (lane == 0) sm.wd[wv] = ss;
+#pragma unroll
+            for (int j = 0; j < GQ; ++j)
+                if ((tid + j * NT) * 4 < a.KS) reinterpret_cast<float4*>(gam_l)[tid + j * NT] = gq[j];
             __syncthreads();
             double tot;
             if (ONE || a.S == 1) {
-                tot = combine_d(a, sm, mrow);
+                tot = row_sum_d(a, sm, mrow);
             } else {
                 if (poller) exchange_poll(a, sm, lane, s, true);
                 __syncthreads();
@@ -973,8 +1008,22 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const float sd = (float)__builtin_sqrt((double)d);   // correctly rounded fp32 sqrt
             const float rr = (float)(1.0 / (double)sd);          // correctly rounded fp32 1/x
             if (row_lead) sm.rr[am.m] = rr;
+            // chunk i of this thread is elements c E .. c E + E - 1 of the slice;
+            // a chunk past the row (h = 0 there) reads the row's last gamma
 #pragma unroll
-            for (int j = 0; j < NCH * E; ++j) h[j] = rms_apply(h[j], rr, gv[j]);
+            for (int i = 0; i < NCH; ++i) {
+                const int cc = min(chunk_of(am, i), am.cpr - 1);
+                const float4* gp = reinterpret_cast<const float4*>(gam_l + cc * E);
+#pragma unroll
+                for (int v = 0; v < E / 4; ++v) {
+                    const float4 g4 = gp[v];
+                    const int j = i * E + 4 * v;
+                    h[j] = rms_apply(h[j], rr, g4.x);
+                    h[j + 1] = rms_apply(h[j + 1], rr, g4.y);
+                    h[j + 2] = rms_apply(h[j + 2], rr, g4.z);
+                    h[j + 3] = rms_apply(h[j + 3], rr, g4.w);
+                }
+            }
         }
         float amx;
         {

@@ -316,6 +316,33 @@ def test_fused_rmsnorm(m, fmt, g, xt):
     assert torch.equal(y, y_pub)
 
 
+@pytest.mark.parametrize("m", [2, 6, 7, 8])
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+def test_fused_rmsnorm_hidden_5120(m, xt):
+    """At hidden 5120 an RMSNorm launch with M >= 6 holds 40 activations per
+    thread (gamma kept in LDS) and runs one K-slice; q, sx and P stay bit-exact,
+    N ragged."""
+    n, k, g = 400, 5120, 32
+    plan = sk.gemm_plan(n, k, g, sk.SK_W4_SYM, m, prologue=sk.PRO_RMSNORM)
+    if m >= 6:
+        assert plan["S"] == 1 and plan["wide"] and plan["ept"] == 40
+    w, buf = gpu_weight(0, n, k, g, 44)
+    sk.sk_repack_w4a8(w)
+    x_dev, x = to_dev(S.activations(45 + m, m, k) * F32(1.5), xt)
+    gam = S.gamma(46, k)
+    eps = 1e-5
+    y, q, sx, p = sk.sk_debug_gemm(w, sk.PRO_RMSNORM, x_dev, gamma=torch.from_numpy(gam).cuda(), eps=eps)
+    y_pub = sk.sk_gemm_fused_rmsnorm(w, x_dev, torch.from_numpy(gam).cuda(), eps)
+    torch.cuda.synchronize()
+    h = O.prologue_rmsnorm(x, gam, eps)
+    ref = O.reference(0, buf, n, k, g, h)
+    assert np.array_equal(sx.cpu().numpy().view(np.uint32), ref["sx"].view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), ref["q"])
+    assert np.array_equal(p.cpu().numpy().astype(np.int64), ref["P"])
+    assert_y_close(y.cpu().numpy(), ref)
+    assert torch.equal(y, y_pub)
+
+
 @pytest.mark.parametrize("m", [1, 3, 8])
 @pytest.mark.parametrize("xt", ["f32", "bf16"])
 def test_fused_swiglu(m, xt):

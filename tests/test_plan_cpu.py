@@ -44,9 +44,9 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     elif m == 1 or pro == sk.PRO_SWIGLU or (pro == sk.PRO_RMSNORM and fmt != 0):
         assert ept == 16 and not p["wide"]
     elif pro == sk.PRO_RMSNORM:
-        # 32 activations with RMSNorm only in the one-slice instances, and only
+        # 40 activations with RMSNorm only in the one-slice instances, and only
         # where 16 would need a K-split
-        assert ept == (32 if p["wide"] else 16)
+        assert ept == (40 if p["wide"] else 16)
         if p["wide"]:
             assert S == 1 and k > 16 * 64 * (NW // m)
     else:
@@ -60,6 +60,15 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert p["TW"] * p["KW"] <= NW and p["TW"] * m * 16 <= NW * 64
     assert p["spw"] * p["KW"] == p["KBs"]
     assert p["lds"] <= 150 * 1024
+    # LDS: q (int8, or bf16 after the codebook's 64-byte level table), the wave
+    # partials' two halves, and for RMSNorm the slice's gamma
+    KS = p["KS"]
+    red = 2 * 8 * 16 * 20 * 4
+    gam = 4 * KS if pro == sk.PRO_RMSNORM else 0
+    if fmt == sk.SK_W4_CODEBOOK:
+        assert p["lds"] == 64 + m * (2 * KS + 64) + red + gam
+    else:
+        assert p["lds"] == m * (KS + 32) + red + gam
     if m == 1 and k <= 16384:
         assert S == 1                                        # no cross-slice merge at M = 1
     assert p["part_floats"] == (T * S * m * 16 if S > 1 else 0)
