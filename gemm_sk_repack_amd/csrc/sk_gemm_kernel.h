@@ -473,34 +473,20 @@ __device__ inline double row_sum_d(const KArgs& a, const Smem& sm, int m) {
     v += dpp_d<DPP_MIRROR>(v);
     return v;
 }
+// A row's slice statistic from its waves' values in ascending wave order, as a
+// short loop: these run once per launch from a cold instruction cache, where
+// every 64 bytes of code cost about 0.1 us.
 __device__ inline double combine_d(const KArgs& a, const Smem& sm, int m) {
-    const int lo = m * a.WPR, hi = lo + a.WPR;
-    const double2* p = reinterpret_cast<const double2*>(sm.wd);
-    double v[NW];
-#pragma unroll
-    for (int q = 0; q < NW / 2; ++q) {
-        const double2 t = p[q];
-        v[2 * q] = t.x;
-        v[2 * q + 1] = t.y;
-    }
-    double s = 0.0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) s = (w >= lo && w < hi) ? s + v[w] : s;
-    return s;
+    double v = 0.0;
+#pragma nounroll
+    for (int w = m * a.WPR; w < (m + 1) * a.WPR; ++w) v += sm.wd[w];
+    return v;
 }
 __device__ inline float combine_f(const KArgs& a, const Smem& sm, int m) {
-    const int lo = m * a.WPR, hi = lo + a.WPR;
-    const float4* p = reinterpret_cast<const float4*>(sm.wf);
-    float s = 0.0f;
-#pragma unroll
-    for (int q = 0; q < NW / 4; ++q) {
-        const float4 t = p[q];
-        const float e[4] = {t.x, t.y, t.z, t.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (4 * q + k >= lo && 4 * q + k < hi) s = fmaxf(s, e[k]);
-    }
-    return s;
+    float v = 0.0f;
+#pragma nounroll
+    for (int w = m * a.WPR; w < (m + 1) * a.WPR; ++w) v = fmaxf(v, sm.wf[w]);
+    return v;
 }
 // Max over the waves of row m (m wave-uniform): lane k of each 16-lane row
 // takes wave k's value, and a max within the row leaves the result in every
@@ -581,83 +567,81 @@ __device__ inline void slice_stat(const KArgs& a, Smem& sm, uint32_t wt, int lan
 #endif
 constexpr uint64_t kXcdPollTicks = SK_XCD_POLL_TICKS;
 
-// Exchange this slice's per-row value with the other slices (S > 1), run by
+// Exchange of this slice's per-row value with the other slices (S > 1), run by
 // the poller wave only, after the waves' values are in sm.wd / sm.wf.  Every
 // word carries the call's tag in its high half, so no fence is needed: a
 // reader simply waits until all words show the tag.  absmax: one word
 // (tag | float bits).  Sum of squares (double): two words (tag | high half),
-// (tag | low half).
+// (tag | low half).  Word j = sl * 8 + row of slice sl.
+//
+// The code is kept short on purpose: one wave runs it once per launch from a
+// cold instruction cache, where every 64 bytes of code cost about 0.1 us.
+//
+// absmax with the slices on one XCD: the slices of a range are workgroups r,
+// r + R, r + 2R, ...; with R a multiple of the 8 chiplets and round-robin
+// dispatch they share an XCD, so a word stored through the L1 into that XCD's
+// L2 (sc0) is seen there by the other slices' polls within a few hundred ns.
+// The device-scope copy is written only after this wave's polls: its write is
+// acknowledged once it has gone out to memory, and every poll's wait would
+// wait for that acknowledgement too (a wave's vector memory operations
+// complete in order).  A poll that sees nothing on the chiplet for
+// kXcdPollTicks (the slices sit on other XCDs) turns to the device-scope copy.
+__device__ inline void exchange_publish(const KArgs& a, Smem& sm, int lane, int s, bool is_ss) {
+    if (lane >= a.m) return;
+    const u64 tag = (u64)sm.tag << 32;
+    const int j = s * 8 + lane;
+    if (is_ss) {
+        const double v = combine_d(a, sm, lane);
+        sm.exd[lane * SMAX + s] = v;
+        const u64 bits = (u64)__double_as_longlong(v);
+        __hip_atomic_store(&a.ws->ssh[j], tag | (bits >> 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&a.ws->ssl[j], tag | (bits & 0xFFFFFFFFull), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+        const float v = combine_f(a, sm, lane);
+        sm.exf[lane * SMAX + s] = v;
+        const u64 w = tag | __float_as_uint(v);
+        if ((a.R & 7) == 0)
+            __asm__ volatile("global_store_dwordx2 %0, %1, off sc0" ::"v"(&a.ws->amax_xcd[j]), "v"(w) : "memory");
+        else
+            __hip_atomic_store(&a.ws->amax[j], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 __device__ inline void exchange_poll(const KArgs& a, Smem& sm, int lane, int s, bool is_ss) {
     const uint32_t tag = sm.tag;
-    if (lane < a.m) {
-        const int slot = s * 8 + lane;
-        if (is_ss) {
-            const double v = combine_d(a, sm, lane);
-            sm.exd[lane * SMAX + s] = v;
-            const u64 bits = (u64)__double_as_longlong(v);
-            __hip_atomic_store(&a.ws->ssh[slot], ((u64)tag << 32) | (bits >> 32), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ws->ssl[slot], ((u64)tag << 32) | (bits & 0xFFFFFFFFull),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-            const float v = combine_f(a, sm, lane);
-            sm.exf[lane * SMAX + s] = v;
-            const u64 w = ((u64)tag << 32) | __float_as_uint(v);
-            // the chiplet-local copy first: a store reaches this XCD's L2
-            // (sc0: written through the CU's L1), where the other slices of
-            // the range read it when they run on the same XCD
-            __asm__ volatile("global_store_dwordx2 %0, %1, off sc0" ::"v"(&a.ws->amax_xcd[slot]), "v"(w) : "memory");
-            __hip_atomic_store(&a.ws->amax[slot], w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
+    const bool xcd = !is_ss && (a.R & 7) == 0;
     if (lane < SMAX) sm.miss[lane] = 0;
-    for (int j = lane; j < a.S * a.m; j += 64) {
-        const int sl = j / a.m, mm = j % a.m;
-        const int slot = sl * 8 + mm;
-        if (sl == s) continue;
+#pragma nounroll
+    for (int j = lane; j < a.S * 8; j += 64) {
+        const int sl = j >> 3, mm = j & 7;
+        if (sl == s || mm >= a.m) continue;
+        const u64* p = is_ss ? &a.ws->ssh[j] : xcd ? &a.ws->amax_xcd[j] : &a.ws->amax[j];
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         bool ok = false;
-        if (!is_ss) {
-            // The slices of a range are workgroups r, r + R, r + 2R, ...; with R
-            // a multiple of the 8 chiplets and round-robin dispatch they share
-            // an XCD, so the value shows up in this L2 within a few hundred ns.
-            // Only a short bounded poll: when the slices sit on other XCDs it
-            // never shows, and the device-scope words below serve.
-            const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-            for (int it = 0; (a.R & 7) == 0 && it < a.spin_limit; ++it) {
-                u64 v;
-                __asm__ volatile("global_load_dwordx2 %0, %1, off sc0\n\ts_waitcnt vmcnt(0)"
-                                 : "=v"(v) : "v"(&a.ws->amax_xcd[slot]) : "memory");
-                if ((uint32_t)(v >> 32) == tag) {
-                    sm.exf[mm * SMAX + sl] = __uint_as_float((uint32_t)v);
-                    ok = true;
-                    break;
-                }
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kXcdPollTicks) break;
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        for (int it = 0; !ok && it < a.spin_limit; ++it) {
+#pragma nounroll
+        for (int it = 0; it < a.spin_limit; ++it) {
+            const u64 v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            uint32_t lo = (uint32_t)v;
+            bool seen = (uint32_t)(v >> 32) == tag;
             if (is_ss) {
-                const u64 hi = __hip_atomic_load(&a.ws->ssh[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                const u64 lo = __hip_atomic_load(&a.ws->ssl[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if ((uint32_t)(hi >> 32) == tag && (uint32_t)(lo >> 32) == tag) {
-                    sm.exd[mm * SMAX + sl] = __longlong_as_double((long long)(((hi & 0xFFFFFFFFull) << 32) |
-                                                                    (lo & 0xFFFFFFFFull)));
-                    ok = true;
-                    break;
-                }
-            } else {
-                const u64 v = __hip_atomic_load(&a.ws->amax[slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if ((uint32_t)(v >> 32) == tag) {
-                    sm.exf[mm * SMAX + sl] = __uint_as_float((uint32_t)v);
-                    ok = true;
-                    break;
-                }
+                const u64 w = __hip_atomic_load(&a.ws->ssl[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                seen = seen && (uint32_t)(w >> 32) == tag;
+                if (seen) sm.exd[mm * SMAX + sl] = __longlong_as_double((long long)(((u64)lo << 32) | (uint32_t)w));
+            } else if (seen) {
+                sm.exf[mm * SMAX + sl] = __uint_as_float(lo);
             }
+            if (seen) {
+                ok = true;
+                break;
+            }
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kXcdPollTicks) p = is_ss ? p : &a.ws->amax[j];
             __builtin_amdgcn_s_sleep(1);
         }
         if (!ok) sm.miss[sl] = 1;          // every writer stores the same value
     }
+    if (xcd && lane < a.m)
+        __hip_atomic_store(&a.ws->amax[s * 8 + lane], ((u64)tag << 32) | __float_as_uint(sm.exf[lane * SMAX + s]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // y of output row omm in tile ot from its scaled sum: sx * sum, or NaN for a
@@ -997,7 +981,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             if (ONE || a.S == 1) {
                 tot = row_sum_d(a, sm, mrow);
             } else {
-                if (poller) exchange_poll(a, sm, lane, s, true);
+                if (poller) {
+                    exchange_publish(a, sm, lane, s, true);
+                    exchange_poll(a, sm, lane, s, true);
+                }
                 __syncthreads();
                 for (int sl = 0; sl < a.S; ++sl)
                     if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, true);
@@ -1033,7 +1020,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             if (ONE || a.S == 1) {
                 amx = row_max(a, sm, mrow, lane);
             } else {
-                if (poller) exchange_poll(a, sm, lane, s, false);
+                if (poller) {
+                    exchange_publish(a, sm, lane, s, false);
+                    exchange_poll(a, sm, lane, s, false);
+                }
                 __syncthreads();
                 for (int sl = 0; sl < a.S; ++sl)
                     if (sm.miss[sl]) slice_stat<PRO, XT, EPT>(a, sm, wt, lane, wv, sl, false);
@@ -1384,7 +1374,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    arrive adds them, for every tile of the range, in slice order
     if (!ONE && a.S > 1) {
         __syncthreads();
-        if (tid == 0) {
+        // counted by the poller wave: it stored no partials, so the count's
+        // round trip does not wait behind their writes
+        if (poller && lane == 0) {
             const uint32_t old = __hip_atomic_fetch_add(&a.ws->cnt[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const int lst = old == (uint32_t)(a.S - 1);
             if (lst) __hip_atomic_store(&a.ws->cnt[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
