@@ -1374,9 +1374,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    arrive adds them, for every tile of the range, in slice order
     if (!ONE && a.S > 1) {
         __syncthreads();
-        // counted by the poller wave: it stored no partials, so the count's
-        // round trip does not wait behind their writes
-        if (poller && lane == 0) {
+        // counted by the poller wave (the last one): it stored no partials,
+        // so the count's round trip does not wait behind their writes
+        if (tid == (NW - 1) * 64) {
             const uint32_t old = __hip_atomic_fetch_add(&a.ws->cnt[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const int lst = old == (uint32_t)(a.S - 1);
             if (lst) __hip_atomic_store(&a.ws->cnt[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
