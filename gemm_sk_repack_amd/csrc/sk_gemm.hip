@@ -2,6 +2,7 @@
 // (the kernel itself is in sk_gemm_kernel.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "sk_gemm_kernel.h"
@@ -90,9 +91,12 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     p.ept = ept;
     p.wide = false;
     auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
+    // tile-epilogue partials: TW * kwp <= 4 * min(16, 64 / M) (KW <= 4) or
+    // 32 (KW >= 5), for M * 16 outputs per tile group, two halves
+    const size_t red_max = 2 * 4 * (size_t)m * 16 * (size_t)std::max(4 * std::min(16, 64 / m), 32);
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
-        const size_t red = 2 * (size_t)kRedHalf * 4;
+        const size_t red = red_max;
         const size_t gam = (pro == PRO_RMSNORM) ? 4 * KS : 0;     // RMSNorm: the slice's gamma
         if (cb) return 64 + (size_t)m * (2 * KS + 64) + red + gam;   // levels, bf16 q, partials
         return (size_t)m * (KS + 32) + red + gam;
@@ -143,7 +147,10 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
         const int need = (p.KS + ept * 64 - 1) / (ept * 64);
         if (need >= 1 && need < p.WPR) p.WPR = need;
     }
-    p.lds = (S > 0) ? lds_of(S) : 0;
+    p.kwp = red_kwp(p.KW);
+    p.red_half = p.TW * m * 16 * p.kwp;
+    // the exact partials buffer of this wave split (at most red_max)
+    p.lds = (S > 0) ? lds_of(S) - red_max + 2 * 4 * (size_t)p.red_half : 0;
     p.part_floats = (S > 1) ? (size_t)T * S * m * 16 : 0;
     p.ok = valid(S) && p.KBs >= 1 && p.spw >= 1 && p.P >= 1 && m >= 1 && m <= 8;
     return p;
@@ -245,6 +252,9 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.n = (int)G.n;
     a.k = (int)G.k;
     a.m = c.m;
+    a.m_magic = (65536 + c.m - 1) / c.m;
+    a.kwp = p.kwp;
+    a.red_half = p.red_half;
     a.T = (int)G.T;
     a.KB = (int)G.KB;
     a.kg = (int)G.kg;
@@ -273,6 +283,7 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.ks = p.ks;
     a.spin_limit = c.spin_limit > 0 ? c.spin_limit : (1 << 20);
     a.tpe = c.rows_per_expert / TILE_ROWS;
+    a.tpe_magic = a.tpe > 0 ? (1ull << 40) / (u64)a.tpe + 1 : 0;
     a.n_experts = c.n_experts;
     a.experts = c.experts;
     a.tq = (int)(G.T / p.R);

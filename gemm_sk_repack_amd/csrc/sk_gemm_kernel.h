@@ -72,9 +72,10 @@ constexpr int kPipeDot4 = SK_PIPE_DOT4, kPrimeDot4 = SK_PRIME_DOT4;
 constexpr int kPipeMfma = SK_PIPE_MFMA, kPrimeMfma = SK_PRIME_MFMA;
 constexpr int pipe_of(bool dot4) { return dot4 ? kPipeDot4 : kPipeMfma; }
 constexpr int SMAX = 32;       // largest number of K-slices
-// Tile-epilogue LDS: per half, [8 rows][16 columns][kRedPitch >= NW waves] floats.
-constexpr int kRedPitch = 20;
-constexpr int kRedHalf = 8 * 16 * kRedPitch;
+// Tile-epilogue LDS: per half, [tile group][row][column][kwp] floats, kwp =
+// the k-parts per tile group rounded up to 4, 8 or 16 (the entries past KW
+// stay zero), so a thread sums its output's partials without masks.
+constexpr int red_kwp(int kw) { return kw <= 4 ? 4 : kw <= 8 ? 8 : 16; }
 // Weight-stream buffer loads: the resource of a slot group spans kRsrcMax bytes
 // from the group's first byte (every real slot lies inside), and an offset of
 // kOutside lies past it, so such a load returns zeros without touching memory.
@@ -135,6 +136,9 @@ struct KArgs {
     int n, k;
     int T, kg;
     int R, P, KW, WPR, ks;
+    int m_magic;            // (65536 + M - 1) / M: x / M = (x * m_magic) >> 16 for x < 64
+    int kwp, red_half;      // partials pitch and floats per half of the tile-epilogue buffer
+    u64 tpe_magic;          // floor(2^40 / tpe) + 1: t / tpe = (t * tpe_magic) >> 40 for t < 2^20
     int spin_limit;
 };
 
@@ -654,9 +658,14 @@ __device__ inline int expert_id(const KArgs& a, int i) {
     return ((const_i32*)(a.experts))[__builtin_amdgcn_readfirstlane(i)];
 }
 
+// Index in the expert list of logical tile t (t < 2^20), without a division.
+__device__ inline int tile_expert(const KArgs& a, int t) {
+    return (int)(((u64)(uint32_t)t * a.tpe_magic) >> 40);
+}
+
 __device__ inline float out_value(const KArgs& a, const Smem& sm, int ot, int omm, float sum) {
     if (a.tpe) {
-        const int e = expert_id(a, ot / a.tpe);
+        const int e = expert_id(a, tile_expert(a, ot));
         if (e < 0 || e >= a.n_experts) return __builtin_nanf("");
     }
     return sm.sx[omm] * sum;
@@ -704,7 +713,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                      "s"(a.wtab[wv]));
     const int nl = lane & 15;
     const int hl = lane >> 4;
-    const int M = a.m;
+    const int M = DOT4 ? 1 : a.m;                 // the v_dot4 instances run M = 1 only
     const int r = blockIdx.x;
     const int s = blockIdx.y;
     const int k_lo = s * a.KS;
@@ -713,13 +722,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    statistics -> q -> every dot product), so their loads go out before
     //    any other address arithmetic; then the call's tag and the weight stream
     //    (a wave's loads complete in issue order)
-    // The launch generation first: loads complete in issue order, so waiting
-    // for it later never waits for the activations or weights issued after
-    // it.  The load is unconditional (a conditional one would be waited for
-    // where the two paths join); a launch that does not split K has no
-    // workspace and reads a word of the activations instead, unused.
-    const uint32_t* gen_p = (!ONE && a.S > 1) ? &a.ws->gen : static_cast<const uint32_t*>(a.x);
-    const uint32_t gen = __hip_atomic_load(gen_p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The launch generation first (K-split launches only): loads complete in
+    // issue order, so waiting for it later never waits for the activations or
+    // weights issued after it.  A launch that does not split K skips it: a
+    // device-scope load goes past the chiplet's L2, and the activation loads
+    // behind it (which mostly hit there) would wait for its round trip.
+    uint32_t gen = 0;
+    if (!ONE && a.S > 1) gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t wt = a.wtab[wv];
     const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
     uint4 xr[NCH], ur[NCH];
@@ -783,7 +792,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     uint32_t* lut_l = reinterpret_cast<uint32_t*>(lds);
     int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
     float* red_l = reinterpret_cast<float*>(q_l + (size_t)M * a.ks);
-    float* gam_l = red_l + 2 * kRedHalf;          // RMSNorm: the slice's gamma, KS floats
+    float* gam_l = red_l + 2 * a.red_half;        // RMSNorm: the slice's gamma, KS floats
+    // the partials' padding entries must read as zero: clear both halves (the
+    // first tile step's barrier orders this before any partial is written)
+    for (int i = tid; i < a.red_half / 2; i += NT)
+        reinterpret_cast<float4*>(red_l)[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
     // Slots: the wave's weight stream is a sequence of super-blocks, spw per
     // tile step, walked in groups of PIPE slots (a tile step's last group is
@@ -849,8 +862,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             const int tv = valid ? t : 0;
             int tb = t;
             if (a.tpe) {
-                const int e = expert_id(a, tv / a.tpe);
-                tb = ((e >= 0 && e < a.n_experts) ? e : 0) * a.tpe + tv % a.tpe;
+                const int li = tile_expert(a, tv);
+                const int e = expert_id(a, li);
+                tb = ((e >= 0 && e < a.n_experts) ? e : 0) * a.tpe + (tv - li * a.tpe);
             }
             const int64_t wo = (int64_t)tb * a.tile_full + (int64_t)kb * a.sbf;
             gw = !valid ? 0 : grg ? a.rag_w + (int64_t)kb * a.rag_sbw : wo;
@@ -1119,8 +1133,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             }
         }
     }
-    __syncthreads();
-
+    // The rest of the first group's loads and the next group's cursor go out
+    // before the workgroup waits for q: waves without activations get there
+    // first and, with the loop set-up after them, bring that code into the
+    // instruction cache (empty at every launch) while the others quantise.
 #pragma unroll
     for (int d = PRIME; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
     group_next();
@@ -1300,45 +1316,49 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // kRedPitch floats, so one thread reads all the waves' values of its output
     // with four 16-byte LDS reads (the 16 lanes of a row write to distinct banks).
     auto tile_epilogue = [&](const float* v4, const int j) {
-        float* red = red_l + (j & 1) * kRedHalf;
+        float* red = red_l + (j & 1) * a.red_half;
         if (DOT4) {
             // the four k-quarters of a row sit 16 lanes apart
             float v = v4[0];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
-            if (lane < 16) red[nl * kRedPitch + wv] = v;
-        } else {
+            if (active && lane < 16) red[(tg * 16 + nl) * a.kwp + kw] = v;
+        } else if (active) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int mm = 4 * hl + rr;
-                if (mm < M) red[(mm * 16 + nl) * kRedPitch + wv] = v4[rr];
+                if (mm < M) red[((tg * M + mm) * 16 + nl) * a.kwp + kw] = v4[rr];
             }
         }
         __syncthreads();
         const int nout = a.TW * M * 16;
         if (tid < nout) {
-            const int ogrp = tid / (M * 16);
-            const int omm = (tid / 16) % M;
+            // output (tile group ogrp, row omm, column onn) of thread tid:
+            // tid / 16 = ogrp * M + omm, divided by M through a multiply
+            const int o16 = tid >> 4;
+            const int ogrp = DOT4 ? o16 : (o16 * a.m_magic) >> 16;
+            const int omm = DOT4 ? 0 : o16 - ogrp * M;
             const int onn = tid & 15;
             const int ot = t_begin + ogrp + j * a.TW;
             if (ot < t_end) {
-                // the KW k-parts of tile group ogrp are waves w0 .. w0 + KW - 1,
-                // added in wave order
-                const int w0 = ogrp * a.KW;
-                const float4* rp = reinterpret_cast<const float4*>(red + (omm * 16 + onn) * kRedPitch);
+                // the KW k-parts of tile group ogrp, added in k order (then the
+                // zero padding); all reads go out first: one LDS round trip
+                const float4* rp = reinterpret_cast<const float4*>(red + (o16 * 16 + onn) * a.kwp);
+                float4 t4[4];
+                t4[0] = rp[0];
+                t4[1] = t4[2] = t4[3] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+                if (a.kwp > 4) t4[1] = rp[1];
+                if (a.kwp > 8) {
+                    t4[2] = rp[2];
+                    t4[3] = rp[3];
+                }
                 float osum = 0.0f;
-                // all four reads first: one LDS round trip
-                float4 t4[NW / 4];
 #pragma unroll
-                for (int q4 = 0; q4 < NW / 4; ++q4) t4[q4] = rp[q4];
-#pragma unroll
-                for (int q4 = 0; q4 < NW / 4; ++q4) {
-                    const float wv4[4] = {t4[q4].x, t4[q4].y, t4[q4].z, t4[q4].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int w = 4 * q4 + e;
-                        osum = (w >= w0 && w < w0 + a.KW) ? osum + wv4[e] : osum;
-                    }
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    osum += t4[q4].x;
+                    osum += t4[q4].y;
+                    osum += t4[q4].z;
+                    osum += t4[q4].w;
                 }
                 if (ONE || a.S == 1) {
                     if (ot * TILE_ROWS + onn < a.n)
@@ -1353,6 +1373,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     };
 
     for (int pj = 0; pj < jn; ++pj) {
+        if (pj == 0) __syncthreads();           // q (and sx) complete in LDS
         const bool pvalid = pj < jw;
         const int t = t_begin + tg + pj * a.TW;
         for (int pg = 0; pg < ngrp; ++pg) {

@@ -87,6 +87,8 @@ struct Plan {
     int ept;      // activations per thread (16, 24, 32 or 40)
     bool wide;    // the kernel instances with the larger activation budget
     int ks;       // LDS row stride of q
+    int kwp;      // k-parts per tile group rounded up to 4, 8 or 16 (tile-epilogue pitch)
+    int red_half; // floats per half of the tile-epilogue partials buffer
     size_t lds;   // dynamic LDS bytes
     size_t part_floats;  // workspace words (8 bytes) for slice partials
     bool ok;

@@ -63,7 +63,8 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     # LDS: q (int8, or bf16 after the codebook's 64-byte level table), the wave
     # partials' two halves, and for RMSNorm the slice's gamma
     KS = p["KS"]
-    red = 2 * 8 * 16 * 20 * 4
+    kwp = 4 if p["KW"] <= 4 else 8 if p["KW"] <= 8 else 16   # k-parts padded for the epilogue reads
+    red = 2 * p["TW"] * m * 16 * kwp * 4
     gam = 4 * KS if pro == sk.PRO_RMSNORM else 0
     if fmt == sk.SK_W4_CODEBOOK:
         assert p["lds"] == 64 + m * (2 * KS + 64) + red + gam
