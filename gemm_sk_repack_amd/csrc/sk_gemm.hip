@@ -91,15 +91,20 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     p.ept = ept;
     p.wide = false;
     auto fits = [&](int s) { return (G.k / s) / ept <= (int64_t)tpr; };
-    // tile-epilogue partials: TW * kwp <= 4 * min(16, 64 / M) (KW <= 4) or
-    // 32 (KW >= 5), for M * 16 outputs per tile group, two halves
-    const size_t red_max = 2 * 4 * (size_t)m * 16 * (size_t)std::max(4 * std::min(16, 64 / m), 32);
+    // dynamic LDS of a launch with s slices: q, the tile-epilogue partials of
+    // its wave split (two halves of TW tile groups x M x 16 outputs x kwp), for
+    // RMSNorm the slice's gamma, and (integer formats) the quantiser's list of
+    // chunks to redo
     auto lds_of = [&](int s) {
         const size_t KS = (size_t)(G.k / s);
-        const size_t red = red_max;
+        const int R = workgroups_per_slice(cus, s, T);
+        int kw, tw;
+        split_waves(KB / s, (T + R - 1) / R, m, (s > 1) ? NW - 1 : NW, pipe, kw, tw);
+        const size_t red = 2 * 4 * (size_t)tw * m * 16 * red_kwp(kw);
         const size_t gam = (pro == PRO_RMSNORM) ? 4 * KS : 0;     // RMSNorm: the slice's gamma
         if (cb) return 64 + (size_t)m * (2 * KS + 64) + red + gam;   // levels, bf16 q, partials
-        return (size_t)m * (KS + 32) + red + gam;
+        const size_t fix = (size_t)kFixCap * kFixStride * 4;         // list of chunks to redo
+        return (size_t)m * (KS + 32) + red + gam + fix;
     };
     const size_t kLdsMax = 150 * 1024;
     auto valid = [&](int s) { return s >= 1 && s <= SMAX && KB % s == 0 && fits(s) && lds_of(s) <= kLdsMax; };
@@ -149,8 +154,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     }
     p.kwp = red_kwp(p.KW);
     p.red_half = p.TW * m * 16 * p.kwp;
-    // the exact partials buffer of this wave split (at most red_max)
-    p.lds = (S > 0) ? lds_of(S) - red_max + 2 * 4 * (size_t)p.red_half : 0;
+    p.lds = (S > 0) ? lds_of(S) : 0;
     p.part_floats = (S > 1) ? (size_t)T * S * m * 16 : 0;
     p.ok = valid(S) && p.KBs >= 1 && p.spw >= 1 && p.P >= 1 && m >= 1 && m <= 8;
     return p;

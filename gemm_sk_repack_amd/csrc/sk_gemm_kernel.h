@@ -231,6 +231,14 @@ constexpr float kRoundMagic = 12582912.0f;   // 1.5 * 2^23
 constexpr float kInvLo = 0x1.fffff8p-1f;      // 1 - 2^-22
 constexpr float kInvHi = 0x1.000004p+0f;      // 1 + 2^-22
 constexpr float kMinCorrectedSx = 0x1p-100f;  // below it, IEEE division for every element
+// Chunks with an element whose bracketing products round apart are listed by
+// their wave in LDS (the chunk's h values and its position in q) and redone by
+// all 64 lanes of the wave, one element each, rather than by a chunk-wide
+// branch that every lane of the wave executes whenever one lane needs it.
+// A wave lists at most kWaveFix chunks; any more are redone in place.
+constexpr int kWaveFix = 16;
+constexpr int kFixCap = NW * kWaveFix;
+constexpr int kFixStride = 12;                 // floats per entry: up to 8 h values, position
 // Code bits of h (its low byte is the int8 code) from the lower product; `split`
 // becomes nonzero when the two products round differently.  Both results are
 // 1.5 * 2^23 plus an integer of magnitude <= 128, so their low 16 bits differ
@@ -722,13 +730,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     //    statistics -> q -> every dot product), so their loads go out before
     //    any other address arithmetic; then the call's tag and the weight stream
     //    (a wave's loads complete in issue order)
-    // The launch generation first (K-split launches only): loads complete in
-    // issue order, so waiting for it later never waits for the activations or
-    // weights issued after it.  A launch that does not split K skips it: a
-    // device-scope load goes past the chiplet's L2, and the activation loads
-    // behind it (which mostly hit there) would wait for its round trip.
-    uint32_t gen = 0;
-    if (!ONE && a.S > 1) gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t wt = a.wtab[wv];
     const Act<XT, EPT> am = act_map<XT, EPT>(a, wt, lane);
     uint4 xr[NCH], ur[NCH];
@@ -771,6 +772,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         }
     }
 
+    // The launch generation (K-split launches only), after the activation
+    // loads: it is a device-scope round trip, and loads complete in issue
+    // order, so the activations must not queue behind it.  (The compiler waits
+    // for it right away; the K-split launches run on the MFMA path, which waits
+    // for its activations before the weight stream anyway.)
+    uint32_t gen = 0;
+    if (!ONE && a.S > 1) gen = __hip_atomic_load(&a.ws->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
     // work assignment: block (r, s) owns tiles [t_begin, t_end) of K-slice s;
     // wave wv works on tile group tg (every TW-th tile) and super-blocks
     // [kw * spw, (kw + 1) * spw) of the slice
@@ -793,6 +802,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     int8_t* q_l = reinterpret_cast<int8_t*>(lds + (CB ? 64 : 0));
     float* red_l = reinterpret_cast<float*>(q_l + (size_t)M * a.ks);
     float* gam_l = red_l + 2 * a.red_half;        // RMSNorm: the slice's gamma, KS floats
+    float* fix_l = gam_l + (PRO == PRO_RMSNORM ? a.KS : 0);   // chunks to redo, kFixCap entries
+    constexpr bool FIXLIST = !DBG && !CB && PRO != PRO_QIN;
     // the partials' padding entries must read as zero: clear both halves (the
     // first tile step's barrier orders this before any partial is written)
     for (int i = tid; i < a.red_half / 2; i += NT)
@@ -1070,9 +1081,43 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 for (int e = 0; e < E; ++e) b[i * E + e] = code_bits(h[i * E + e], inv_lo, inv_hi, split);
                 rare |= (split != 0 ? 1u : 0u) << i;
             }
+            // LDS order: in each 128-k super-block, octet 4j + h is stored at position
+            // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
+            // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
+            // is chunk 0's plus i whole super-blocks.
+            const int c0 = am.it;
+            const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
+            const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
+            const int pstep = am.tpr * E;
+            int nfix_w = 0;                                       // chunks this wave listed
+            float* const fix_w = fix_l + wv * (kWaveFix * kFixStride);
             if (__builtin_expect(sx < kMinCorrectedSx && sx > 0.0f, 0)) {
 #pragma unroll
                 for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
+            } else if (FIXLIST) {
+                // list this wave's chunks that need the corrected quotient: the
+                // entry index of a lane is the count of listing lanes below it
+#pragma unroll
+                for (int i = 0; i < NCH; ++i) {
+                    const uint64_t bal = __ballot((rare >> i) & 1u);
+                    if (bal) {
+                        const int idx = nfix_w + (int)__builtin_amdgcn_mbcnt_hi(
+                                                     (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                        if ((rare >> i) & 1u) {
+                            if (idx < kWaveFix) {
+                                float4* en = reinterpret_cast<float4*>(fix_w + idx * kFixStride);
+                                en[0] = make_float4(h[i * E], h[i * E + 1], h[i * E + 2], h[i * E + 3]);
+                                if (E == 8) en[1] = make_float4(h[i * E + 4 % E], h[i * E + 5 % E], h[i * E + 6 % E],
+                                                                h[i * E + 7 % E]);
+                                fix_w[idx * kFixStride + 8] = __int_as_float(pos0 + i * pstep);
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < E; ++e) b[i * E + e] = corrected_code_bits(h[i * E + e], sx, inv);
+                            }
+                        }
+                        nfix_w += (int)__builtin_popcountll(bal);
+                    }
+                }
             } else if (__builtin_expect(rare != 0, 0)) {
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
@@ -1085,14 +1130,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             uint32_t pk[NCH * E / 4];
 #pragma unroll
             for (int w = 0; w < NCH * E / 4; ++w) pk[w] = pack_low_bytes(b[4 * w], b[4 * w + 1], b[4 * w + 2], b[4 * w + 3]);
-            // LDS order: in each 128-k super-block, octet 4j + h is stored at position
-            // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
-            // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
-            // is chunk 0's plus i whole super-blocks.
-            const int c0 = am.it;
-            const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
-            const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
-            const int pstep = am.tpr * E;
 #pragma unroll
             for (int i = 0; i < NCH; ++i) {
                 const uint32_t* pc = pk + i * (E / 4);
@@ -1118,6 +1155,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pc[0];
                         else *reinterpret_cast<uint2*>(dst) = make_uint2(pc[0], pc[E / 4 - 1]);
                     }
+                }
+            }
+            if (FIXLIST && nfix_w > 0) {
+                // the listed chunks, element by element over the wave's lanes,
+                // written over the codes stored above (a wave's LDS operations
+                // complete in order)
+                const int nel = min(nfix_w, kWaveFix) * E;
+                for (int t = lane; t < nel; t += 64) {
+                    const float* en = fix_w + (t / E) * kFixStride;
+                    const uint32_t cbits = corrected_code_bits(en[t % E], sx, inv);
+                    q_l[am.m * a.ks + __float_as_int(en[8]) + t % E] = (int8_t)cbits;
                 }
             }
             if (DBG && a.q_out && r == 0) {          // debug export of q

@@ -262,6 +262,59 @@ def test_near_tie_activations_bit_exact(m):
     assert np.array_equal(sx.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
 
 
+def tie_heavy_rows(seed, m, k):
+    """Rows whose quotients h / sx sit on half-integers (before sx is rounded)
+    at many elements.  Even rows: absmax 254/128 with every other element an odd
+    multiple of 1/128 in [1, 2), so 127 h / absmax = (odd) / 2 for about half
+    the row (more such chunks than the kernels list per workgroup); odd rows:
+    N(0, 1) with about 100 elements set to +-absmax / 2.  Every value is exact
+    in bf16."""
+    rng = np.random.default_rng(seed)
+    h = S.activations(seed + 1, m, k)
+    for r in range(m):
+        if r % 2 == 0:
+            h[r] = rng.uniform(-0.99, 0.99, k).astype(F32)
+            h[r, 0] = F32(254.0 / 128.0)
+            idx = rng.choice(np.arange(1, k), k // 2, replace=False)
+            odd = 2 * rng.integers(64, 127, size=idx.size) + 1            # 129 .. 253
+            h[r, idx] = (odd / 128.0 * np.where(rng.random(idx.size) < 0.5, 1, -1)).astype(F32)
+        else:
+            amx = np.abs(h[r]).max()
+            idx = rng.choice(k, 100, replace=False)
+            h[r, idx] = (amx / 2.0 * np.where(rng.random(100) < 0.5, 1, -1)).astype(F32)
+    return O.bf16_to_f32(S.to_bf16_bits(h))
+
+
+@pytest.mark.parametrize("xt", ["f32", "bf16"])
+@pytest.mark.parametrize("m,split", [(1, 0), (2, 0), (8, 0), (8, 2)])
+def test_tie_heavy_rows_production_equals_debug(xt, m, split):
+    """Chunks whose codes need the corrected quotient: the production kernels list
+    them and redo them after the quantiser (more of them than the list holds are
+    redone in place); the debug instances redo every one in place.  q and sx are
+    checked against the oracle on the debug run, and the production y must equal
+    the debug y bit for bit."""
+    n, k, g = 400, 2048, 32
+    w, buf = gpu_weight(0, n, k, g, 41)
+    sk.sk_repack_w4a8(w)
+    h = tie_heavy_rows(42 + m, 8, k)[:m]
+    # row 0 alone has more half-integer quotients than one workgroup's list holds
+    sx0 = np.float32(np.abs(h[0]).max() / np.float32(127.0))
+    quot = h[0].astype(np.float64) / float(sx0)
+    assert np.count_nonzero(np.abs(np.abs(quot - np.trunc(quot)) - 0.5) < 1e-4) > 256
+    h_dev, h_ref = to_dev(np.ascontiguousarray(h), xt)
+    sk.set_split(split)
+    try:
+        y_dbg, ref = check_call(w, buf, 0, n, k, g, h_dev, h_ref, m)
+        y, yt = sentinel_out((m, n), torch.float32)
+        ws = sk.Workspace(sk.gemm_workspace_size(n, k, g, sk.SK_W4_SYM, m)) if split else None
+        sk.sk_gemm_w4a8(w, h_dev, y=y, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        sk.set_split(0)
+    assert_tails_untouched(yt)
+    assert torch.equal(y, y_dbg), (xt, m, split)
+
+
 def test_rows_do_not_interact_and_runs_repeat():
     n, k, g = 512, 2048, 32
     w, buf = gpu_weight(0, n, k, g, 31)
