@@ -82,7 +82,7 @@ int workgroups_per_slice(int cus, int S, int T) {
 // budget for the prologue).  An RMSNorm launch also keeps the slice's gamma in LDS.
 Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pro) {
     Plan p;
-    const int pipe = pipe_of(m == 1 && G.fmt != FMT_CB);
+    const int pipe = pipe_of(m == 1 && G.fmt != FMT_CB, G.fmt == FMT_CB);
     const int KB = (int)G.KB;
     const int T = (int)G.T;
     const bool cb = G.fmt == FMT_CB;

@@ -54,13 +54,13 @@ constexpr int NT = NW * 64;    // threads per workgroup
 // how many of them each wave issues before the activation prologue, for the
 // v_dot4 instances (M = 1) and the MFMA instances (M >= 2, the codebook).
 #ifndef SK_PIPE_DOT4
-#define SK_PIPE_DOT4 4
+#define SK_PIPE_DOT4 5
 #endif
 #ifndef SK_PRIME_DOT4
 #define SK_PRIME_DOT4 2
 #endif
 #ifndef SK_PIPE_MFMA
-#define SK_PIPE_MFMA 4
+#define SK_PIPE_MFMA 5
 #endif
 #ifndef SK_PRIME_MFMA
 #define SK_PRIME_MFMA 2
@@ -70,7 +70,9 @@ constexpr int NT = NW * 64;    // threads per workgroup
 #endif
 constexpr int kPipeDot4 = SK_PIPE_DOT4, kPrimeDot4 = SK_PRIME_DOT4;
 constexpr int kPipeMfma = SK_PIPE_MFMA, kPrimeMfma = SK_PRIME_MFMA;
-constexpr int pipe_of(bool dot4) { return dot4 ? kPipeDot4 : kPipeMfma; }
+// The codebook keeps 4 (its G = 16 scales take two registers more per slot).
+constexpr int kPipeCb = 4;
+constexpr int pipe_of(bool dot4, bool cb) { return cb ? kPipeCb : dot4 ? kPipeDot4 : kPipeMfma; }
 constexpr int SMAX = 32;       // largest number of K-slices
 // Tile-epilogue LDS: per half, [tile group][row][column][kwp] floats, kwp =
 // the k-parts per tile group rounded up to 4, 8 or 16 (the entries past KW
@@ -706,7 +708,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : (PRO == PRO_NONE || ONE) ? (WIDE ? 40 : 32) : 16;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
-    constexpr int PIPE = DOT4 ? kPipeDot4 : kPipeMfma;
+    constexpr int PIPE = pipe_of(DOT4, CB);
     constexpr int PRIME = DOT4 ? kPrimeDot4 : kPrimeMfma;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
