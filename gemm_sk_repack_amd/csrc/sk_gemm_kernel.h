@@ -1066,7 +1066,74 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 
         // quantise this slice into LDS (straight-line code: it runs once per
         // launch, so every instruction of it is a cold instruction-cache fetch)
-        if (am.nw > 0) {
+        // LDS order of q: in each 128-k super-block, octet 4j + h is stored at
+        // position 4h + j, so a lane's four octets are contiguous.  Chunk i of a
+        // thread is TPR chunks (a multiple of 128 elements) after chunk 0, so its
+        // position is chunk 0's plus i whole super-blocks.
+        const int c0 = am.it;
+        const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
+        const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
+        const int pstep = am.tpr * E;
+        if (FIXLIST && am.nw > 0) {
+            // One chunk at a time: its codes from the bracketing products, then
+            // (if an element's products round apart) a place in the wave's list
+            // of chunks to redo, then its store, so only one chunk's codes are
+            // live at a time.  A wave holds one activation row, so sx and the
+            // tiny-scale branch are wave-uniform.
+            const float inv_lo = inv * kInvLo, inv_hi = inv * kInvHi;
+            const bool tiny = sx < kMinCorrectedSx && sx > 0.0f;
+            int nfix_w = 0;                                       // chunks this wave listed
+            float* const fix_w = fix_l + wv * (kWaveFix * kFixStride);
+#pragma unroll
+            for (int i = 0; i < NCH; ++i) {
+                uint32_t bc[E];
+                uint32_t split = 0;
+#pragma unroll
+                for (int e = 0; e < E; ++e) bc[e] = code_bits(h[i * E + e], inv_lo, inv_hi, split);
+                if (__builtin_expect(tiny, 0)) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) bc[e] = __float_as_uint(h[i * E + e] / sx + kRoundMagic);
+                } else {
+                    const bool redo = split != 0;
+                    const uint64_t bal = __ballot(redo);
+                    if (bal) {
+                        const int idx = nfix_w + (int)__builtin_amdgcn_mbcnt_hi(
+                                                     (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                        if (redo) {
+                            if (idx < kWaveFix) {
+                                float4* en = reinterpret_cast<float4*>(fix_w + idx * kFixStride);
+                                en[0] = make_float4(h[i * E], h[i * E + 1], h[i * E + 2], h[i * E + 3]);
+                                if (E == 8) en[1] = make_float4(h[i * E + 4 % E], h[i * E + 5 % E], h[i * E + 6 % E],
+                                                                h[i * E + 7 % E]);
+                                fix_w[idx * kFixStride + 8] = __int_as_float(pos0 + i * pstep);
+                            } else {
+#pragma unroll
+                                for (int e = 0; e < E; ++e) bc[e] = corrected_code_bits(h[i * E + e], sx, inv);
+                            }
+                        }
+                        nfix_w += (int)__builtin_popcountll(bal);
+                    }
+                }
+                int8_t* dst = q_l + am.m * a.ks + pos0 + i * pstep;
+                if (i < am.nw && chunk_of(am, i) < am.cpr) {
+                    if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pack_low_bytes(bc[0], bc[1], bc[2], bc[3]);
+                    else *reinterpret_cast<uint2*>(dst) = make_uint2(pack_low_bytes(bc[0], bc[1], bc[2], bc[3]),
+                                                                     pack_low_bytes(bc[4 % E], bc[5 % E], bc[6 % E],
+                                                                                    bc[7 % E]));
+                }
+            }
+            if (nfix_w > 0) {
+                // the listed chunks, element by element over the wave's lanes,
+                // written over the codes stored above (a wave's LDS operations
+                // complete in order)
+                const int nel = min(nfix_w, kWaveFix) * E;
+                for (int t = lane; t < nel; t += 64) {
+                    const float* en = fix_w + (t / E) * kFixStride;
+                    const uint32_t cbits = corrected_code_bits(en[t % E], sx, inv);
+                    q_l[am.m * a.ks + __float_as_int(en[8]) + t % E] = (int8_t)cbits;
+                }
+            }
+        } else if (am.nw > 0) {
             // Codes of all elements from the bracketing products, noting the chunks
             // that hold an element whose products round apart.  Such elements are
             // common (with bf16 data most rows have some), so their chunks are
@@ -1083,43 +1150,9 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 for (int e = 0; e < E; ++e) b[i * E + e] = code_bits(h[i * E + e], inv_lo, inv_hi, split);
                 rare |= (split != 0 ? 1u : 0u) << i;
             }
-            // LDS order: in each 128-k super-block, octet 4j + h is stored at position
-            // 4h + j, so a lane's four octets are contiguous.  Chunk i of a thread is
-            // TPR chunks (a multiple of 128 elements) after chunk 0, so its position
-            // is chunk 0's plus i whole super-blocks.
-            const int c0 = am.it;
-            const int o0 = (c0 * E) >> 3, ow0 = o0 & 15;
-            const int pos0 = (o0 >> 4) * 128 + ((ow0 & 3) * 4 + (ow0 >> 2)) * 8 + ((c0 * E) & 7);
-            const int pstep = am.tpr * E;
-            int nfix_w = 0;                                       // chunks this wave listed
-            float* const fix_w = fix_l + wv * (kWaveFix * kFixStride);
             if (__builtin_expect(sx < kMinCorrectedSx && sx > 0.0f, 0)) {
 #pragma unroll
                 for (int j = 0; j < NCH * E; ++j) b[j] = __float_as_uint(h[j] / sx + kRoundMagic);
-            } else if (FIXLIST) {
-                // list this wave's chunks that need the corrected quotient: the
-                // entry index of a lane is the count of listing lanes below it
-#pragma unroll
-                for (int i = 0; i < NCH; ++i) {
-                    const uint64_t bal = __ballot((rare >> i) & 1u);
-                    if (bal) {
-                        const int idx = nfix_w + (int)__builtin_amdgcn_mbcnt_hi(
-                                                     (uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                        if ((rare >> i) & 1u) {
-                            if (idx < kWaveFix) {
-                                float4* en = reinterpret_cast<float4*>(fix_w + idx * kFixStride);
-                                en[0] = make_float4(h[i * E], h[i * E + 1], h[i * E + 2], h[i * E + 3]);
-                                if (E == 8) en[1] = make_float4(h[i * E + 4 % E], h[i * E + 5 % E], h[i * E + 6 % E],
-                                                                h[i * E + 7 % E]);
-                                fix_w[idx * kFixStride + 8] = __int_as_float(pos0 + i * pstep);
-                            } else {
-#pragma unroll
-                                for (int e = 0; e < E; ++e) b[i * E + e] = corrected_code_bits(h[i * E + e], sx, inv);
-                            }
-                        }
-                        nfix_w += (int)__builtin_popcountll(bal);
-                    }
-                }
             } else if (__builtin_expect(rare != 0, 0)) {
 #pragma unroll
                 for (int i = 0; i < NCH; ++i) {
@@ -1157,17 +1190,6 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                         if (E == 4) *reinterpret_cast<uint32_t*>(dst) = pc[0];
                         else *reinterpret_cast<uint2*>(dst) = make_uint2(pc[0], pc[E / 4 - 1]);
                     }
-                }
-            }
-            if (FIXLIST && nfix_w > 0) {
-                // the listed chunks, element by element over the wave's lanes,
-                // written over the codes stored above (a wave's LDS operations
-                // complete in order)
-                const int nel = min(nfix_w, kWaveFix) * E;
-                for (int t = lane; t < nel; t += 64) {
-                    const float* en = fix_w + (t / E) * kFixStride;
-                    const uint32_t cbits = corrected_code_bits(en[t % E], sx, inv);
-                    q_l[am.m * a.ks + __float_as_int(en[8]) + t % E] = (int8_t)cbits;
                 }
             }
             if (DBG && a.q_out && r == 0) {          // debug export of q
