@@ -68,6 +68,10 @@ constexpr int NT = NW * 64;    // threads per workgroup
 #ifndef SK_MFMA_ACT_FIRST
 #define SK_MFMA_ACT_FIRST 1
 #endif
+// G = 32 scales on the v_dot4 path: one per lane (1), or the row's four (0)
+#ifndef SK_SCALE1
+#define SK_SCALE1 1
+#endif
 constexpr int kPipeDot4 = SK_PIPE_DOT4, kPrimeDot4 = SK_PRIME_DOT4;
 constexpr int kPipeMfma = SK_PIPE_MFMA, kPrimeMfma = SK_PRIME_MFMA;
 // The codebook keeps 4 (its G = 16 scales take two registers more per slot).
@@ -691,6 +695,10 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     __shared__ Smem sm;
     constexpr bool CB = FMT == FMT_CB;          // codebook levels instead of integer weights
     constexpr int NG = (GS == 0) ? 8 : 4 / GS;  // groups per super-block (GS = 0: G = 16)
+    // G = 32 on the v_dot4 path: one 4-byte scale load per lane per slot instead
+    // of the row's four (16 bytes, the same for the four lanes of a column); the
+    // lanes trade block sums instead (see the v_dot4 step of `process`)
+    constexpr bool SCALE1 = SK_SCALE1 && NG == 4 && DOT4 && !CB;
     // The weight bytes fed to the dot products hold w scaled by 16 (W4: the
     // nibble in the byte's top half) or 4 (W6: the 6 bits in the top of the
     // byte), so sign extension is free; the sums are scaled back at the store.
@@ -914,6 +922,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                                  __builtin_nontemporal_load(sp + 2), __builtin_nontemporal_load(sp + 3));
                 sv2 = make_float4(__builtin_nontemporal_load(sp + 4), __builtin_nontemporal_load(sp + 5),
                                   __builtin_nontemporal_load(sp + 6), __builtin_nontemporal_load(sp + 7));
+            } else if (NG == 4 && SCALE1) {
+                sv = make_float4(__builtin_nontemporal_load(sp + hl), 0.0f, 0.0f, 0.0f);
             } else if (NG == 4) {
                 sv = make_float4(__builtin_nontemporal_load(sp), __builtin_nontemporal_load(sp + 1),
                                  __builtin_nontemporal_load(sp + 2), __builtin_nontemporal_load(sp + 3));
@@ -937,6 +947,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                 sv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, so, 0, kStreamPolicy));
                 sv2 = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, on ? so + 16 : kOutside, 0,
                                                                                        kStreamPolicy));
+            } else if (NG == 4 && SCALE1) {
+                // one scale per lane, s[row nl][block hl]
+                sv = make_float4(__builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                               grs, on ? so + 4 * hl : kOutside, 0, kStreamPolicy)),
+                                 0.0f, 0.0f, 0.0f);
             } else if (NG == 4) {
                 sv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(grs, so, 0, kStreamPolicy));
             } else if (NG == 2) {
@@ -1332,7 +1347,21 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                     pg[gi] = 0;
 #pragma unroll
                     for (int jj = 0; jj < GS; ++jj) pg[gi] += part[gi * GS + jj];
-                    acc[0] = __builtin_fmaf(sv[gi], (float)pg[gi], acc[0]);
+                }
+                if (SCALE1) {
+                    // Transpose-reduce over the four 16-lane rows (lane swaps
+                    // move whole rows, so every lane keeps its column nl): lane
+                    // (nl, hl) ends with the sum of block hl's four octets for
+                    // row nl and needs one scale, s[nl][hl], the one it loaded.
+                    // Rows 0-1 and 2-3 trade blocks 2-3 for 0-1 and add; then
+                    // odd and even rows trade and add.
+                    const auto x02 = __builtin_amdgcn_permlane32_swap((uint32_t)pg[0], (uint32_t)pg[2], false, false);
+                    const auto x13 = __builtin_amdgcn_permlane32_swap((uint32_t)pg[1], (uint32_t)pg[3], false, false);
+                    const auto y = __builtin_amdgcn_permlane16_swap(x02[0] + x02[1], x13[0] + x13[1], false, false);
+                    acc[0] = __builtin_fmaf(sv[0], (float)(int)(y[0] + y[1]), acc[0]);
+                } else {
+#pragma unroll
+                    for (int gi = 0; gi < NG; ++gi) acc[0] = __builtin_fmaf(sv[gi], (float)pg[gi], acc[0]);
                 }
                 if (DBG && a.p_out) {        // debug export: this lane's share of each group partial
                     if (row_ok) {
