@@ -72,6 +72,11 @@ constexpr int NT = NW * 64;    // threads per workgroup
 #ifndef SK_SCALE1
 #define SK_SCALE1 1
 #endif
+// The rest of the first load group issued one slot per quantised chunk (1: on
+// the MFMA path, 2: on the v_dot4 path too), or all of it after the quantiser (0)
+#ifndef SK_REST_IN_Q
+#define SK_REST_IN_Q 1
+#endif
 constexpr int kPipeDot4 = SK_PIPE_DOT4, kPrimeDot4 = SK_PRIME_DOT4;
 constexpr int kPipeMfma = SK_PIPE_MFMA, kPrimeMfma = SK_PRIME_MFMA;
 // The codebook keeps 4 (its G = 16 scales take two registers more per slot).
@@ -699,6 +704,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // of the row's four (16 bytes, the same for the four lanes of a column); the
     // lanes trade block sums instead (see the v_dot4 step of `process`)
     constexpr bool SCALE1 = SK_SCALE1 && NG == 4 && DOT4 && !CB;
+    constexpr bool REST_IN_Q = SK_REST_IN_Q && !CB && (SK_REST_IN_Q > 1 || !DOT4);
     // The weight bytes fed to the dot products hold w scaled by 16 (W4: the
     // nibble in the byte's top half) or 4 (W6: the 6 bits in the top of the
     // byte), so sign extension is free; the sums are scaled back at the store.
@@ -976,6 +982,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     float4 sbuf[PIPE], sbuf2[PIPE];
 #pragma unroll
     for (int d = 0; d < PRIME; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+    bool rest_done = false;
 
     // 2. activation prologue: per-row statistics of h, then q into LDS
     if (!ONE && a.S > 1 && tid == 0) sm.tag = gen + 1u;
@@ -1136,6 +1143,16 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
                                                                      pack_low_bytes(bc[4 % E], bc[5 % E], bc[6 % E],
                                                                                     bc[7 % E]));
                 }
+                // one more slot of the first group after each chunk but the last:
+                // the address unit is idle while the quantiser runs, and a burst
+                // of loads here would hold the waves at issue
+                if (REST_IN_Q && PRIME + i < PIPE && i + 1 < NCH)
+                    load_slot(PRIME + i, wbuf[PRIME + i], hbuf[PRIME + i], sbuf[PRIME + i], sbuf2[PRIME + i]);
+            }
+            if (REST_IN_Q) {
+#pragma unroll
+                for (int d = PRIME + NCH - 1; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+                rest_done = true;
             }
             if (nfix_w > 0) {
                 // the listed chunks, element by element over the wave's lanes,
@@ -1220,12 +1237,15 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
             }
         }
     }
-    // The rest of the first group's loads and the next group's cursor go out
-    // before the workgroup waits for q: waves without activations get there
-    // first and, with the loop set-up after them, bring that code into the
-    // instruction cache (empty at every launch) while the others quantise.
+    // The rest of the first group's loads (unless the quantiser issued them) and
+    // the next group's cursor go out before the workgroup waits for q: waves
+    // without activations get there first and, with the loop set-up after them,
+    // bring that code into the instruction cache (empty at every launch) while
+    // the others quantise.
+    if (!rest_done) {
 #pragma unroll
-    for (int d = PRIME; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+        for (int d = PRIME; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+    }
     group_next();
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
