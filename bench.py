@@ -266,10 +266,11 @@ def probe_us(torch, sk, stream, bufs, out):
 def instance_of(sk, n, k, m, xt):
     """(key, template-argument pattern) of the kernel instance a W4 G=32 call runs."""
     p = sk.gemm_plan(n, k, GROUP, sk.SK_W4_SYM, m)
-    dot4, wide = m == 1, bool(p["wide"])
-    key = f"{'dot4' if dot4 else 'mfma'}_{'wide' if wide else 'narrow'}"
+    dot4, wide, pipe4 = m == 1, bool(p["wide"]), p["pipe"] == 4
+    key = f"{'dot4' if dot4 else 'mfma'}_{'wide' if wide else 'narrow'}{'_pipe4' if pipe4 else ''}"
+    # the last template argument: 4 for the 4-slot pipeline instances, else 0
     pat = (r"gemm_kernel<0, 0, " + str(xt) + r", \d+, " + ("true" if dot4 else "false")
-           + r", false, false, " + ("true" if wide else "false") + ">")
+           + r", false, false, " + ("true" if wide else "false") + (", 4>" if pipe4 else ", 0>"))
     return key, pat
 
 

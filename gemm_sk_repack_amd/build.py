@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libsk_repack.so")
 SOURCES = ["sk_api.hip", "sk_repack.hip", "sk_gemm.hip",
-           "sk_gemm_w4.hip", "sk_gemm_w6.hip", "sk_gemm_cb.hip",
+           "sk_gemm_w4.hip", "sk_gemm_w4_pipe4.hip", "sk_gemm_w6.hip", "sk_gemm_cb.hip",
            "sk_gemm_w4_dbg.hip", "sk_gemm_w6_dbg.hip", "sk_gemm_cb_dbg.hip",
            "sk_gemm_split.hip", "sk_attention.hip", "sk_mtp.cpp"]
 ARCH = "gfx950"

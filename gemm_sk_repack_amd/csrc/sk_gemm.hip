@@ -95,16 +95,19 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     // its wave split (two halves of TW tile groups x M x 16 outputs x kwp), for
     // RMSNorm the slice's gamma, and (integer formats) the quantiser's list of
     // chunks to redo
-    auto lds_of = [&](int s) {
+    auto lds_for = [&](int s, int kw, int tw) {
         const size_t KS = (size_t)(G.k / s);
-        const int R = workgroups_per_slice(cus, s, T);
-        int kw, tw;
-        split_waves(KB / s, (T + R - 1) / R, m, (s > 1) ? NW - 1 : NW, pipe, kw, tw);
         const size_t red = 2 * 4 * (size_t)tw * m * 16 * red_kwp(kw);
         const size_t gam = (pro == PRO_RMSNORM) ? 4 * KS : 0;     // RMSNorm: the slice's gamma
         if (cb) return 64 + (size_t)m * (2 * KS + 64) + red + gam;   // levels, bf16 q, partials
         const size_t fix = (size_t)kFixCap * kFixStride * 4;         // list of chunks to redo
         return (size_t)m * (KS + 32) + red + gam + fix;
+    };
+    auto lds_of = [&](int s) {
+        const int R = workgroups_per_slice(cus, s, T);
+        int kw, tw;
+        split_waves(KB / s, (T + R - 1) / R, m, (s > 1) ? NW - 1 : NW, pipe, kw, tw);
+        return lds_for(s, kw, tw);
     };
     const size_t kLdsMax = 150 * 1024;
     auto valid = [&](int s) { return s >= 1 && s <= SMAX && KB % s == 0 && fits(s) && lds_of(s) <= kLdsMax; };
@@ -142,7 +145,24 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     const int R = (S > 0) ? workgroups_per_slice(cus, S, T) : 1;
     p.R = R;
     // with S > 1 one wave is reserved for the exchange
-    split_waves(p.KBs, (T + R - 1) / R, m, (S > 1) ? NW - 1 : NW, pipe, p.KW, p.TW);
+    const int nwa = (S > 1) ? NW - 1 : NW;
+    const int64_t slots = split_waves(p.KBs, (T + R - 1) / R, m, nwa, pipe, p.KW, p.TW);
+    p.pipe = pipe;
+    // 4-bit weights without a prologue also have instances with a 4-slot
+    // pipeline: taken where its wave split pads at least a tenth fewer slots
+    // (e.g. 4 or 12 super-blocks per wave, where 5 slots would carry a stand-in
+    // in every group; a smaller saving was measured to be a loss at M = 8).
+    // The split path's q-input launches keep the same wave split, so their sums
+    // stay in the same order.
+    if (G.fmt == FMT_W4 && (pro == PRO_NONE || pro == PRO_QIN) && pipe != 4 && S > 0) {
+        int kw4 = 1, tw4 = 1;
+        const int64_t slots4 = split_waves(p.KBs, (T + R - 1) / R, m, nwa, 4, kw4, tw4);
+        if (slots4 * 10 <= slots * 9 && lds_for(S, kw4, tw4) <= kLdsMax) {
+            p.KW = kw4;
+            p.TW = tw4;
+            p.pipe = 4;
+        }
+    }
     p.spw = p.KW > 0 ? p.KBs / p.KW : 0;
     p.P = S * R;
     p.ks = cb ? 2 * p.KS + 64 : p.KS + 32;
@@ -154,7 +174,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     }
     p.kwp = red_kwp(p.KW);
     p.red_half = p.TW * m * 16 * p.kwp;
-    p.lds = (S > 0) ? lds_of(S) : 0;
+    p.lds = (S > 0) ? lds_for(S, p.KW, p.TW) : 0;
     p.part_floats = (S > 1) ? (size_t)T * S * m * 16 : 0;
     p.ok = valid(S) && p.KBs >= 1 && p.spw >= 1 && p.P >= 1 && m >= 1 && m <= 8;
     return p;
@@ -235,8 +255,12 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     const bool dot4 = (c.m == 1) && G.fmt != FMT_CB;
     const int gs = (int)(G.g / 32);                // 0 for the codebook's G = 16
     const bool dbg = c.q_out || c.sx_out || c.p_out;
+    // the plan's pipeline depth is a performance choice: an instance of any
+    // depth computes the same sums for the same wave split
     KernelFn fn = c.canon ? pick_kernel_split(c.prologue, c.xt, gs, dot4, p.wide)
-                          : pick(G.fmt, c.prologue, c.xt, gs, dot4, dbg, p.wide);
+                  : (p.pipe == 4 && !dbg && G.fmt == FMT_W4 && c.prologue == PRO_NONE)
+                      ? pick_kernel_w4_pipe4(c.xt, gs, dot4, p.wide)
+                      : pick(G.fmt, c.prologue, c.xt, gs, dot4, dbg, p.wide);
     if (!fn) return hipErrorInvalidValue;
 
     KArgs a;

@@ -176,6 +176,8 @@ KernelFn pick_kernel_w4_dbg(int pro, int xt, int gs, bool dot4, bool wide);
 KernelFn pick_kernel_w6_dbg(int pro, int xt, int gs, bool dot4, bool wide);
 KernelFn pick_kernel_cb_dbg(int pro, int xt, int gs, bool dot4, bool wide);
 KernelFn pick_kernel_split(int pro, int xt, int gs, bool dot4, bool wide);
+// 4-bit weights, no prologue, production: the instances with a 4-slot pipeline
+KernelFn pick_kernel_w4_pipe4(int xt, int gs, bool dot4, bool wide);
 
 namespace {
 
@@ -694,7 +696,7 @@ __device__ inline float out_value(const KArgs& a, const Smem& sm, int ot, int om
 // the kernel
 // --------------------------------------------------------------------------
 
-template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG, bool CANON, bool WIDE>
+template <int FMT, int PRO, int XT, int GS, bool DOT4, bool DBG, bool CANON, bool WIDE, int PD>
 __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     extern __shared__ __align__(16) uint8_t lds[];
     __shared__ Smem sm;
@@ -722,7 +724,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     constexpr int EPT = DOT4 ? (WIDE ? 24 : 16) : (PRO == PRO_NONE || ONE) ? (WIDE ? 40 : 32) : 16;
     constexpr int E = Act<XT, EPT>::E;
     constexpr int NCH = Act<XT, EPT>::NCH;
-    constexpr int PIPE = pipe_of(DOT4, CB);
+    constexpr int PIPE = PD ? PD : pipe_of(DOT4, CB);   // PD: a depth other than the path's own
     constexpr int PRIME = DOT4 ? kPrimeDot4 : kPrimeMfma;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1583,20 +1585,20 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
 template <int FMT, int PRO, int XT, int GS, bool DBG>
 KernelFn pick_dot(bool dot4, bool wide) {
     if constexpr (FMT == FMT_CB) {
-        return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;   // the codebook runs on MFMA for every M
+        return gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false, 0>;   // the codebook runs on MFMA for every M
     } else if constexpr (PRO == PRO_NONE) {
         if (dot4)
-            return wide ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, true>
-                        : gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>;
-        return wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true>
-                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
+            return wide ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, true, 0>
+                        : gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false, 0>;
+        return wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true, 0>
+                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false, 0>;
     } else if constexpr (PRO == PRO_RMSNORM && FMT == FMT_W4) {
-        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>
-               : wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true>
-                      : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false, 0>
+               : wide ? gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, true, 0>
+                      : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false, 0>;
     } else {
-        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false>
-                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false>;
+        return dot4 ? gemm_kernel<FMT, PRO, XT, GS, true, DBG, false, false, 0>
+                    : gemm_kernel<FMT, PRO, XT, GS, false, DBG, false, false, 0>;
     }
 }
 template <int FMT, int PRO, int XT, bool DBG>
@@ -1614,17 +1616,39 @@ template <int FMT, int PRO, bool DBG>
 KernelFn pick_xt(int xt, int gs, bool dot4, bool wide) {
     return xt == 1 ? pick_gs<FMT, PRO, 1, DBG>(gs, dot4, wide) : pick_gs<FMT, PRO, 0, DBG>(gs, dot4, wide);
 }
+// 4-bit weights without a prologue and a pipeline of PD slots (the planner's
+// choice where PD divides a wave's super-blocks per tile and the default does not)
+template <int PD, int XT, int GS>
+KernelFn pick_pipe_dot(bool dot4, bool wide) {
+    if (dot4)
+        return wide ? gemm_kernel<FMT_W4, PRO_NONE, XT, GS, true, false, false, true, PD>
+                    : gemm_kernel<FMT_W4, PRO_NONE, XT, GS, true, false, false, false, PD>;
+    return wide ? gemm_kernel<FMT_W4, PRO_NONE, XT, GS, false, false, false, true, PD>
+                : gemm_kernel<FMT_W4, PRO_NONE, XT, GS, false, false, false, false, PD>;
+}
+template <int PD>
+KernelFn pick_pipe(int xt, int gs, bool dot4, bool wide) {
+    switch (gs * 2 + (xt == 1 ? 1 : 0)) {
+        case 2: return pick_pipe_dot<PD, 0, 1>(dot4, wide);
+        case 3: return pick_pipe_dot<PD, 1, 1>(dot4, wide);
+        case 4: return pick_pipe_dot<PD, 0, 2>(dot4, wide);
+        case 5: return pick_pipe_dot<PD, 1, 2>(dot4, wide);
+        case 8: return pick_pipe_dot<PD, 0, 4>(dot4, wide);
+        case 9: return pick_pipe_dot<PD, 1, 4>(dot4, wide);
+        default: return nullptr;
+    }
+}
 // The split path's kernels: 4-bit weights in the canonical layout, either
 // quantising x in the launch (PRO_NONE) or reading q from memory (PRO_QIN,
 // which has no activation budget).
 template <int PRO, int XT, int GS>
 KernelFn pick_canon_dot(bool dot4, bool wide) {
     if constexpr (PRO == PRO_NONE) {
-        if (!dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, true>;
-        if (dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, true>;
+        if (!dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, true, 0>;
+        if (dot4 && wide) return gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, true, 0>;
     }
-    return dot4 ? gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, false>
-                : gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, false>;
+    return dot4 ? gemm_kernel<FMT_W4, PRO, XT, GS, true, false, true, false, 0>
+                : gemm_kernel<FMT_W4, PRO, XT, GS, false, false, true, false, 0>;
 }
 template <int PRO, int XT>
 KernelFn pick_canon_gs(int gs, bool dot4, bool wide) {

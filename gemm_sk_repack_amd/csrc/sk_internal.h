@@ -89,6 +89,7 @@ struct Plan {
     int ks;       // LDS row stride of q
     int kwp;      // k-parts per tile group rounded up to 4, 8 or 16 (tile-epilogue pitch)
     int red_half; // floats per half of the tile-epilogue partials buffer
+    int pipe;     // register-pipeline depth the wave split was chosen for
     size_t lds;   // dynamic LDS bytes
     size_t part_floats;  // workspace words (8 bytes) for slice partials
     bool ok;

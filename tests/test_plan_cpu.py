@@ -71,6 +71,14 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     else:
         fix = 256 * 12 * 4                                   # the quantiser's list of chunks to redo
         assert p["lds"] == m * (KS + 32) + red + gam + fix
+    # register-pipeline depth: 4 for the codebook; 4-bit weights without a
+    # prologue take 4 where that pads at least a tenth fewer slots than 5
+    if fmt == sk.SK_W4_CODEBOOK:
+        assert p["pipe"] == 4
+    elif fmt == sk.SK_W4_SYM and pro == sk.PRO_NONE:
+        assert p["pipe"] in (4, 5)
+    else:
+        assert p["pipe"] == 5
     if m == 1 and k <= 16384:
         assert S == 1                                        # no cross-slice merge at M = 1
     assert p["part_floats"] == (T * S * m * 16 if S > 1 else 0)
@@ -135,6 +143,17 @@ def test_forced_split_hook_validates():
 def test_wide_budget_where_measured_faster(n, k, m, S, wide):
     p = sk.gemm_plan(n, k, 32, 0, m)
     assert (p["S"], p["wide"]) == (S, wide), p
+
+
+@pytest.mark.parametrize("n,k,m,pipe", [
+    (7168, 5120, 1, 5), (7168, 5120, 8, 5), (34816, 5120, 1, 5), (34816, 5120, 8, 5),
+    (5120, 17408, 1, 5), (5120, 17408, 8, 5), (6144, 4096, 1, 4), (6144, 4096, 8, 4),
+    (24576, 4096, 1, 4), (4096, 12288, 1, 4),
+])
+def test_pipeline_depth_where_measured_faster(n, k, m, pipe):
+    """27B-class shapes (5 or 17 super-blocks per wave): 5 slots; 9B-class (4, 6 or 8): 4."""
+    p = sk.gemm_plan(n, k, 32, sk.SK_W4_SYM, m)
+    assert p["pipe"] == pipe, p
 
 
 @pytest.mark.parametrize("m,wide", [(1, 0), (4, 0), (5, 1), (8, 1)])
