@@ -149,15 +149,17 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     const int64_t slots = split_waves(p.KBs, (T + R - 1) / R, m, nwa, pipe, p.KW, p.TW);
     p.pipe = pipe;
     // 4-bit weights without a prologue also have instances with a 4-slot
-    // pipeline: taken where its wave split pads at least a tenth fewer slots
-    // (e.g. 4 or 12 super-blocks per wave, where 5 slots would carry a stand-in
-    // in every group; a smaller saving was measured to be a loss at M = 8).
-    // The split path's q-input launches keep the same wave split, so their sums
-    // stay in the same order.
+    // pipeline: taken where its wave split pads fewer slots (e.g. 4 or 12
+    // super-blocks per wave, where 5 slots would carry a stand-in in every
+    // group); at M >= 2 only for a saving of at least a tenth (the 27B-class
+    // gate+up split, 24 slots instead of 25, was measured slower there and
+    // faster at M = 1).  The split path's q-input launches keep the same wave
+    // split, so their sums stay in the same order.
     if (G.fmt == FMT_W4 && (pro == PRO_NONE || pro == PRO_QIN) && pipe != 4 && S > 0) {
         int kw4 = 1, tw4 = 1;
         const int64_t slots4 = split_waves(p.KBs, (T + R - 1) / R, m, nwa, 4, kw4, tw4);
-        if (slots4 * 10 <= slots * 9 && lds_for(S, kw4, tw4) <= kLdsMax) {
+        const bool fewer = (m == 1) ? slots4 < slots : slots4 * 10 <= slots * 9;
+        if (fewer && lds_for(S, kw4, tw4) <= kLdsMax) {
             p.KW = kw4;
             p.TW = tw4;
             p.pipe = 4;
