@@ -65,8 +65,10 @@ constexpr int NT = NW * 64;    // threads per workgroup
 #ifndef SK_PRIME_MFMA
 #define SK_PRIME_MFMA 2
 #endif
+// M >= 2: a wave's first weight loads wait for its own activations (2), for
+// every wave's (1, a workgroup barrier), or go out at once (0)
 #ifndef SK_MFMA_ACT_FIRST
-#define SK_MFMA_ACT_FIRST 1
+#define SK_MFMA_ACT_FIRST 2
 #endif
 // G = 32 scales on the v_dot4 path: one per lane (1), or the row's four (0)
 #ifndef SK_SCALE1
@@ -973,11 +975,13 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     };
 
     // M >= 2 (more activation loads, and with S > 1 every slice's statistics
-    // gate the exchange): the weight stream starts once the activations are in,
-    // so their loads do not queue behind a burst of cold weight requests.
+    // gate the exchange): a wave's weight stream starts once its own
+    // activations are in, so they do not queue behind a burst of cold weight
+    // requests.  Waiting for the whole workgroup's (a barrier) was slower: the
+    // waves whose activations arrive first then sit idle.
     if (!DOT4 && SK_MFMA_ACT_FIRST) {
         __builtin_amdgcn_s_waitcnt(0xF70);    // vmcnt(0)
-        __syncthreads();
+        if (SK_MFMA_ACT_FIRST == 1) __syncthreads();
     }
     uint4 wbuf[PIPE];
     uint2 hbuf[PIPE];
