@@ -1248,11 +1248,17 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // without activations get there first and, with the loop set-up after them,
     // bring that code into the instruction cache (empty at every launch) while
     // the others quantise.
-    if (!rest_done) {
+    // On the v_dot4 path a wave whose whole share is one load group and that
+    // quantised issues that group's rest after the barrier instead: those loads
+    // queue behind the other waves' (issued right after the statistics), and
+    // the barrier would wait for the queue.  With more groups the wave's stream
+    // is long and the late start costs more than the barrier saves.
+    const bool late_rest = DOT4 && am.nw > 0 && !rest_done && jn * ngrp == 1;
+    if (!rest_done && !late_rest) {
 #pragma unroll
         for (int d = PRIME; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
     }
-    group_next();
+    if (!late_rest) group_next();
 
     // 3. stream the weights: a register pipeline of PIPE slots in flight
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1500,7 +1506,14 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     };
 
     for (int pj = 0; pj < jn; ++pj) {
-        if (pj == 0) __syncthreads();           // q (and sx) complete in LDS
+        if (pj == 0) {
+            __syncthreads();                    // q (and sx) complete in LDS
+            if (late_rest) {
+#pragma unroll
+                for (int d = PRIME; d < PIPE; ++d) load_slot(d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);
+                group_next();
+            }
+        }
         const bool pvalid = pj < jw;
         const int t = t_begin + tg + pj * a.TW;
         for (int pg = 0; pg < ngrp; ++pg) {
