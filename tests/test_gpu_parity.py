@@ -315,6 +315,28 @@ def test_tie_heavy_rows_production_equals_debug(xt, m, split):
     assert torch.equal(y, y_dbg), (xt, m, split)
 
 
+@pytest.mark.parametrize("n,k,m", [(4096, 12288, 1), (6144, 4096, 8), (2048, 12288, 2)])
+def test_pipeline_depths_sum_alike(n, k, m):
+    """Shapes whose plan takes the 4-slot pipeline with several slots per wave:
+    the production instance (4 slots per load group) and the debug instance (the
+    default 5) walk the same wave split in different groups, so their y must be
+    equal bit for bit; the debug run is checked against the oracle."""
+    p = sk.gemm_plan(n, k, 32, sk.SK_W4_SYM, m)
+    assert p["pipe"] == 4 and p["spw"] > 1, p
+    g = 32
+    w, buf = gpu_weight(0, n, k, g, 51 + m)
+    sk.sk_repack_w4a8(w)
+    h = S.activations(52 + m, m, k)
+    h_dev, h_ref = to_dev(h, "bf16")
+    y_dbg, ref = check_call(w, buf, 0, n, k, g, h_dev, h_ref, m)
+    y, yt = sentinel_out((m, n), torch.float32)
+    ws = sk.Workspace(sk.gemm_workspace_size(n, k, g, sk.SK_W4_SYM, m)) if p["S"] > 1 else None
+    sk.sk_gemm_w4a8(w, h_dev, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert_tails_untouched(yt)
+    assert torch.equal(y, y_dbg), (n, k, m)
+
+
 def test_rows_do_not_interact_and_runs_repeat():
     n, k, g = 512, 2048, 32
     w, buf = gpu_weight(0, n, k, g, 31)
