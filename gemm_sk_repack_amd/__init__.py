@@ -414,7 +414,7 @@ def sk_debug_gemm(w: QuantWeight, prologue: int, x: torch.Tensor, x2=None, gamma
 
 
 PLAN_FIELDS = ["S", "R", "P", "TW", "KW", "spw", "KBs", "KS", "WPR", "lds", "part_floats", "ept",
-               "wide", "pipe"]
+               "wide", "pipe", "srem"]
 
 
 def gemm_plan(n: int, k: int, group: int, fmt: int, m: int, cus: int = 256,

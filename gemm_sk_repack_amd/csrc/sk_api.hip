@@ -364,9 +364,9 @@ SK_EXPORT sk_status sk_test_gemm_plan(int n, int k, int group, int format, int m
         return SK_ERR_SHAPE;
     const Geom G = sk::make_geom(n, k, group, format);
     const sk::Plan p = sk::make_plan(G, m, prologue, cus, 0);
-    const int64_t v[14] = {p.S, p.R, p.P, p.TW, p.KW, p.spw, p.KBs, p.KS, p.WPR, (int64_t)p.lds,
-                           (int64_t)p.part_floats, p.ept, p.wide ? 1 : 0, p.pipe};
-    for (int i = 0; i < 14; ++i) fields[i] = v[i];
+    const int64_t v[15] = {p.S, p.R, p.P, p.TW, p.KW, p.spw, p.KBs, p.KS, p.WPR, (int64_t)p.lds,
+                           (int64_t)p.part_floats, p.ept, p.wide ? 1 : 0, p.pipe, p.srem};
+    for (int i = 0; i < 15; ++i) fields[i] = v[i];
     return p.ok ? SK_OK : SK_ERR_UNSUPPORTED;
 }
 

@@ -40,23 +40,24 @@ int g_split_override = 0;
 namespace {
 
 // Waves of a workgroup: TW tile groups x KW waves along k (KW divides the
-// slice's KBs super-blocks).  Each wave walks ceil(tiles / TW) tile steps of
-// KBs / KW super-blocks, in groups of `pipe` slots (a step's last group padded
-// with slots that load nothing); the split with the fewest slots per wave,
+// slice's KBs super-blocks, or with `uneven` the first KBs % KW k-parts take one
+// super-block more).  Each wave walks ceil(tiles / TW) tile steps of its k-part,
+// in groups of `pipe` slots (a step's last group padded with slots that load
+// nothing); the split with the fewest slots per wave (the longest k-part),
 // padding included (the register pipeline's round trips), wins, then the one
 // with the fewest real slots per wave, then the one with the fewest tile
 // steps (each ends with a workgroup barrier).  Returns the padded slots per wave.
-int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int pipe, int& KW, int& TW) {
+int64_t split_waves(int KBs, int tiles_per_wg, int m, int nwa, int pipe, bool uneven, int& KW, int& TW) {
     KW = 1;
     TW = 1;
     int64_t best_slots = -1, best_real = -1, best_steps = -1;
-    for (int kw = 1; kw <= nwa && KBs > 0; ++kw) {
-        if (KBs % kw != 0) continue;
+    for (int kw = 1; kw <= nwa && kw <= KBs; ++kw) {
+        if (!uneven && KBs % kw != 0) continue;
         int tw = nwa / kw;
         while (tw > 1 && tw * m * 16 > NT) --tw;      // the epilogue uses one thread per output
         if (tw > tiles_per_wg) tw = tiles_per_wg;
         const int64_t steps = (tiles_per_wg + tw - 1) / tw;
-        const int spw = KBs / kw;
+        const int spw = (KBs + kw - 1) / kw;              // the longest k-part
         const int64_t slots = steps * ((spw + pipe - 1) / pipe * pipe);   // padded to whole groups
         const int64_t real = steps * spw;
         if (best_slots < 0 || slots < best_slots || (slots == best_slots && real < best_real) ||
@@ -106,7 +107,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     auto lds_of = [&](int s) {
         const int R = workgroups_per_slice(cus, s, T);
         int kw, tw;
-        split_waves(KB / s, (T + R - 1) / R, m, (s > 1) ? NW - 1 : NW, pipe, kw, tw);
+        split_waves(KB / s, (T + R - 1) / R, m, (s > 1) ? NW - 1 : NW, pipe, s > 1, kw, tw);
         return lds_for(s, kw, tw);
     };
     const size_t kLdsMax = 150 * 1024;
@@ -129,7 +130,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
             const int R = workgroups_per_slice(cus, s, T);
             const int64_t tpw = (T + R - 1) / R;
             int kw, tw;
-            const int64_t slots = split_waves(KB / s, (int)tpw, m, NW - 1, pipe, kw, tw);
+            const int64_t slots = split_waves(KB / s, (int)tpw, m, NW - 1, pipe, true, kw, tw);
             // in units of 1/2048
             const int64_t cost = 8192 * slots + (int64_t)m * (G.k / s) + 128 * tpw * s * m +
                                  ((R & 7) ? 8192 * 24 : 0);
@@ -146,7 +147,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     p.R = R;
     // with S > 1 one wave is reserved for the exchange
     const int nwa = (S > 1) ? NW - 1 : NW;
-    const int64_t slots = split_waves(p.KBs, (T + R - 1) / R, m, nwa, pipe, p.KW, p.TW);
+    const int64_t slots = split_waves(p.KBs, (T + R - 1) / R, m, nwa, pipe, S > 1, p.KW, p.TW);
     p.pipe = pipe;
     // 4-bit weights without a prologue also have instances with a 4-slot
     // pipeline: taken where its wave split pads fewer slots (e.g. 4 or 12
@@ -157,7 +158,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
     // split, so their sums stay in the same order.
     if (G.fmt == FMT_W4 && (pro == PRO_NONE || pro == PRO_QIN) && pipe != 4 && S > 0) {
         int kw4 = 1, tw4 = 1;
-        const int64_t slots4 = split_waves(p.KBs, (T + R - 1) / R, m, nwa, 4, kw4, tw4);
+        const int64_t slots4 = split_waves(p.KBs, (T + R - 1) / R, m, nwa, 4, S > 1, kw4, tw4);
         const bool fewer = (m == 1) ? slots4 < slots : slots4 * 10 <= slots * 9;
         if (fewer && lds_for(S, kw4, tw4) <= kLdsMax) {
             p.KW = kw4;
@@ -166,6 +167,7 @@ Plan plan_for(const Geom& G, int m, int cus, int split_override, int ept, int pr
         }
     }
     p.spw = p.KW > 0 ? p.KBs / p.KW : 0;
+    p.srem = p.KW > 0 ? p.KBs % p.KW : 0;
     p.P = S * R;
     p.ks = cb ? 2 * p.KS + 64 : p.KS + 32;
     // only as many waves per row as the slice needs: the activation work then
@@ -307,6 +309,7 @@ hipError_t launch_gemm(const Geom& G, const GemmCall& c, hipStream_t st) {
     a.TW = p.TW;
     a.KW = p.KW;
     a.spw = p.spw;
+    a.srem = p.srem;
     a.KBs = p.KBs;
     a.KS = p.KS;
     a.WPR = p.WPR;

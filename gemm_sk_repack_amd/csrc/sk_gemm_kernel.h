@@ -121,6 +121,7 @@ struct KArgs {
     // = tiles per tile group, rounded up, for the two block sizes
     int tq, trem, jn0, jn1;
     int TW, spw, KB;
+    int srem;               // super-blocks per wave along k: spw, plus one for the first srem k-parts
     int sbf, swo;           // bytes per super-block of a full tile; offset of its scales
     int t_rag;              // index of the ragged tile, -1 if N % 16 == 0
     int nr_last;            // rows of the ragged tile (16 if none)
@@ -736,7 +737,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // dependent argument fetches).
     __asm__ volatile("" ::"s"(a.data), "s"(a.x), "s"(a.ld), "s"(a.tile_full), "s"(a.rag_w), "s"(a.rag_s),
                      "s"(a.m), "s"(a.KS), "s"(a.S), "s"(a.KBs), "s"(a.tq), "s"(a.trem), "s"(a.jn0),
-                     "s"(a.jn1), "s"(a.TW), "s"(a.spw), "s"(a.KB), "s"(a.sbf), "s"(a.swo), "s"(a.t_rag),
+                     "s"(a.jn1), "s"(a.TW), "s"(a.spw), "s"(a.srem), "s"(a.KB), "s"(a.sbf), "s"(a.swo), "s"(a.t_rag),
                      "s"(a.nr_last), "s"(a.rag_sbw), "s"(a.rag_sbs), "s"(a.cpr), "s"(a.tpr), "s"(a.tpe),
                      "s"(a.wtab[wv]));
     const int nl = lane & 15;
@@ -810,7 +811,11 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     const int jn = big ? a.jn1 : a.jn0;         // tiles per group, padded
     const int tg = wt & 31;
     const int kw = (wt >> 5) & 31;
-    const int kbw = kb_lo + kw * a.spw;
+    // the wave's k-part of the slice: spw super-blocks, one more for the first
+    // srem k-parts (K-split launches, where the slice's count has few divisors)
+    const int spw_w = a.spw + (kw < a.srem ? 1 : 0);
+    const int kwo = kw * a.spw + min(kw, a.srem);   // its first super-block in the slice
+    const int kbw = kb_lo + kwo;
     // With S > 1 the last wave only runs the cross-slice exchange: it never has
     // weight loads in flight, so its polls are not queued behind them.
     const bool poller = !ONE && (a.S > 1) && (wv == NW - 1);
@@ -839,7 +844,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
     // tiles tg, tg + TW, ... below ntile: jn = ceil(ntile / TW) of them, one
     // fewer for the groups past the last step's share
     const int jw = active ? jn - (tg >= ntile - (jn - 1) * a.TW ? 1 : 0) : 0;
-    const int ngrp = (a.spw + PIPE - 1) / PIPE;      // slot groups per tile step
+    const int ngrp = (spw_w + PIPE - 1) / PIPE;      // slot groups per tile step
 
     // Per-lane byte offsets inside a super-block: a full tile (16 rows) and the
     // weight's ragged last tile (nr_last rows; its lanes nl >= nr_last read
@@ -875,7 +880,7 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         const int t = t_begin + tg + lj * a.TW;
         const bool valid = lj < jw;
         const int kb = kbw + lg * PIPE;
-        gnv = valid ? min(PIPE, a.spw - lg * PIPE) : 0;
+        gnv = valid ? min(PIPE, spw_w - lg * PIPE) : 0;
         if constexpr (CANON) {
             const int tt = valid ? t : 0;
             const int nlc = min(tt * TILE_ROWS + nl, a.n - 1) - tt * TILE_ROWS;
@@ -1517,8 +1522,8 @@ __global__ __launch_bounds__(NT) void gemm_kernel(KArgs a) {
         const bool pvalid = pj < jw;
         const int t = t_begin + tg + pj * a.TW;
         for (int pg = 0; pg < ngrp; ++pg) {
-            const int pnv = pvalid ? min(PIPE, a.spw - pg * PIPE) : 0;
-            const int kb0 = kw * a.spw + pg * PIPE;
+            const int pnv = pvalid ? min(PIPE, spw_w - pg * PIPE) : 0;
+            const int kb0 = kwo + pg * PIPE;
 #pragma unroll
             for (int d = 0; d < PIPE; ++d) {
                 process(d < pnv, t, kb0 + d, wbuf[d], hbuf[d], sbuf[d], sbuf2[d]);

@@ -80,7 +80,8 @@ struct Plan {
     int R;        // workgroups per slice
     int P;        // workgroups = S * R
     int TW, KW;   // waves = TW tile groups x KW waves along k
-    int spw;      // super-blocks per wave per tile
+    int spw;      // super-blocks per wave per tile (the first srem k-parts take one more)
+    int srem;
     int KBs;      // super-blocks per slice
     int KS;       // K per slice
     int WPR;      // waves per activation row in the prologue

@@ -29,14 +29,16 @@ sk_status sk_test_repack_on_host(const sk_weight* w, void* host_bytes, int inver
 /*
  * The launch plan the library would use for a GEMM call with this shape, M,
  * prologue (0 none, 1 RMSNorm, 2 SwiGLU) and compute-unit count (host
- * arithmetic only).  fields[0..13] receive
+ * arithmetic only).  fields[0..14] receive
  * S (K-slices), R (workgroups per slice), P (workgroups), TW (tile groups per
  * workgroup), KW (waves along k), super-blocks per wave per tile,
  * super-blocks per slice, K per slice, waves per activation row, dynamic LDS
  * bytes, workspace floats for slice partials, activations per thread in the
  * prologue (16, 24, 32 or 40), 1 if the kernel instance with the larger activation
- * budget runs (else 0) and the register-pipeline depth the wave split was chosen
- * for (slots of weights in flight per wave).  SK_ERR_UNSUPPORTED if no
+ * budget runs (else 0), the register-pipeline depth the wave split was chosen
+ * for (slots of weights in flight per wave) and the number of k-parts that take
+ * one super-block more than the given count (K-split launches only; else 0).
+ * SK_ERR_UNSUPPORTED if no
  * plan exists; SK_ERR_SHAPE for shapes outside the backend's range.
  */
 sk_status sk_test_gemm_plan(int n, int k, int group, int format, int m, int prologue, int cus,

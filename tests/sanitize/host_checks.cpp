@@ -160,7 +160,7 @@ static void check_planners() {
                     for (int m = 1; m <= 8; ++m)
                         for (int pro = 0; pro < 3; ++pro)
                             for (int cu : cus) {
-                                int64_t f[14];
+                                int64_t f[15];
                                 const sk_status st = sk_test_gemm_plan(n, k, g, fmt, m, pro, cu, f);
                                 CHECK(st == SK_OK || st == SK_ERR_UNSUPPORTED || st == SK_ERR_SHAPE ||
                                       st == SK_ERR_FORMAT);
@@ -168,6 +168,7 @@ static void check_planners() {
                                     ++ok;
                                     CHECK(f[0] >= 1 && f[1] >= 1 && f[2] == f[0] * f[1] && f[3] >= 1 && f[4] >= 1);
                                     CHECK(f[13] == 4 || f[13] == 5);
+                                    CHECK(f[14] >= 0 && f[14] < f[4] && (f[0] > 1 || f[14] == 0));
                                 }
                             }
     CHECK(ok > 1000);

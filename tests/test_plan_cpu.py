@@ -58,7 +58,9 @@ def test_plan_within_kernel_assumptions(n, k, g, fmt, m, pro):
     assert p["WPR"] == min(NW // m, -(-p["KS"] // (ept * 64)))
     assert p["KS"] // ept <= p["WPR"] * 64                 # the slice fits the registers
     assert p["TW"] * p["KW"] <= NW and p["TW"] * m * 16 <= NW * 64
-    assert p["spw"] * p["KW"] == p["KBs"]
+    # k-parts: spw super-blocks each, one more for the first srem (K-split only)
+    assert p["spw"] * p["KW"] + p["srem"] == p["KBs"] and 0 <= p["srem"] < p["KW"]
+    assert S > 1 or p["srem"] == 0
     assert p["lds"] <= 150 * 1024
     # LDS: q (int8, or bf16 after the codebook's 64-byte level table), the wave
     # partials' two halves, and for RMSNorm the slice's gamma
@@ -97,13 +99,15 @@ def covered(n, k, m, p):
         jn = (ntile + p["TW"] - 1) // p["TW"]
         for wv in range(NW):
             tg, kw = wv // p["KW"], wv % p["KW"]
-            if tg >= p["TW"]:
+            if tg >= p["TW"] or (p["S"] > 1 and wv == NW - 1):
                 continue
-            for i in range(jn * p["spw"]):
-                t = t0 + tg + (i // p["spw"]) * p["TW"]
+            spw_w = p["spw"] + (1 if kw < p["srem"] else 0)
+            kwo = kw * p["spw"] + min(kw, p["srem"])
+            for i in range(jn * spw_w):
+                t = t0 + tg + (i // spw_w) * p["TW"]
                 if t >= t1:
                     continue
-                kb = s * p["KBs"] + kw * p["spw"] + i % p["spw"]
+                kb = s * p["KBs"] + kwo + i % spw_w
                 seen[t, kb] += 1
     return seen
 
@@ -113,6 +117,18 @@ def covered(n, k, m, p):
 def test_work_covers_every_superblock_once(n, k, g, fmt, m):
     p = sk.gemm_plan(n, k, g, fmt, m)
     assert np.all(covered(n, k, m, p) == 1)
+
+
+@pytest.mark.parametrize("n,k,m", [(5120, 17408, 8), (5120, 17408, 6), (4096, 12288, 8), (4096, 12288, 4),
+                                   (1000, 17408, 8), (12288, 4096, 8)])
+def test_uneven_k_parts_cover_every_superblock_once(n, k, m):
+    """K-split plans may give the first srem k-parts one super-block more; the
+    27B-class down projection at M = 8 (34 super-blocks per slice) then runs 15
+    waves (5 tile groups x 3 k-parts) instead of 10."""
+    p = sk.gemm_plan(n, k, 32, sk.SK_W4_SYM, m)
+    assert np.all(covered(n, k, m, p) == 1)
+    if (n, k, m) == (5120, 17408, 8):
+        assert (p["S"], p["TW"], p["KW"], p["spw"], p["srem"]) == (4, 5, 3, 11, 1), p
 
 
 @pytest.mark.parametrize("cus", [1, 7, 64, 80, 256, 304])
@@ -147,12 +163,13 @@ def test_wide_budget_where_measured_faster(n, k, m, S, wide):
 
 @pytest.mark.parametrize("n,k,m,pipe", [
     (7168, 5120, 1, 5), (7168, 5120, 8, 5), (34816, 5120, 1, 4), (34816, 5120, 8, 5),
-    (5120, 17408, 1, 5), (5120, 17408, 8, 5), (6144, 4096, 1, 4), (6144, 4096, 8, 4),
+    (5120, 17408, 1, 5), (5120, 17408, 8, 4), (6144, 4096, 1, 4), (6144, 4096, 8, 4),
     (24576, 4096, 1, 4), (4096, 12288, 1, 4),
 ])
 def test_pipeline_depth_where_measured_faster(n, k, m, pipe):
     """27B-class shapes (5 or 17 super-blocks per wave): 5 slots, except gate+up at
-    M = 1 (a 15-wave split of 8); 9B-class (4, 6 or 8): 4."""
+    M = 1 (a 15-wave split of 8) and down at M = 8 (k-parts of 12/11/11); 9B-class
+    (4, 6 or 8): 4."""
     p = sk.gemm_plan(n, k, 32, sk.SK_W4_SYM, m)
     assert p["pipe"] == pipe, p
 
